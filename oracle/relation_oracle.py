@@ -1,0 +1,230 @@
+"""Plain fp64 CPU oracle for the causal Self-Exchange Relation (SER / MHR).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call this
+module: only the test suite, the smoke check and the benchmark's CPU-baseline
+leg do. It shares no code with the HIP kernels and is deliberately slow and
+literal: it materialises the T x T relation matrix R and the flow F per head.
+
+Source: "Ask Self, Ask Others: Relation Is All You Need" (arXiv 2608.20172),
+abbreviated [paper] below, and the author's blog post on the derivation
+(qingkeai.online, "Attention -> Relation"), abbreviated [blog].
+
+Definition followed by ``relation_head`` (one head, rows of P1/P2/V are tokens):
+  U_ij = p1_i . p2_j / sqrt(d_h)                        [paper] Eq. (1)
+  S_i  = sigmoid(U_ii / tau_S)                          [paper] Eq. (2)
+  E_ij = SiLU(U_ij) = U_ij * sigmoid(U_ij)              [paper] Eq. (2)
+  R_ii = S_i;  R_ij = E_ij - lambda * log(i) for j < i;  R_ij = -inf for j > i
+        with i one-based                                [paper] Eq. (2), App. A intro
+  F_i  = softmax(R_i);  Y_i = sum_{j<=i} F_ij V_j       [paper] Eq. (3)
+V stands for the information state after head mixing (I~ in [paper] Eq. (4)-(5));
+head mixing and RoPE happen before this operator and are not part of it.
+
+Readings taken where the pages leave a choice open:
+  * lambda (the count calibration) is an argument, default 0 (the paper's
+    "no count calibration" variant, Table 3); tau_S is one value per head.
+  * S_i enters R as a logit (it is exponentiated by the softmax), not rescaled.
+  * Decode: the new token sits at one-based position L+1 after L cached rows;
+    its row is the definition's last row on [cache rows; new token]
+    ([paper] Eq. (18), App. A.5).
+
+Cross-check routes (exact algebra per the paper; used only to pin this file):
+  * ``factorized_head``: Eq. (6)-(9) / App. A.1.2-A.1.6.
+  * ``flash_scan_head``: the tiled (m, l, z) Exchange scan, Eq. (12)-(14) /
+    App. A.3, with caller-chosen tile boundaries.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "sigmoid", "silu", "evidence", "relation_matrix", "flow", "relation_head",
+    "relation_fwd", "relation_rows", "relation_decode", "factorized_head",
+    "flash_scan_head",
+]
+
+
+def sigmoid(x):
+    """Logistic function, evaluated without overflow for either sign."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x): the Exchange map ([paper] Eq. (2))."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def evidence(p1, p2):
+    """U = P1 P2^T / sqrt(d_h) for one head ([paper] Eq. (1))."""
+    d_h = p1.shape[-1]
+    return (p1 @ p2.T) / math.sqrt(d_h)
+
+
+def relation_matrix(p1, p2, tau, lam=0.0):
+    """The causal relation matrix R of one head ([paper] Eq. (2)).
+
+    p1, p2: float64 [T, d_h]. Returns float64 [T, T] with -inf above the diagonal.
+    """
+    T = p1.shape[0]
+    U = evidence(p1, p2)
+    R = np.full((T, T), -np.inf)
+    below = np.tril(np.ones((T, T), dtype=bool), k=-1)
+    i_one_based = np.arange(1, T + 1, dtype=np.float64)
+    count = lam * np.log(i_one_based)                  # -lambda log i, row-wise
+    E = silu(U)
+    R[below] = (E - count[:, None])[below]
+    diag = np.arange(T)
+    R[diag, diag] = sigmoid(U[diag, diag] / float(tau))
+    return R
+
+
+def flow(R):
+    """Row-wise softmax of R ([paper] Eq. (3)); exp(-inf) contributes 0."""
+    mx = np.max(R, axis=1, keepdims=True)
+    W = np.exp(R - mx)
+    return W / np.sum(W, axis=1, keepdims=True)
+
+
+def relation_head(p1, p2, v, tau, lam=0.0, return_flow=False):
+    """Y = F V for one head; all arguments float64 [T, d_h]."""
+    F = flow(relation_matrix(p1, p2, tau, lam))
+    Y = F @ v
+    return (Y, F) if return_flow else Y
+
+
+def relation_fwd(P1, P2, V, tau, lam=0.0):
+    """Multi-head forward: [B, H, T, d_h] float64 arrays, tau float[H].
+
+    Heads are independent ([paper] Sec. 3.2, App. A.2.1): loop over (b, h).
+    """
+    B, H, T, _ = P1.shape
+    Y = np.empty(V.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            Y[b, h] = relation_head(P1[b, h], P2[b, h], V[b, h], tau[h], lam)
+    return Y
+
+
+def relation_rows(p1, p2, v, tau, lam, rows):
+    """Selected output rows of one head, each straight from the definition.
+
+    rows: zero-based row indices r; row r is token i = r + 1. Row r reads only
+    p1[r], p2[:r+1] and v[:r+1], so large T costs O(r d_h) per row.
+    """
+    d_h = p1.shape[-1]
+    out = np.empty((len(rows), v.shape[1]), dtype=np.float64)
+    for k, r in enumerate(rows):
+        u = (p2[: r + 1] @ p1[r]) / math.sqrt(d_h)        # U_{i, 1..i}
+        logits = silu(u) - lam * math.log(r + 1)           # Exchange entries
+        logits[r] = sigmoid(np.array([u[r] / float(tau)]))[0]  # Self entry
+        w = np.exp(logits - logits.max())
+        out[k] = (w / w.sum()) @ v[: r + 1]
+    return out
+
+
+def relation_decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam=0.0):
+    """One decode step against a Relation Cache ([paper] Eq. (18), App. A.5).
+
+    p1, p2, v: [B, H, d_h]; cache_P2, cache_V: [B, H, L_cap, d_h]; lens: [B].
+    The output for (b, h) is the last row of the forward on the sequence
+    [cache rows 0..L_b-1; new token]. Cache rows at or past L_b are not read.
+    """
+    B, H, d_h = p1.shape
+    y = np.empty((B, H, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(H):
+            P2seq = np.concatenate([cache_P2[b, h, :L], p2[b, h][None]], axis=0)
+            Vseq = np.concatenate([cache_V[b, h, :L], v[b, h][None]], axis=0)
+            P1row = np.zeros_like(P2seq)
+            P1row[L] = p1[b, h]
+            y[b, h] = relation_rows(P1row, P2seq, Vseq, tau[h], lam, [L])[0]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Cross-check routes (pins for the definition above; never used by the kernels)
+# ---------------------------------------------------------------------------
+
+def _lse(a):
+    """log sum exp over a 1-D array; -inf for an empty array ([paper] App. A.1.7)."""
+    if a.size == 0:
+        return -np.inf
+    m = np.max(a)
+    return m + math.log(np.sum(np.exp(a - m)))
+
+
+def factorized_head(p1, p2, v, tau, lam=0.0):
+    """Self mass / Exchange mass / Exchange allocation route, Eq. (6)-(9).
+
+    Returns dict with Y, S, A, F_self (= F_ii), g, pi (strictly lower, rows sum
+    to 1 for i > 1) and Ibar (the normalised historical summary, NaN on row 1).
+    """
+    T = p1.shape[0]
+    U = evidence(p1, p2)
+    d = np.arange(T)
+    S = sigmoid(U[d, d] / float(tau))
+    E = silu(U)
+    A = np.empty(T)
+    pi = np.zeros((T, T))
+    Ibar = np.full(v.shape, np.nan)
+    for r in range(T):
+        i = r + 1
+        LE = _lse(E[r, :r])                          # Eq. (6)
+        A[r] = LE - lam * math.log(i)
+        if r > 0:
+            w = np.exp(E[r, :r] - np.max(E[r, :r]))
+            pi[r, :r] = w / w.sum()                  # Eq. (8)
+            Ibar[r] = pi[r, :r] @ v[:r]
+    F_self = sigmoid(S - A)                          # Eq. (7)
+    g = sigmoid(A - S)
+    Y = F_self[:, None] * v                          # Eq. (9)
+    Y[1:] += g[1:, None] * Ibar[1:]
+    return dict(Y=Y, S=S, A=A, F_self=F_self, g=g, pi=pi, Ibar=Ibar)
+
+
+def flash_scan_head(p1, p2, v, tau, lam=0.0, bounds=None):
+    """Tiled historical Exchange scan, Eq. (12)-(14) / App. A.3.
+
+    bounds: increasing key-tile boundaries starting at 0 (e.g. [0, 3, 7, ...]);
+    default one tile per key. Self is not part of the scan; it enters once,
+    after the scan, through A_i and g_i. Row 1 follows App. A.1.7 (Y_1 = V_1).
+    """
+    T, d_h = p1.shape
+    if bounds is None:
+        bounds = list(range(T + 1))
+    bounds = list(bounds)
+    if bounds[-1] < T:
+        bounds.append(T)
+    Y = np.empty(v.shape, dtype=np.float64)
+    for r in range(T):
+        i = r + 1
+        m, l, z = -np.inf, 0.0, np.zeros(v.shape[1])    # empty-set state
+        for t0, t1 in zip(bounds[:-1], bounds[1:]):
+            t1 = min(t1, r)                              # historical j < i only
+            if t0 >= t1:
+                break
+            u = (p2[t0:t1] @ p1[r]) / math.sqrt(d_h)
+            E = silu(u)
+            m_new = max(m, float(np.max(E)))
+            scale = math.exp(m - m_new) if m != -np.inf else 0.0
+            p = np.exp(E - m_new)
+            l = scale * l + float(np.sum(p))
+            z = scale * z + p @ v[t0:t1]
+            m = m_new
+        S = float(sigmoid(np.array([(p1[r] @ p2[r]) / math.sqrt(d_h) / float(tau)]))[0])
+        if r == 0:
+            Y[r] = v[r]                                  # A_1 = -inf: g_1 = 0
+            continue
+        A = m + math.log(l) - lam * math.log(i)          # Eq. (13)-(14)
+        g = float(sigmoid(np.array([A - S]))[0])
+        Y[r] = (1.0 - g) * v[r] + g * (z / l)
+    return Y
