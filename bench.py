@@ -1,0 +1,175 @@
+"""Benchmark: causal Self-Exchange Relation forward (FlashRelation) on one GPU.
+
+One step = one relation_fwd call over the T = 8192 workload
+(B=1, H=32, T=8192, d_h=128, bf16, P1/P2/V ~ 0.5 N(0,1), tau = 1, seed 42),
+inputs resident in HBM before timing starts. Throughput counts the causal
+FLOPs 2 B H T^2 d_h (evidence over j <= i plus transport over j < i).
+
+Prints ONE JSON line. Also reported (not the headline): one Relation Cache
+decode step (B=64, H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of
+algorithmic cache traffic, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "relation_fwd TFLOP/s (causal) and % of MI355X bf16 MFMA peak at T=8192"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FWD_KERNEL_SRC = os.path.join(ROOT, "causal_self_exchange_amd", "csrc", "fwd_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_traffic.json")
+
+
+def _src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(launch_bytes_key="bytes_per_launch"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only
+    while the kernel source is unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != _src_sha(FWD_KERNEL_SRC):
+        return None
+    return t.get(launch_bytes_key)
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Per-launch durations (ms) from HIP events on the launching stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total = evs[0].elapsed_time(evs[-1])
+    return per, total, wall
+
+
+def cpu_baseline(inp, seconds_hint=True):
+    """The CPU oracle (materialised fp64 definition) on one head of the same
+    workload; reported in the headline unit."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import relation_oracle as O
+    import torch
+    p1 = inp["P1"][0, 0].to(torch.float64).numpy()
+    p2 = inp["P2"][0, 0].to(torch.float64).numpy()
+    v = inp["V"][0, 0].to(torch.float64).numpy()
+    T, d = p1.shape
+    t0 = time.perf_counter()
+    O.relation_head(p1, p2, v, float(inp["tau"][0]), 0.0)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": 2.0 * T * T * d / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"1 of 32 heads (b=0, h=0) of the B=1 H=32 T={T} d_h={d} workload, "
+                      "fp64 materialised R and F; numpy elementwise on 1 thread, BLAS on `cores`"}
+
+
+def bench_decode(torch, R, W, steps, warmup):
+    cfg = W.DECODE_CONFIG
+    inp = W.make_decode_inputs(cfg, 42)
+    d = {k: inp[k].cuda() for k in ("p1", "p2", "v", "cache_P2", "cache_V")}
+    lens = torch.from_numpy(inp["lens"]).cuda()
+    ws = torch.empty(R.decode_workspace_bytes(cfg.B, cfg.H, cfg.L_cap, cfg.d_h), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty_like(d["v"])
+
+    def fn():
+        R.decode(d["p1"], d["p2"], d["v"], d["cache_P2"], d["cache_V"], lens, inp["tau"], 0.0,
+                 out=y, workspace=ws)
+
+    per, total, _ = time_launches(fn, steps, warmup, torch)
+    L = inp["lens"].astype(np.int64)
+    bytes_alg = float(np.sum(L) * cfg.H * cfg.d_h * 2 * 2 + 4 * cfg.B * cfg.H * cfg.d_h * 2)
+    ms = total / steps
+    return {"workload": "decode: B=64 H=32 d_h=128 bf16, cache lengths U{1024..4096}, seed 42",
+            "us_per_step": round(ms * 1e3, 2), "GB/s": round(bytes_alg / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(bytes_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": bytes_alg}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the operator shards over heads with no "
+              f"communication); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_self_exchange_amd import relation as R
+    from causal_self_exchange_amd import workloads as W
+
+    cfg = W.CONFIGS["long"]
+    inp = W.make_fwd_inputs(cfg, 42)
+    P1, P2, V = (inp[k].cuda() for k in ("P1", "P2", "V"))
+    Y = torch.empty_like(V)
+    tau = inp["tau"]
+
+    def step():
+        R.fwd(P1, P2, V, tau, 0.0, out=Y)
+
+    per, total, wall = time_launches(step, args.steps, args.warmup, torch)
+    ms_step = total / args.steps
+    avg_launch_ms = float(np.mean(per))
+    flops = cfg.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = _traffic()
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long-context SER/MHR forward: B=1 H=32 T=8192 d_h=128 bf16, "
+                               "P1/P2/V ~ 0.5 N(0,1), tau=1, causal, seed 42",
+                   "B": cfg.B, "H": cfg.H, "T": cfg.T, "d_h": cfg.d_h},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "relation_fwd (bf16 MFMA FlashRelation)",
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "median_launch_us": round(float(np.median(per)) * 1e3, 2),
+                     "min_launch_us": round(float(np.min(per)) * 1e3, 2)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, R, W, max(10, args.steps // 2), args.warmup)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

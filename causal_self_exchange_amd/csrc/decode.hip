@@ -1,0 +1,214 @@
+// Relation Cache decode ("Ask Self, Ask Others: Relation Is All You Need",
+// Sec. 5.3, Eq. (18); App. A.5): one new row per (sequence, head) against the
+// cached P2 and information rows.
+//
+// The step is a stream over the cache, so it is split along the history:
+//   decode_partial: one work-group per (chunk of kDecodeChunk cached rows,
+//     head, sequence) scans its rows' Exchange entries and leaves a partial
+//     state (m, l, z[d_h]) in the workspace. Each row is read by d_h/VEC
+//     lanes with 16-byte loads, so a wave reads whole 256-byte rows.
+//   decode_merge: one wave per (head, sequence) merges the partial states
+//     (the scan update of Eq. (12) applied to whole chunks), adds the Self
+//     entry of the new token and the count term for position L + 1, and
+//     writes y.
+// relation_cache_append implements the cache update of App. A.5.3.
+#include "rel_internal.h"
+#include "rel_device.h"
+
+namespace rel {
+
+namespace {
+
+constexpr int kPartialThreads = 256;
+
+template <typename Tin>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(Tin);
+  Tin v[N];
+};
+
+template <typename Tin>
+__device__ __forceinline__ Vec16<Tin> load16(const Tin* p) {
+  Vec16<Tin> out;
+  *reinterpret_cast<uint4*>(out.v) = *reinterpret_cast<const uint4*>(p);
+  return out;
+}
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeArgs a, HeadParams hp) {
+  constexpr int VEC = 16 / sizeof(Tin);
+  constexpr int LPR = D / VEC;                      // lanes per cached row
+  constexpr int GROUPS = kPartialThreads / LPR;     // rows in flight per step
+  __shared__ float s_m[GROUPS];
+  __shared__ float s_l[GROUPS];
+  __shared__ float s_z[GROUPS][D + 1];
+
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = clamp_len(a.len[b], a.L_cap);
+  const int j_begin = chunk * kDecodeChunk;
+  if (j_begin >= L) return;                         // uniform for the block
+  const int j_end = min(L, j_begin + kDecodeChunk);
+
+  const int tid = threadIdx.x;
+  const int g = tid / LPR;
+  const int sl = tid % LPR;
+  const size_t bh = (size_t)b * a.H + h;
+  const Tin* p1 = static_cast<const Tin*>(a.p1) + bh * D + sl * VEC;
+  const Tin* cP2 = static_cast<const Tin*>(a.cP2) + bh * (size_t)a.L_cap * D + sl * VEC;
+  const Tin* cV = static_cast<const Tin*>(a.cV) + bh * (size_t)a.L_cap * D + sl * VEC;
+
+  float q[VEC], z[VEC];
+  {
+    const Vec16<Tin> t = load16(p1);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { q[e] = to_f32(t.v[e]); z[e] = 0.0f; }
+  }
+  float m = kEmptyMax, l = 0.0f;
+
+  for (int j = j_begin + g; j < j_end; j += GROUPS) {
+    const Vec16<Tin> kp = load16(cP2 + (size_t)j * D);
+    const Vec16<Tin> kv = load16(cV + (size_t)j * D);
+    float part = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) part = fmaf(q[e], to_f32(kp.v[e]), part);
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    const float E = silu_f32(part * hp.scale);
+    if (E > m) {
+      const float s = expf(m - E);
+      l *= s;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) z[e] *= s;
+      m = E;
+    }
+    const float p = expf(E - m);
+    l += p;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) z[e] = fmaf(p, to_f32(kv.v[e]), z[e]);
+  }
+
+  if (sl == 0) { s_m[g] = m; s_l[g] = l; }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s_z[g][sl * VEC + e] = z[e];
+  __syncthreads();
+
+  float* out = a.ws + (bh * a.n_chunks + chunk) * (size_t)(D + 2);
+  for (int k = tid; k < D; k += kPartialThreads) {
+    float M = kEmptyMax;
+    for (int gg = 0; gg < GROUPS; ++gg) M = fmaxf(M, s_m[gg]);
+    float zs = 0.0f, ls = 0.0f;
+    for (int gg = 0; gg < GROUPS; ++gg) {
+      const float w = expf(s_m[gg] - M);
+      zs = fmaf(w, s_z[gg][k], zs);
+      ls = fmaf(w, s_l[gg], ls);
+    }
+    out[2 + k] = zs;
+    if (k == 0) { out[0] = M; out[1] = ls; }
+  }
+}
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, HeadParams hp) {
+  constexpr int PER = (D + 63) / 64;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int L = clamp_len(a.len[b], a.L_cap);
+  const int nch = (L + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t bh = (size_t)b * a.H + h;
+  const float* ws = a.ws + bh * a.n_chunks * (size_t)(D + 2);
+
+  float M = kEmptyMax;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, ws[c * (D + 2)]);
+  float lsum = 0.0f;
+  float zsum[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) zsum[t] = 0.0f;
+  for (int c = 0; c < nch; ++c) {
+    const float* st = ws + c * (D + 2);
+    const float w = expf(st[0] - M);
+    lsum = fmaf(w, st[1], lsum);
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int k = lane + 64 * t;
+      if (k < D) zsum[t] = fmaf(w, st[2 + k], zsum[t]);
+    }
+  }
+
+  const Tin* p1 = static_cast<const Tin*>(a.p1) + bh * D;
+  const Tin* p2 = static_cast<const Tin*>(a.p2) + bh * D;
+  const Tin* v = static_cast<const Tin*>(a.v) + bh * D;
+  Tin* y = static_cast<Tin*>(a.y) + bh * D;
+  float dself = 0.0f;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int k = lane + 64 * t;
+    if (k < D) dself = fmaf(to_f32(p1[k]), to_f32(p2[k]), dself);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dself += __shfl_xor(dself, off);
+  const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
+  const RowCombine cmb(S, M, lsum, hp.lambda * logf((float)(L + 1)));
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int k = lane + 64 * t;
+    if (k < D) y[k] = from_f32<Tin>(cmb.w_self * to_f32(v[k]) + cmb.w_hist * zsum[t]);
+  }
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void cache_append_kernel(Tin* cP2, Tin* cV, int32_t* len,
+                                                           const Tin* p2, const Tin* v, int H,
+                                                           int L_cap, int D) {
+  const int b = blockIdx.x;
+  const int L = len[b];
+  __syncthreads();                       // every thread has read len[b]
+  if (L < 0 || L >= L_cap) return;       // uniform for the block
+  for (int idx = threadIdx.x; idx < H * D; idx += blockDim.x) {
+    const int h = idx / D, k = idx % D;
+    const size_t bh = (size_t)b * H + h;
+    cP2[(bh * L_cap + L) * D + k] = p2[bh * D + k];
+    cV[(bh * L_cap + L) * D + k] = v[bh * D + k];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) len[b] = L + 1;
+}
+
+template <typename Tin, int D>
+hipError_t launch_decode_typed(const DecodeArgs& a, const HeadParams& hp, hipStream_t s) {
+  dim3 g1(a.n_chunks, a.H, a.B);
+  hipLaunchKernelGGL((decode_partial_kernel<Tin, D>), g1, dim3(kPartialThreads), 0, s, a, hp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(a.H, a.B);
+  hipLaunchKernelGGL((decode_merge_kernel<Tin, D>), g2, dim3(64), 0, s, a, hp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s) {
+  switch (a.d_h) {
+    case 32: return bf16 ? launch_decode_typed<__bf16, 32>(a, hp, s) : launch_decode_typed<float, 32>(a, hp, s);
+    case 64: return bf16 ? launch_decode_typed<__bf16, 64>(a, hp, s) : launch_decode_typed<float, 64>(a, hp, s);
+    case 128: return bf16 ? launch_decode_typed<__bf16, 128>(a, hp, s) : launch_decode_typed<float, 128>(a, hp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
+                               int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s) {
+  if (bf16) {
+    hipLaunchKernelGGL(cache_append_kernel<__bf16>, dim3(B), dim3(256), 0, s,
+                       static_cast<__bf16*>(cP2), static_cast<__bf16*>(cV), len,
+                       static_cast<const __bf16*>(p2), static_cast<const __bf16*>(v), H, L_cap, d_h);
+  } else {
+    hipLaunchKernelGGL(cache_append_kernel<float>, dim3(B), dim3(256), 0, s,
+                       static_cast<float*>(cP2), static_cast<float*>(cV), len,
+                       static_cast<const float*>(p2), static_cast<const float*>(v), H, L_cap, d_h);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rel

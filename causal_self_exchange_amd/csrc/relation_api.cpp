@@ -1,0 +1,185 @@
+// Host side of librelation.so: argument validation, per-head parameter
+// packing and kernel dispatch for the C ABI declared in include/relation.h.
+// Every check runs before any HIP call, so an invalid call launches nothing.
+#include "relation.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "rel_internal.h"
+
+namespace {
+
+using rel::HeadParams;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t elem_size(rel_dtype dt) { return dt == REL_BF16 ? 2 : 4; }
+
+bool dtype_ok(rel_dtype dt) { return dt == REL_F32 || dt == REL_BF16; }
+
+bool head_dim_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128; }
+
+// Product of positive ints; false if any is < 1 or the product exceeds 2^40
+// elements (4 TiB of fp32, far beyond one GPU's memory).
+bool count(int64_t& out, std::initializer_list<int64_t> dims) {
+  constexpr int64_t kMaxElems = int64_t(1) << 40;
+  int64_t p = 1;
+  for (int64_t d : dims) {
+    if (d < 1) return false;
+    if (p > kMaxElems / d) return false;
+    p *= d;
+  }
+  out = p;
+  return true;
+}
+
+rel_status pack_heads(HeadParams& hp, const float* tau, int H, int d_h, float lambda) {
+  if (!std::isfinite(lambda)) return REL_E_LAMBDA;
+  for (int h = 0; h < H; ++h) {
+    const float t = tau[h];
+    if (!std::isfinite(t) || !(t > 0.0f)) return REL_E_TAU;
+    hp.inv_tau[h] = 1.0f / t;
+  }
+  for (int h = H; h < REL_MAX_HEADS; ++h) hp.inv_tau[h] = 0.0f;
+  hp.scale = 1.0f / std::sqrt(static_cast<float>(d_h));
+  hp.lambda = lambda;
+  return REL_OK;
+}
+
+// Which forward kernel runs: the MFMA kernel for bf16 where it exists, else
+// the row-scan kernel. RELATION_FWD_KERNEL=scan forces the row-scan kernel
+// (used to time and test it on its own).
+bool use_mfma(rel_dtype dt, int d_h) {
+  if (dt != REL_BF16 || !rel::fwd_mfma_supported(d_h)) return false;
+  const char* env = std::getenv("RELATION_FWD_KERNEL");
+  return !(env && std::strcmp(env, "scan") == 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* relation_status_str(rel_status s) {
+  switch (s) {
+    case REL_OK: return "ok";
+    case REL_E_NULL: return "null pointer";
+    case REL_E_SHAPE: return "invalid shape";
+    case REL_E_DTYPE: return "unknown dtype";
+    case REL_E_HEADDIM: return "unsupported head dimension";
+    case REL_E_TAU: return "tau must be finite and > 0";
+    case REL_E_LAMBDA: return "lambda must be finite";
+    case REL_E_ALIGN: return "pointer not 16-byte aligned";
+    case REL_E_ALIAS: return "output overlaps an input";
+    case REL_E_WORKSPACE: return "workspace missing or too small";
+    case REL_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V, const float* tau_s,
+                           float lambda, void* Y, int B, int H, int T, int d_h, rel_dtype dt,
+                           hipStream_t stream) {
+  if (!P1 || !P2 || !V || !tau_s || !Y) return REL_E_NULL;
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  HeadParams hp;
+  const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
+  if (st != REL_OK) return st;
+  if (!aligned16(P1) || !aligned16(P2) || !aligned16(V) || !aligned16(Y)) return REL_E_ALIGN;
+  const size_t bytes = static_cast<size_t>(n) * elem_size(dt);
+  if (overlaps(Y, bytes, P1, bytes) || overlaps(Y, bytes, P2, bytes) || overlaps(Y, bytes, V, bytes))
+    return REL_E_ALIAS;
+
+  rel::FwdArgs a{P1, P2, V, Y, B, H, T, d_h};
+  const hipError_t e = use_mfma(dt, d_h) ? rel::launch_fwd_mfma_bf16(a, hp, stream)
+                                         : rel::launch_fwd_scan(a, hp, dt == REL_BF16, stream);
+  return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+rel_status relation_fwd(const void* P1, const void* P2, const void* V, const float* tau_s, void* Y,
+                        int B, int H, int T, int d_h, rel_dtype dt, hipStream_t stream) {
+  return relation_fwd_ex(P1, P2, V, tau_s, 0.0f, Y, B, H, T, d_h, dt, stream);
+}
+
+size_t relation_decode_workspace_bytes(int B, int H, int L_cap, int d_h) {
+  int64_t n = 0;
+  if (!count(n, {B, H, L_cap, d_h}) || !head_dim_ok(d_h)) return 0;
+  const int64_t chunks = (L_cap + rel::kDecodeChunk - 1) / rel::kDecodeChunk;
+  return static_cast<size_t>(B) * H * chunks * (d_h + 2) * sizeof(float);
+}
+
+rel_status relation_decode(const void* p1, const void* p2, const void* v, const void* cache_P2,
+                           const void* cache_V, const int32_t* len, const float* tau_s, float lambda,
+                           void* y, int B, int H, int L_cap, int d_h, rel_dtype dt, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!p1 || !p2 || !v || !cache_P2 || !cache_V || !len || !tau_s || !y) return REL_E_NULL;
+  int64_t ncache = 0, ntok = 0;
+  if (!count(ncache, {B, H, L_cap, d_h}) || !count(ntok, {B, H, d_h}) || H > REL_MAX_HEADS ||
+      B > 65535)
+    return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  HeadParams hp;
+  const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
+  if (st != REL_OK) return st;
+  const size_t need = relation_decode_workspace_bytes(B, H, L_cap, d_h);
+  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  if (!aligned16(p1) || !aligned16(p2) || !aligned16(v) || !aligned16(cache_P2) ||
+      !aligned16(cache_V) || !aligned16(y) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(len) & 3u))
+    return REL_E_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t tb = static_cast<size_t>(ntok) * es, cb = static_cast<size_t>(ncache) * es;
+  const size_t lb = static_cast<size_t>(B) * sizeof(int32_t);
+  if (overlaps(y, tb, p1, tb) || overlaps(y, tb, p2, tb) || overlaps(y, tb, v, tb) ||
+      overlaps(y, tb, cache_P2, cb) || overlaps(y, tb, cache_V, cb) || overlaps(y, tb, len, lb) ||
+      overlaps(y, tb, workspace, need))
+    return REL_E_ALIAS;
+  if (overlaps(workspace, need, p1, tb) || overlaps(workspace, need, p2, tb) ||
+      overlaps(workspace, need, v, tb) || overlaps(workspace, need, cache_P2, cb) ||
+      overlaps(workspace, need, cache_V, cb) || overlaps(workspace, need, len, lb))
+    return REL_E_ALIAS;
+
+  rel::DecodeArgs a{p1, p2, v, cache_P2, cache_V, len, y, static_cast<float*>(workspace),
+                    B, H, L_cap, d_h, static_cast<int>((L_cap + rel::kDecodeChunk - 1) / rel::kDecodeChunk)};
+  const hipError_t e = rel::launch_decode(a, hp, dt == REL_BF16, stream);
+  return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len, const void* p2,
+                                 const void* v, int B, int H, int L_cap, int d_h, rel_dtype dt,
+                                 hipStream_t stream) {
+  if (!cache_P2 || !cache_V || !len || !p2 || !v) return REL_E_NULL;
+  int64_t ncache = 0, ntok = 0;
+  if (!count(ncache, {B, H, L_cap, d_h}) || !count(ntok, {B, H, d_h}) || H > REL_MAX_HEADS ||
+      B > 65535)
+    return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!aligned16(cache_P2) || !aligned16(cache_V) || !aligned16(p2) || !aligned16(v) ||
+      (reinterpret_cast<uintptr_t>(len) & 3u))
+    return REL_E_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t tb = static_cast<size_t>(ntok) * es, cb = static_cast<size_t>(ncache) * es;
+  const size_t lb = static_cast<size_t>(B) * sizeof(int32_t);
+  if (overlaps(cache_P2, cb, cache_V, cb) || overlaps(cache_P2, cb, p2, tb) ||
+      overlaps(cache_P2, cb, v, tb) || overlaps(cache_V, cb, p2, tb) || overlaps(cache_V, cb, v, tb) ||
+      overlaps(len, lb, cache_P2, cb) || overlaps(len, lb, cache_V, cb) || overlaps(len, lb, p2, tb) ||
+      overlaps(len, lb, v, tb))
+    return REL_E_ALIAS;
+  const hipError_t e =
+      rel::launch_cache_append(cache_P2, cache_V, len, p2, v, B, H, L_cap, d_h, dt == REL_BF16, stream);
+  return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""Thin Python binding over librelation.so (ctypes).
+
+Argument marshalling only: every step of the forward and decode runs in the
+HIP kernels behind the C ABI (include/relation.h). PyTorch supplies device
+memory and the current stream. There is no CPU fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librelation.so")
+
+REL_F32, REL_BF16 = 0, 1
+_DT = {torch.float32: REL_F32, torch.bfloat16: REL_BF16}
+
+_lib = None
+
+
+class RelationError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().relation_status_str(status).decode()
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load librelation.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run causal_self_exchange_amd.build first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, fp, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
+        L.relation_fwd.argtypes = [vp, vp, vp, fp, vp, i, i, i, i, i, vp]
+        L.relation_fwd.restype = i
+        L.relation_fwd_ex.argtypes = [vp, vp, vp, fp, f, vp, i, i, i, i, i, vp]
+        L.relation_fwd_ex.restype = i
+        L.relation_decode_workspace_bytes.argtypes = [i, i, i, i]
+        L.relation_decode_workspace_bytes.restype = sz
+        L.relation_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp, sz, vp]
+        L.relation_decode.restype = i
+        L.relation_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.relation_cache_append.restype = i
+        L.relation_status_str.argtypes = [i]
+        L.relation_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_decode_workspace_bytes",
+           "relation_decode", "relation_cache_append", "relation_status_str")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _tau_arg(tau, H: int):
+    arr = np.ascontiguousarray(np.broadcast_to(np.asarray(tau, dtype=np.float32), (H,)))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise RelationError(fn, st)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def fwd(P1, P2, V, tau, lam: float = 0.0, out=None, stream=None):
+    """Y = relation forward of [B, H, T, d_h] device tensors; tau: float or [H]."""
+    _require_cuda(P1, P2, V)
+    B, H, T, D = P1.shape
+    if P2.shape != P1.shape or V.shape != P1.shape or P2.dtype != P1.dtype or V.dtype != P1.dtype:
+        raise ValueError("P1, P2, V must share shape and dtype")
+    if out is None:
+        out = torch.empty_like(V)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_fwd_ex(_ptr(P1), _ptr(P2), _ptr(V), tau_p, float(lam), _ptr(out),
+                               B, H, T, D, _dtype_code(P1), _stream(stream))
+    del tau_keep
+    _check("relation_fwd_ex", st)
+    return out
+
+
+def decode_workspace_bytes(B: int, H: int, L_cap: int, d_h: int) -> int:
+    return int(lib().relation_decode_workspace_bytes(B, H, L_cap, d_h))
+
+
+def decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam: float = 0.0, out=None,
+           workspace=None, stream=None):
+    """One Relation Cache decode step; p1/p2/v [B,H,d_h], caches [B,H,L_cap,d_h],
+    lens int32[B] on the device."""
+    _require_cuda(p1, p2, v, cache_P2, cache_V, lens)
+    B, H, L_cap, D = cache_P2.shape
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    need = decode_workspace_bytes(B, H, L_cap, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=p1.device)
+    if out is None:
+        out = torch.empty_like(v)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_decode(_ptr(p1), _ptr(p2), _ptr(v), _ptr(cache_P2), _ptr(cache_V),
+                               _ptr(lens), tau_p, float(lam), _ptr(out), B, H, L_cap, D,
+                               _dtype_code(p1), _ptr(workspace), workspace.numel(), _stream(stream))
+    del tau_keep
+    _check("relation_decode", st)
+    return out
+
+
+def cache_append(cache_P2, cache_V, lens, p2, v, stream=None):
+    """Append the token's p2, v [B,H,d_h] at row lens[b] and increment lens."""
+    _require_cuda(cache_P2, cache_V, lens, p2, v)
+    B, H, L_cap, D = cache_P2.shape
+    st = lib().relation_cache_append(_ptr(cache_P2), _ptr(cache_V), _ptr(lens), _ptr(p2), _ptr(v),
+                                     B, H, L_cap, D, _dtype_code(p2), _stream(stream))
+    _check("relation_cache_append", st)

@@ -1,0 +1,141 @@
+/*
+ * relation.h - C ABI of librelation.so: the causal Self-Exchange Relation
+ * forward (FlashRelation form) and its Relation Cache decode step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operator ("Ask Self, Ask Others: Relation Is All You Need", Eq. (1)-(3)),
+ * per batch entry b and head h, for query row i (one-based) of T:
+ *   U_ij = p1_i . p2_j / sqrt(d_h)
+ *   R_ii = sigmoid(U_ii / tau_h)                  (Self)
+ *   R_ij = SiLU(U_ij) - lambda * log(i),  j < i   (Exchange)
+ *   R_ij = -inf,                          j > i
+ *   Y_i  = sum_{j<=i} softmax(R_i)_j V_j
+ * Execution follows the paper's factorised tiled scan (Sec. 5.1, Eq. (12)-(14)):
+ * Exchange is scanned with running (max, sum, accumulator) and Self enters
+ * once per row afterwards, so U, R and F are never materialised.
+ * V is the information state after any head mixing (I~ in Eq. (4)-(5)); P1
+ * and P2 are taken after any positional rotation. Heads are independent
+ * (App. A.2.1).
+ *
+ * Common conventions
+ *   - Tensors are device memory, contiguous row-major [B, H, T, d_h] (forward)
+ *     or [B, H, d_h] / [B, H, L_cap, d_h] (decode); all of one dtype.
+ *   - tau_s is HOST memory, float[H], read during the call (may be freed on
+ *     return). Every tau must be finite and > 0 (the paper requires tau_S > 0).
+ *   - lambda is the count-calibration coefficient; 0 gives the operator without
+ *     count calibration.
+ *   - The caller owns every buffer. The library allocates nothing, keeps no
+ *     pointer after returning and holds no mutable global state.
+ *   - All argument checks run on the host before any HIP call; on an error
+ *     nothing is launched and no memory is touched.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *     caller synchronises. REL_E_LAUNCH reports a launch failure.
+ *   - Pointers must be 16-byte aligned; an output range may not overlap any
+ *     input range.
+ *   - Supported: d_h in {32, 64, 128}; 1 <= H <= REL_MAX_HEADS; B <= 65535.
+ */
+#ifndef RELATION_H
+#define RELATION_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REL_MAX_HEADS 256
+
+typedef enum {
+  REL_OK = 0,
+  REL_E_NULL = 1,      /* a required pointer is NULL                         */
+  REL_E_SHAPE = 2,     /* B, H, T, d_h or L_cap out of range / overflow      */
+  REL_E_DTYPE = 3,     /* unknown dtype                                      */
+  REL_E_HEADDIM = 4,   /* d_h not supported                                  */
+  REL_E_TAU = 5,       /* a tau is NaN, infinite or <= 0                     */
+  REL_E_LAMBDA = 6,    /* lambda is NaN or infinite                          */
+  REL_E_ALIGN = 7,     /* a pointer is not 16-byte aligned                   */
+  REL_E_ALIAS = 8,     /* an output range overlaps an input range           */
+  REL_E_WORKSPACE = 9, /* workspace missing or smaller than required         */
+  REL_E_LAUNCH = 10    /* a kernel launch failed                             */
+} rel_status;
+
+typedef enum { REL_F32 = 0, REL_BF16 = 1 } rel_dtype;
+
+/*
+ * relation_fwd - causal multi-head Relation forward without count
+ * calibration (lambda = 0): the paper's Eq. (1)-(3) evaluated by the tiled
+ * scan of Sec. 5.1. Equivalent to relation_fwd_ex(..., lambda = 0, ...).
+ *
+ *   P1, P2, V : in,  device [B, H, T, d_h], dtype dt
+ *   tau_s     : in,  host float[H], per-head Self temperature
+ *   Y         : out, device [B, H, T, d_h], dtype dt
+ * Numerics: REL_BF16 computes both contractions on bf16 MFMA with fp32
+ * accumulation, keeps the scan state and the Self term in fp32, rounds the
+ * Exchange weights to bf16 as the second contraction's operand, and rounds Y
+ * to bf16 (nearest-even). REL_F32 computes in fp32 throughout.
+ */
+rel_status relation_fwd(const void* P1, const void* P2, const void* V,
+                        const float* tau_s, void* Y, int B, int H, int T,
+                        int d_h, rel_dtype dt, hipStream_t stream);
+
+/*
+ * relation_fwd_ex - as relation_fwd, with the count calibration
+ * -lambda * log(i) on every Exchange entry of row i (Eq. (2); i one-based).
+ * lambda must be finite.
+ */
+rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V,
+                           const float* tau_s, float lambda, void* Y, int B,
+                           int H, int T, int d_h, rel_dtype dt,
+                           hipStream_t stream);
+
+/*
+ * relation_decode_workspace_bytes - bytes of device workspace relation_decode
+ * needs for these sizes (split-history partial states). 0 on invalid sizes.
+ */
+size_t relation_decode_workspace_bytes(int B, int H, int L_cap, int d_h);
+
+/*
+ * relation_decode - one autoregressive step against a Relation Cache
+ * (Eq. (18), App. A.5): the cache holds the historical P2 rows and
+ * information rows of each sequence; the new token's p1 is matched against
+ * them, its own p1 . p2 gives the Self entry, and the output is row L_b + 1 of
+ * the forward on [cache rows 0..L_b-1; new token].
+ *
+ *   p1, p2, v          : in, device [B, H, d_h], the new token's states
+ *   cache_P2, cache_V  : in, device [B, H, L_cap, d_h]; rows >= len[b] are
+ *                        never read (they may hold anything, NaN included)
+ *   len                : in, device int32[B], cached rows per sequence; a value
+ *                        outside [0, L_cap] is clamped into that range
+ *   tau_s, lambda      : as for relation_fwd_ex (new token position L_b + 1)
+ *   y                  : out, device [B, H, d_h]
+ *   workspace          : device scratch of >= relation_decode_workspace_bytes
+ * The cache is not modified; append with relation_cache_append afterwards.
+ */
+rel_status relation_decode(const void* p1, const void* p2, const void* v,
+                           const void* cache_P2, const void* cache_V,
+                           const int32_t* len, const float* tau_s,
+                           float lambda, void* y, int B, int H, int L_cap,
+                           int d_h, rel_dtype dt, void* workspace,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * relation_cache_append - the cache update of App. A.5.3: write the token's
+ * p2 and v ([B, H, d_h]) as row len[b] of cache_P2 / cache_V and increment
+ * len[b]. A sequence whose len[b] is already >= L_cap (or < 0) is left
+ * unchanged, len included.
+ */
+rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len,
+                                 const void* p2, const void* v, int B, int H,
+                                 int L_cap, int d_h, rel_dtype dt,
+                                 hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* relation_status_str(rel_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELATION_H */

@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/relation.h declares, and rejects every invalid call with its status
+code before any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from causal_self_exchange_amd import relation as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_TAU, E_LAMBDA, E_ALIGN, E_ALIAS, E_WS, E_LAUNCH = range(11)
+
+# Fake, never-dereferenced device addresses (16-byte aligned, far apart).
+A, B_, C, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _tau(vals):
+    arr = np.asarray(vals, dtype=np.float32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "relation.h")).read()
+    return sorted(set(re.findall(r"\b(relation_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.lib()
+    syms = declared_symbols()
+    assert set(syms) == set(R.EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings():
+    lib = R.lib()
+    for code in range(11):
+        assert lib.relation_status_str(code)
+    assert lib.relation_status_str(99) == b"unknown status"
+
+
+def fwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, B=1, H=2, T=16, D=64, dt=R.REL_BF16):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    return R.lib().relation_fwd_ex(P1, P2, V, tp, lam, Yp, B, H, T, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P1=None), E_NULL), (dict(V=None), E_NULL), (dict(Yp=None), E_NULL), (dict(tau=None), E_NULL),
+    (dict(T=0), E_SHAPE), (dict(B=0), E_SHAPE), (dict(H=0, tau=(1.0,)), E_SHAPE), (dict(D=-64), E_SHAPE),
+    (dict(B=70000), E_SHAPE), (dict(H=257, tau=[1.0] * 257), E_SHAPE),
+    (dict(T=2**31 - 1, B=65535, H=256, tau=[1.0] * 256, D=128), E_SHAPE),
+    (dict(dt=7), E_DTYPE), (dict(D=48), E_HEADDIM), (dict(D=256), E_HEADDIM),
+    (dict(tau=(1.0, 0.0)), E_TAU), (dict(tau=(-1.0, 1.0)), E_TAU),
+    (dict(tau=(1.0, float("nan"))), E_TAU), (dict(tau=(float("inf"), 1.0)), E_TAU),
+    (dict(lam=float("nan")), E_LAMBDA), (dict(lam=float("inf")), E_LAMBDA),
+    (dict(P2=B_ + 8), E_ALIGN), (dict(Yp=Y + 2), E_ALIGN),
+    (dict(Yp=A), E_ALIAS), (dict(Yp=C + 16), E_ALIAS), (dict(Yp=B_ - 16), E_ALIAS),
+])
+def test_fwd_rejects_invalid_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fwd_plain_entry_rejects_like_ex():
+    keep, tp = _tau([1.0, -2.0])
+    assert R.lib().relation_fwd(A, B_, C, tp, Y, 1, 2, 16, 64, R.REL_BF16, None) == E_TAU
+    assert R.lib().relation_fwd(None, B_, C, tp, Y, 1, 2, 16, 64, R.REL_BF16, None) == E_NULL
+
+
+def test_decode_workspace_bytes():
+    lib = R.lib()
+    assert lib.relation_decode_workspace_bytes(64, 32, 4096, 128) == 64 * 32 * 16 * 130 * 4
+    assert lib.relation_decode_workspace_bytes(2, 3, 1, 32) == 2 * 3 * 1 * 34 * 4
+    assert lib.relation_decode_workspace_bytes(2, 3, 257, 64) == 2 * 3 * 2 * 66 * 4
+    assert lib.relation_decode_workspace_bytes(0, 3, 10, 64) == 0
+    assert lib.relation_decode_workspace_bytes(1, 1, 10, 48) == 0
+
+
+LEN, WS, YD, CP, CV = 0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+
+def dec(p1=A, p2=B_, v=C, cP2=CP, cV=CV, ln=LEN, tau=(1.0, 1.0), lam=0.0, y=YD,
+        B=2, H=2, L=300, D=128, dt=R.REL_BF16, ws=WS, wsb=None):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    if wsb is None:
+        wsb = R.lib().relation_decode_workspace_bytes(B, H, L, D)
+    return R.lib().relation_decode(p1, p2, v, cP2, cV, ln, tp, lam, y, B, H, L, D, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p1=None), E_NULL), (dict(cV=None), E_NULL), (dict(ln=None), E_NULL), (dict(y=None), E_NULL),
+    (dict(L=0), E_SHAPE), (dict(B=-1), E_SHAPE), (dict(dt=3), E_DTYPE), (dict(D=80), E_HEADDIM),
+    (dict(tau=(0.0, 1.0)), E_TAU), (dict(lam=float("-inf")), E_LAMBDA),
+    (dict(ws=None), E_WS), (dict(wsb=16), E_WS),
+    (dict(cP2=CP + 4), E_ALIGN), (dict(ln=LEN + 2), E_ALIGN), (dict(ws=WS + 8), E_ALIGN),
+    (dict(y=A), E_ALIAS), (dict(y=CP + 1024), E_ALIAS), (dict(ws=CV + 4096), E_ALIAS),
+    (dict(y=WS + 64), E_ALIAS),
+])
+def test_decode_rejects_invalid_arguments(kw, code):
+    assert dec(**kw) == code
+
+
+def test_cache_append_rejects_invalid_arguments():
+    lib = R.lib()
+    f = lib.relation_cache_append
+    assert f(None, CV, LEN, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_NULL
+    assert f(CP, CV, LEN, A, C, 2, 2, 0, 128, R.REL_BF16, None) == E_SHAPE
+    assert f(CP, CV, LEN, A, C, 2, 2, 300, 96, R.REL_BF16, None) == E_HEADDIM
+    assert f(CP, CV, LEN, A, C, 2, 2, 300, 128, 5, None) == E_DTYPE
+    assert f(CP, CV, LEN + 1, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIGN
+    assert f(CP, CP + 256, LEN, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIAS
+    assert f(CP, CV, CV + 64, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIAS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        R.fwd(x, x, x, 1.0)
