@@ -41,7 +41,7 @@ constexpr int kDecodeChunk = 256;
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s);
-bool fwd_mfma_supported(int d_h);
+bool fwd_mfma_supported(int d_h, int T);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
                                int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s);

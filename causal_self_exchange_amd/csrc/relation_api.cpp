@@ -57,8 +57,8 @@ rel_status pack_heads(HeadParams& hp, const float* tau, int H, int d_h, float la
 // Which forward kernel runs: the MFMA kernel for bf16 where it exists, else
 // the row-scan kernel. RELATION_FWD_KERNEL=scan forces the row-scan kernel
 // (used to time and test it on its own).
-bool use_mfma(rel_dtype dt, int d_h) {
-  if (dt != REL_BF16 || !rel::fwd_mfma_supported(d_h)) return false;
+bool use_mfma(rel_dtype dt, int d_h, int T) {
+  if (dt != REL_BF16 || !rel::fwd_mfma_supported(d_h, T)) return false;
   const char* env = std::getenv("RELATION_FWD_KERNEL");
   return !(env && std::strcmp(env, "scan") == 0);
 }
@@ -101,7 +101,7 @@ rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V, const 
     return REL_E_ALIAS;
 
   rel::FwdArgs a{P1, P2, V, Y, B, H, T, d_h};
-  const hipError_t e = use_mfma(dt, d_h) ? rel::launch_fwd_mfma_bf16(a, hp, stream)
+  const hipError_t e = use_mfma(dt, d_h, T) ? rel::launch_fwd_mfma_bf16(a, hp, stream)
                                          : rel::launch_fwd_scan(a, hp, dt == REL_BF16, stream);
   return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
