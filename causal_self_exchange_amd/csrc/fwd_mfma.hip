@@ -293,7 +293,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a, HeadPa
 
   for (int t = 0; t < ntiles; ++t) {
     const char* lb = smem + (t & 1) * C::kBufBytes;
-    if (t + 1 < ntiles) gload(t + 1);
+    // Prefetch the next tile unconditionally: past the last tile the
+    // descriptor has no records, so the loads return zeros without touching
+    // memory, and no branch separates the loads from the compute below.
+    gload(t + 1);
     int mode = 0;
     if (t >= tfull) {
       const int d = t - 2 * qt;                  // 0 or 1: the two tiles holding diagonals
@@ -307,7 +310,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a, HeadPa
     } else if (mode == 2) {
       tile_step<D, 2>(lb, lb, qf, o, m2, lsum, k2, lq, hf, koff, voff);
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
+    // The other buffer was last read in tile t - 1, before the previous
+    // barrier, so it can be overwritten now (with zeros after the last tile).
+    lstore((t + 1) & 1);
     __syncthreads();
   }
 
