@@ -26,9 +26,9 @@
 //
 // Causal tile skip: a work-group scans only key tiles left of its last row;
 // in the last two tiles a wave skips 32-key blocks right of its diagonal.
-// Grid order: heaviest query tiles first, and when B*H is a multiple of 8,
-// all query tiles of one head go to one XCD (work-groups are dealt to the
-// 8 XCDs round-robin), so the head's P2/V stay in that XCD's L2.
+// Grid order: heaviest query tiles first; when B*H is a multiple of 8 the
+// query tiles of one head run together on one XCD (work-groups are dealt to
+// the 8 XCDs round-robin), so the head's P2/V stay in that XCD's L2.
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -90,14 +90,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufFlags);
 }
 
-// (query tile, b*H + h) of this work-group: heaviest tiles first; one head's
-// tiles on one XCD when the head count allows.
+// (query tile, b*H + h) of this work-group: heaviest tiles first; when the
+// head count allows, each XCD runs the query tiles of one head at a time, so
+// that head's P2/V tiles stay in the XCD's L2.
 __device__ __forceinline__ void tile_of_block(int n, int nq, int BH, int& qt, int& bh) {
   if ((BH & 7) == 0) {
     const int per = BH >> 3;          // heads per XCD
     const int xcd = n & 7, loc = n >> 3;
-    bh = xcd * per + loc % per;
-    qt = nq - 1 - loc / per;
+    bh = xcd * per + loc / nq;
+    qt = nq - 1 - loc % nq;
   } else {
     qt = nq - 1 - n / BH;
     bh = n % BH;
@@ -135,7 +136,8 @@ __device__ __forceinline__ void tile_step(const char* kl, const char* vl, const 
   }
 
   // Key of register r within a 32-key block: 8 (r / 4) + 4 hf + r % 4.
-  float mx = -INFINITY;
+  // Four independent partial maxima keep the dependency chain short.
+  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int kb = 0; kb < kBlocks; ++kb) {
     const bool diag = kb == 0 ? kDiag0 : kDiag1;
@@ -143,10 +145,10 @@ __device__ __forceinline__ void tile_step(const char* kl, const char* vl, const 
     for (int r = 0; r < 16; ++r) {
       float x = s[kb][r];
       if (diag) x = (8 * (r >> 2) + 4 * hf + (r & 3)) < lq ? x : -INFINITY;
-      mx = fmaxf(mx, x);
+      mxp[r & 3] = fmaxf(mxp[r & 3], x);
     }
   }
-  mx = lane_pair_max(mx);
+  float mx = lane_pair_max(fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3])));
   const float mc2 = fmaxf(mx, 0.0f) * k2;
   const float mnew = mc2 > m2 + kLazy ? mc2 : m2;
   if (__any(mnew != m2)) {
@@ -174,13 +176,16 @@ __device__ __forceinline__ void tile_step(const char* kl, const char* vl, const 
       if (diag) p = (8 * (r >> 2) + 4 * hf + (r & 3)) < lq ? p : 0.0f;
       pf[kb][r >> 3][r & 7] = (__bf16)p;
     }
+    // Row-sum share from the bf16 weights; two independent partial sums.
+    float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s01, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s23, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s45, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s67, ones, lsum, false);
+      acc0 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s01, ones, acc0, false);
+      acc1 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s23, ones, acc1, false);
+      acc0 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s45, ones, acc0, false);
+      acc1 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s67, ones, acc1, false);
     }
+    lsum += acc0 + acc1;
   }
 
   // Transport: O^T[d][q] += V^T[d][key] P^T[key][q]; the key order inside an
