@@ -1,34 +1,53 @@
 // bf16 MFMA FlashRelation forward for gfx950 ("Ask Self, Ask Others: Relation
 // Is All You Need", Sec. 5.1, Eq. (12)-(14); App. A.3).
 //
-// Work-group = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows.
-// Key tiles of 64 rows of P2 and V are staged through LDS (double-buffered,
-// row pitch padded so every read address is a lane base plus an immediate,
-// loads through buffer descriptors whose range check zero-fills rows >= T)
-// and shared by the 4 waves. Per tile and wave:
-//   evidence  S^T[key][query] = P2 . P1^T  on v_mfma_f32_32x32x16_bf16; the
-//             transposed product puts one query per lane, so a row's 64
-//             scores sit in one lane pair (l, l^32);
-//   roles     only the diagonal tile removes keys j >= i of the row (Self is
-//             not part of the Exchange scan); Exchange E = SiLU(U) in
-//             registers; every other tile runs without any mask;
-//   scan      running stabiliser m (log2 domain) starting at 0, which is
-//             valid because SiLU(u) <= max(u, 0) and SiLU >= -0.2785, so the
-//             largest weight of a non-empty history is >= e^-0.2785;
-//             m moves only when the tile maximum exceeds it by > 8 (lazy
-//             rescaling); weights p = exp(E - m) go to bf16 and the row sum
-//             is accumulated from those bf16 weights with v_dot2;
-//   transport O^T[d][query] += V^T . P^T on the same MFMA; V^T operands come
-//             straight from the row-major LDS tile via ds_read_b64_tr_b16.
-// Epilogue: Self entry S_i = sigmoid(U_ii / tau) from p1_i . p2_i in fp32,
-// count term lambda log i, and the branch-free Self/Exchange combination;
-// the first row gets Y_1 = V_1 exactly.
+// Work-group = 8 waves = 256 query rows of one (b, h); each wave owns 32 rows,
+// two waves share a SIMD. Key tiles of 64 rows of P2 and V are staged through
+// LDS rings of three slots each and shared by the 8 waves; rows are padded so
+// every LDS read is a lane base plus an immediate and conflict-free; global
+// loads go through buffer descriptors whose range check zero-fills rows >= T.
+//
+// Per 64-key tile and wave the work is
+//   evidence  S^T[key][query] = P2 . P1^T   (v_mfma_f32_32x32x16_bf16; the
+//             transposed product puts one query per lane, so a row's scores
+//             sit in one lane pair (l, l^32));
+//   scan      Exchange weights p = exp(SiLU(u) - m) for keys j < i only (Self is
+//             not part of the scan), in the log2 domain:
+//             a = u log2 e, SiLU(u) log2 e = a / (1 + 2^-a); weights go to bf16
+//             for the transport and the row sum is accumulated in fp32;
+//   transport O^T[d][query] += V^T . P^T   (V^T operands come straight from
+//             the row-major LDS tile via ds_read_b64_tr_b16).
+// The three are software-pipelined across tiles: in iteration j the matrix
+// cores run the transport of tile j-1 and the evidence of tile j+1 while the
+// VALU forms the stabiliser and then the weights of tile j. In the steady
+// state the issue order is fixed in steps of 4 MFMAs, each step also carrying
+// a slice of the VALU work and the LDS reads of the next step's operands.
+// The loop is unrolled by two so the evidence and weight registers of
+// consecutive tiles swap roles by name, not by copies.
+//
+// Staging: iteration j loads P2 tile j+3 and V tile j+1 from global memory and
+// writes them to LDS at its end; the barrier then only waits for those writes,
+// while the first transport operands of iteration j+1 (V tile j, written one
+// iteration earlier) are already being read.
+//
+// Stabiliser: m (log2 domain) starts at 0, which is valid because
+// SiLU(u) <= max(u, 0) and SiLU >= -0.2785, so the largest weight of a
+// non-empty history is >= e^-0.2785; m moves only when a tile's maximum
+// exceeds it by > 8 (lazy rescaling, weights stay <= 2^8). O is brought to a
+// new stabiliser at the end of the iteration that set it, after the transport
+// of the last tile weighted with the old one.
+// Self entry S_i = sigmoid(U_ii / tau) from p1_i . p2_i in fp32 (computed in
+// the prologue), count term lambda log i, and the branch-free Self/Exchange
+// combination in the epilogue; the first row gets Y_1 = V_1 exactly.
 //
 // Causal tile skip: a work-group scans only key tiles left of its last row;
-// in the last two tiles a wave skips 32-key blocks right of its diagonal.
+// near the diagonal a wave skips 32-key blocks right of its diagonal block and
+// masks keys j >= i inside it.
 // Grid order: heaviest query tiles first; when B*H is a multiple of 8 the
 // query tiles of one head run together on one XCD (work-groups are dealt to
 // the 8 XCDs round-robin), so the head's P2/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -44,14 +63,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;          // query rows per work-group
+constexpr int kBM = 256;          // query rows per work-group
 constexpr int kBN = 64;           // keys per LDS tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kSlots = 3;         // LDS ring depth of P2 and of V
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
 constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9)
+
+// Block modes of a 64-key tile for one wave (blocks kb0 = keys 0..31, kb1 = 32..63).
+enum : int {
+  kFull = 0,   // both blocks strictly left of the wave's rows
+  kDiag1 = 1,  // kb0 full, kb1 is the wave's diagonal block
+  kDiag0 = 2,  // kb0 is the diagonal block, kb1 lies to the right
+  kOff = 3     // the whole tile lies to the right (or past the history)
+};
 
 template <int D>
 struct Cfg {
@@ -63,12 +91,27 @@ struct Cfg {
   // V rows: +64 B so the transposed 8-byte reads of 4 rows x 64 B by 32 lanes
   // hit 32 different bank pairs.
   static constexpr int kPitchV = kRowBytes + 64;
-  static constexpr int kKBytes = kBN * kPitchK;
-  static constexpr int kVBytes = kBN * kPitchV;
-  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kKBytes = kBN * kPitchK;      // one P2 slot
+  static constexpr int kVBytes = kBN * kPitchV;      // one V slot
+  static constexpr int kLdsBytes = kSlots * (kKBytes + kVBytes);
   static constexpr int kRowsPerPass = kThreads / kChunks;   // staging rows per pass
   static constexpr int kLoads = kBN / kRowsPerPass;
+  static constexpr int kDs = D / 16;                        // evidence MFMA k-steps
+  static constexpr int kDb = D / 32;                        // 32-row blocks of O^T
+  static constexpr int kPV = 2 * 2 * kDb;                   // transport MFMAs per tile
+  static constexpr int kQK = 2 * kDs;                       // evidence MFMAs per tile
+  static constexpr int kSteps = (kPV + kQK) / 4;            // steady-state steps
+  static_assert(kPV >= 4 && (kPV + kQK) % 4 == 0, "step layout");
+  static_assert(kPV == 4 * (kSteps / 2) && kSteps >= 4, "evidence chains start at step kSteps / 2");
 };
+
+// s_waitcnt with only the LDS/scalar counter constrained (gfx9 encoding:
+// vmcnt 63, expcnt 7, lgkmcnt n).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
 
 __device__ __forceinline__ float lane_pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -91,8 +134,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long lo
 }
 
 // (query tile, b*H + h) of this work-group: heaviest tiles first; when the
-// head count allows, each XCD runs the query tiles of one head at a time, so
-// that head's P2/V tiles stay in the XCD's L2.
+// head count allows, each XCD runs the query tiles of one head at a time.
 __device__ __forceinline__ void tile_of_block(int n, int nq, int BH, int& qt, int& bh) {
   if ((BH & 7) == 0) {
     const int per = BH >> 3;          // heads per XCD
@@ -105,113 +147,144 @@ __device__ __forceinline__ void tile_of_block(int n, int nq, int BH, int& qt, in
   }
 }
 
-// Block modes of a 64-key tile for one wave (blocks kb0 = keys 0..31, kb1 = 32..63):
-//   0: both blocks strictly left of the wave's rows (no mask);
-//   1: kb0 full, kb1 is the wave's diagonal block;
-//   2: kb0 is the diagonal block, kb1 lies to the right (skipped).
-template <int D, int MODE>
-__device__ __forceinline__ void tile_step(const char* kl, const char* vl, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&o)[D / 32], float& m2, float& lsum, float k2,
-                                          int lq, int hf, int koff, int voff) {
+// Mode of tile t (key blocks 2t, 2t+1) for the wave whose diagonal block is dblk.
+__device__ __forceinline__ int tile_mode(int t, int ntiles, int dblk) {
+  if (t < 0 || t >= ntiles) return kOff;
+  const int b0 = 2 * t;
+  if (b0 + 1 < dblk) return kFull;
+  if (b0 + 1 == dblk) return kDiag1;
+  return b0 == dblk ? kDiag0 : kOff;
+}
+
+__device__ __forceinline__ bool blk_active(int mode, int kb) {
+  return mode == kFull || mode == kDiag1 || (mode == kDiag0 && kb == 0);
+}
+__device__ __forceinline__ bool blk_diag(int mode, int kb) {
+  return (mode == kDiag1 && kb == 1) || (mode == kDiag0 && kb == 0);
+}
+
+// Evidence of one 32-key block: s = P2[kb] . P1^T.
+template <int D>
+__device__ __forceinline__ f32x16 evidence_block(const char* kl, int kb, const bf16x8 (&qf)[D / 16]) {
   using C = Cfg<D>;
-  constexpr int kDs = D / 16;
-  constexpr int kDb = D / 32;
-  constexpr int kBlocks = MODE == 2 ? 1 : 2;
-  constexpr bool kDiag0 = MODE == 2;
-  constexpr bool kDiag1 = MODE == 1;
-
-  f32x16 s[2];
+  f32x16 s;
 #pragma unroll
-  for (int kb = 0; kb < kBlocks; ++kb) {
-#pragma unroll
-    for (int ds = 0; ds < kDs; ++ds) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff + kb * 32 * C::kPitchK + ds * 32);
-      if (ds == 0) {
-        const f32x16 zero = {};
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], zero, 0, 0, 0);
-      } else {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
-      }
+  for (int ds = 0; ds < C::kDs; ++ds) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kb * 32 * C::kPitchK + ds * 32);
+    if (ds == 0) {
+      const f32x16 zero = {};
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], zero, 0, 0, 0);
+    } else {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s, 0, 0, 0);
     }
   }
+  return s;
+}
 
-  // Key of register r within a 32-key block: 8 (r / 4) + 4 hf + r % 4.
-  // Four independent partial maxima keep the dependency chain short.
-  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-  for (int kb = 0; kb < kBlocks; ++kb) {
-    const bool diag = kb == 0 ? kDiag0 : kDiag1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[kb][r];
-      if (diag) x = (8 * (r >> 2) + 4 * hf + (r & 3)) < lq ? x : -INFINITY;
-      mxp[r & 3] = fmaxf(mxp[r & 3], x);
-    }
-  }
-  float mx = lane_pair_max(fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3])));
-  const float mc2 = fmaxf(mx, 0.0f) * k2;
-  const float mnew = mc2 > m2 + kLazy ? mc2 : m2;
-  if (__any(mnew != m2)) {
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-    lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < kDb; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    m2 = mnew;
-  }
+// Transposed V operand of transport MFMA i = (block kb, k-step ks, O^T block db);
+// the key order inside an MFMA k-step matches the register order of the
+// evidence tile.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* vl, int i) {
+  using C = Cfg<D>;
+  const int kb = i / (2 * C::kDb), ks = (i / C::kDb) % 2, db = i % C::kDb;
+  const char* p = vl + (kb * 32 + 16 * ks) * C::kPitchV + 64 * db;
+  bf16x8 vf;
+  vf.lo = lds_tr_read(p);
+  vf.hi = lds_tr_read(p + 8 * C::kPitchV);
+  return vf;
+}
 
-  // Exchange weights p = exp(SiLU(u) - m) with a = u log2 e:
-  // SiLU(u) log2 e = a / (1 + 2^-a).
-  bf16x8 pf[2][2];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+// Transport of one 32-key block: O^T[d][q] += V^T[d][key] P^T[key][q].
+template <int D>
+__device__ __forceinline__ void transport_block(const char* vl, int kb, const u32x4 (&pf)[2],
+                                                f32x16 (&o)[D / 32]) {
+  using C = Cfg<D>;
 #pragma unroll
-  for (int kb = 0; kb < kBlocks; ++kb) {
-    const bool diag = kb == 0 ? kDiag0 : kDiag1;
+  for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float av = s[kb][r] * k2;
-      const float den = 1.0f + __builtin_amdgcn_exp2f(-av);
-      float p = __builtin_amdgcn_exp2f(av * __builtin_amdgcn_rcpf(den) - m2);
-      if (diag) p = (8 * (r >> 2) + 4 * hf + (r & 3)) < lq ? p : 0.0f;
-      pf[kb][r >> 3][r & 7] = (__bf16)p;
-    }
-    // Row-sum share from the bf16 weights; two independent partial sums.
-    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      acc0 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s01, ones, acc0, false);
-      acc1 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s23, ones, acc1, false);
-      acc0 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s45, ones, acc0, false);
-      acc1 = __builtin_amdgcn_fdot2_f32_bf16(pf[kb][ks].s67, ones, acc1, false);
-    }
-    lsum += acc0 + acc1;
-  }
-
-  // Transport: O^T[d][q] += V^T[d][key] P^T[key][q]; the key order inside an
-  // MFMA k-step matches the register order of the evidence tile.
-#pragma unroll
-  for (int kb = 0; kb < kBlocks; ++kb) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int db = 0; db < kDb; ++db) {
-        const char* p = vl + voff + (kb * 32 + 16 * ks) * C::kPitchV + 64 * db;
-        bf16x8 vf;
-        vf.lo = lds_tr_read(p);
-        vf.hi = lds_tr_read(p + 8 * C::kPitchV);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][ks], o[db], 0, 0, 0);
-      }
+    for (int db = 0; db < C::kDb; ++db) {
+      const bf16x8 vf = v_operand<D>(vl, kb * 2 * C::kDb + ks * C::kDb + db);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pf[ks]), o[db], 0, 0, 0);
     }
   }
 }
 
+// Exchange weight of one score (log2 domain): 2^(a / (1 + 2^-a) - m2), a = s k2.
+__device__ __forceinline__ float exch_weight(float s, float k2, float m2) {
+  const float av = s * k2;
+  const float den = 1.0f + __builtin_amdgcn_exp2f(-av);
+  return __builtin_amdgcn_exp2f(av * __builtin_amdgcn_rcpf(den) - m2);
+}
+
+// Two weights as one packed bf16 pair (round to nearest even).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// Exchange weights of one 32-key block into packed bf16 transport operands
+// (register r of the evidence tile -> operand r / 8, element r % 8) and the
+// row-sum share (fp32 adds into four partial sums).
+template <bool kMasked>
+__device__ __forceinline__ void weights_block(const f32x16& s, float k2, float m2, int hf, int lq,
+                                              u32x4 (&pf)[2], float& lsum) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    float w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      w[e] = exch_weight(s[r + e], k2, m2);
+      // Key of register r within the block: 8 (r / 4) + 4 hf + r % 4.
+      if (kMasked) w[e] = (8 * ((r + e) >> 2) + 4 * hf + ((r + e) & 3)) < lq ? w[e] : 0.0f;
+      acc[(r + e) & 3] += w[e];
+    }
+    pf[r >> 3][(r & 7) >> 1] = pack_bf16(w[0], w[1]);
+  }
+  lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <bool kMasked>
+__device__ __forceinline__ float block_max(const f32x16& s, int hf, int lq) {
+  // Four independent partial maxima keep the dependency chain short.
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = s[r];
+    if (kMasked) x = (8 * (r >> 2) + 4 * hf + (r & 3)) < lq ? x : -INFINITY;
+    mx[r & 3] = fmaxf(mx[r & 3], x);
+  }
+  return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+}
+
+// Lazy stabiliser update from a tile's raw maximum: returns the factor the
+// accumulated O and row sum must be multiplied by (1 if m does not move).
+__device__ __forceinline__ float stabilise(float mx, float k2, float& m2) {
+  mx = lane_pair_max(mx);
+  const float mc2 = fmaxf(mx, 0.0f) * k2;
+  const float mnew = mc2 > m2 + kLazy ? mc2 : m2;
+  const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+  m2 = mnew;
+  return alpha;
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a, HeadParams hp) {
+__device__ __forceinline__ void rescale(f32x16 (&o)[D / 32], float alpha) {
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadParams hp) {
   using C = Cfg<D>;
-  constexpr int kDs = D / 16;
-  constexpr int kDb = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
+  char* const kbase = smem;                          // P2 ring: tile t in slot t % 3
+  char* const vbase = smem + kSlots * C::kKBytes;    // V ring:  tile t in slot t % 3
 
   const int T = a.T;
   const int nq = (T + kBM - 1) / kBM;
@@ -230,112 +303,315 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const auto rY = rsrc(Y, head_bytes);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;                      // query (column) within the wave
   const int hf = lane >> 5;                      // lane half
   const int q0 = qt * kBM;
   const int qrow = q0 + wave * 32 + lq;          // may be >= T: loads give 0, stores drop
+  const int dblk = q0 / 32 + wave;               // the wave's diagonal 32-key block
 
-  // P1 rows as the evidence MFMA's B operand: lane holds p1[qrow][16 ds + 8 hf + 0..7].
+  // P1 rows as the evidence MFMA's B operand: lane holds p1[qrow][16 ds + 8 hf + 0..7];
+  // the same chunks of p2[qrow] give the Self evidence p1_i . p2_i.
   const int qoff = qrow * (D * 2) + hf * 16;
-  bf16x8 qf[kDs];
+  bf16x8 qf[C::kDs];
+  float dself = 0.0f;
+  {
+    bf16x8 kv[C::kDs];
 #pragma unroll
-  for (int ds = 0; ds < kDs; ++ds)
-    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
+    for (int ds = 0; ds < C::kDs; ++ds) {
+      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
+      kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
+    }
+#pragma unroll
+    for (int ds = 0; ds < C::kDs; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[ds][e], dself);
+  }
 
-  f32x16 o[kDb];
-#pragma unroll
-  for (int db = 0; db < kDb; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m2 = 0.0f;                               // stabiliser, log2 domain
-  float lsum = 0.0f;                             // this lane's share of the row sum
   const float k2 = hp.scale * kLog2e;            // raw dot -> log2-domain evidence
 
   // Keys 0 .. kend-1 are history for some row of this tile.
   const int kend = min(q0 + kBM, T) - 1;
   const int ntiles = (kend + kBN - 1) / kBN;
-  const int tfull = min(2 * qt, ntiles);         // tiles left of every wave's diagonal
 
   // Staging: pass `it` moves rows it * kRowsPerPass + tid / kChunks, chunk tid % kChunks.
   const int srow = tid / C::kChunks, sch = tid % C::kChunks;
   const int goff = srow * (D * 2) + sch * 16;
   const int kwoff = srow * C::kPitchK + sch * 16;
-  const int vwoff = C::kKBytes + srow * C::kPitchV + sch * 16;
-  u32x4 kreg[C::kLoads], vreg[C::kLoads];
-  auto gload = [&](int t) {
-    const long long base = (long long)t * kBN * D * 2;
-    const auto rK = rsrc(P2 + (size_t)t * kBN * D, head_bytes - base);
-    const auto rVt = rsrc(V + (size_t)t * kBN * D, head_bytes - base);
+  const int vwoff = srow * C::kPitchV + sch * 16;
+  // Tiles past the last one a work-group needs get an empty descriptor: the
+  // loads still issue (and return zeros) but move no data.
+  auto gload = [&](const __bf16* base, int t, u32x4 (&r)[C::kLoads]) {
+    const long long off = (long long)t * kBN * D * 2;
+    const auto rs = rsrc(base + (size_t)t * kBN * D, t < ntiles ? head_bytes - off : 0);
 #pragma unroll
-    for (int it = 0; it < C::kLoads; ++it) {
-      kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(rK, goff + it * C::kRowsPerPass * D * 2, 0, 0);
-      vreg[it] = __builtin_amdgcn_raw_buffer_load_b128(rVt, goff + it * C::kRowsPerPass * D * 2, 0, 0);
-    }
+    for (int it = 0; it < C::kLoads; ++it)
+      r[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, goff + it * C::kRowsPerPass * D * 2, 0, 0);
   };
-  auto lstore = [&](int buf) {
-    char* b = smem + buf * C::kBufBytes;
+  auto lstore_k = [&](int t, const u32x4 (&r)[C::kLoads]) {
+    char* b = kbase + (t % kSlots) * C::kKBytes + kwoff;
 #pragma unroll
-    for (int it = 0; it < C::kLoads; ++it) {
-      *reinterpret_cast<u32x4*>(b + kwoff + it * C::kRowsPerPass * C::kPitchK) = kreg[it];
-      *reinterpret_cast<u32x4*>(b + vwoff + it * C::kRowsPerPass * C::kPitchV) = vreg[it];
-    }
+    for (int it = 0; it < C::kLoads; ++it) *reinterpret_cast<u32x4*>(b + it * C::kRowsPerPass * C::kPitchK) = r[it];
   };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  auto lstore_v = [&](int t, const u32x4 (&r)[C::kLoads]) {
+    char* b = vbase + (t % kSlots) * C::kVBytes + vwoff;
+#pragma unroll
+    for (int it = 0; it < C::kLoads; ++it) *reinterpret_cast<u32x4*>(b + it * C::kRowsPerPass * C::kPitchV) = r[it];
+  };
 
   // Lane-constant read offsets: evidence operand rows (lq, chunk hf) and the
   // transposed V read (16-lane group g supplies rows 4 (g / 2) + i / 4 and
   // columns 16 (g % 2) + 4 (i % 4), i = lane % 16).
   const int koff = lq * C::kPitchK + hf * 16;
   const int tg = lane >> 4, ti = lane & 15;
-  const int voff = C::kKBytes + (4 * (tg >> 1) + (ti >> 2)) * C::kPitchV + (16 * (tg & 1) + 4 * (ti & 3)) * 2;
+  const int voff = (4 * (tg >> 1) + (ti >> 2)) * C::kPitchV + (16 * (tg & 1) + 4 * (ti & 3)) * 2;
+  // Per-lane read bases of the slot holding tile t. The base is formed once
+  // per use site in a register (opaque to the optimiser), so every operand
+  // read is that register plus an immediate; otherwise the compiler hoists a
+  // separate loop-invariant address per immediate and runs out of registers.
+  auto kslot = [&](int t) -> const char* {
+    unsigned off = (unsigned)(kbase - smem) + (unsigned)((t % kSlots) * C::kKBytes + koff);
+    asm volatile("" : "+v"(off));
+    return smem + off;
+  };
+  auto vslot = [&](int t) -> const char* {
+    unsigned off = (unsigned)(vbase - smem) + (unsigned)((t % kSlots) * C::kVBytes + voff);
+    asm volatile("" : "+v"(off));
+    return smem + off;
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const char* lb = smem + (t & 1) * C::kBufBytes;
-    // Prefetch the next tile unconditionally: past the last tile the
-    // descriptor has no records, so the loads return zeros without touching
-    // memory, and no branch separates the loads from the compute below.
-    gload(t + 1);
-    int mode = 0;
-    if (t >= tfull) {
-      const int d = t - 2 * qt;                  // 0 or 1: the two tiles holding diagonals
-      const int w = wave - 2 * d;                // wave's diagonal block relative to the tile
-      mode = w < 0 ? 3 : (w == 0 ? 2 : (w == 1 ? 1 : 0));
-    }
-    if (mode == 0) {
-      tile_step<D, 0>(lb, lb, qf, o, m2, lsum, k2, lq, hf, koff, voff);
-    } else if (mode == 1) {
-      tile_step<D, 1>(lb, lb, qf, o, m2, lsum, k2, lq, hf, koff, voff);
-    } else if (mode == 2) {
-      tile_step<D, 2>(lb, lb, qf, o, m2, lsum, k2, lq, hf, koff, voff);
-    }
-    // The other buffer was last read in tile t - 1, before the previous
-    // barrier, so it can be overwritten now (with zeros after the last tile).
-    lstore((t + 1) & 1);
-    __syncthreads();
+  // Prologue: P2 tiles 0..2 and V tile 0 into their slots, evidence of tile 0.
+  {
+    u32x4 r0[C::kLoads], r1[C::kLoads], r2[C::kLoads], r3[C::kLoads];
+    gload(P2, 0, r0);
+    gload(P2, 1, r1);
+    gload(P2, 2, r2);
+    gload(V, 0, r3);
+    lstore_k(0, r0);
+    lstore_k(1, r1);
+    lstore_k(2, r2);
+    lstore_v(0, r3);
   }
+  __syncthreads();
+  // Evidence of tile j (s_cur, per 32-key block) and packed bf16 weights of
+  // tile j-1 (p_prev, per block and MFMA k-step) on entry to iteration j.
+  f32x16 s_cur[2];
+  u32x4 p_prev[2][2];
+  {
+    const int md = tile_mode(0, ntiles, dblk);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (blk_active(md, kb)) {
+        s_cur[kb] = evidence_block<D>(kslot(0), kb, qf);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_cur[kb][r] = 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) p_prev[kb][ks] = u32x4{0u, 0u, 0u, 0u};
+  f32x16 o[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m2 = 0.0f;                               // stabiliser, log2 domain
+  float lsum = 0.0f;                             // this lane's share of the row sum
+  constexpr int kRing = 6;                       // operand ring of the steady state:
+  bf16x8 fr[kRing];                              // MFMA i reads fr[i % 6]
+  // P2 slot 0 is rewritten in iteration 0.
+  __syncthreads();
+
+  // Iteration j = 0 .. ntiles (the last one only transports tile ntiles-1).
+  // On entry: m2 = m_{j-1}; O holds tiles <= j-2 (at m_{j-1} once rescaled by
+  // alpha_prev at the start); the row sum holds
+  // tiles <= j-1 at m_{j-1}; LDS holds P2 tiles j+1, j+2 and V tiles j-1, j;
+  // fr[0..3] hold the first transport operands of the steady state.
+  // Every iteration stages two tiles and ends with one barrier, whichever of
+  // the two bodies a wave runs, so the waves of a work-group stay matched.
+  f32x16 s_next[2];
+  u32x4 p_cur[2][2];
+  // O holds tile j-2 at m_{j-2} on entry to iteration j until it is multiplied
+  // by alpha_prev = 2^(m_{j-2} - m_{j-1}) at the start of the iteration (before
+  // the transport of tile j-1, so that no branch splits the iteration body).
+  float alpha_prev = 1.0f;
+  // Staging: iteration j writes P2 tile j+3 into the slot of tile j and V tile
+  // j+1 into the slot of tile j-2 (both last read in iteration j-1).
+  // Iteration end: read the first transport operands of the next iteration,
+  // meet the other waves, and hand the tiles' values on.
+  auto finish = [&](int j, float alpha) __attribute__((always_inline)) {
+    alpha_prev = alpha;
+    // The staging writes must not be reordered after the operand reads below:
+    // the wait before the barrier counts on them being the older LDS operations.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    {
+      const char* vn = vslot(j);   // V tile j, published by the previous barrier
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fr[m] = v_operand<D>(vn, m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Each operand above is two LDS reads: wait for everything older (the
+    // writes), then meet the other waves.
+    wait_lgkm<8>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s_cur[kb] = s_next[kb];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) p_prev[kb][ks] = p_cur[kb][ks];
+    }
+  };
+
+  // Boundary / diagonal iteration: per-block activity and masks.
+  auto generic_iteration = [&](int j) __attribute__((always_inline)) {
+    const char* kl = kslot(j + 1);
+    const char* vl = vslot(j + 2);               // slot of V tile j-1
+    u32x4 kreg[C::kLoads], vreg[C::kLoads];
+    gload(P2, j + 3, kreg);
+    gload(V, j + 1, vreg);
+    rescale<D>(o, alpha_prev);
+    const int md_prev = tile_mode(j - 1, ntiles, dblk);
+    const int md_cur = tile_mode(j, ntiles, dblk);
+    const int md_next = tile_mode(j + 1, ntiles, dblk);
+    float alpha;
+    // Phases run in the order that frees registers soonest: the transport
+    // releases the previous weights, the weights release this tile's scores
+    // before the next tile's evidence is formed.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (blk_active(md_cur, kb))
+        mx = fmaxf(mx, blk_diag(md_cur, kb) ? block_max<true>(s_cur[kb], hf, lq) : block_max<false>(s_cur[kb], hf, lq));
+    alpha = stabilise(mx, k2, m2);
+    lsum *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (blk_active(md_prev, kb)) transport_block<D>(vl, kb, p_prev[kb], o);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (blk_active(md_cur, kb)) {
+        if (blk_diag(md_cur, kb)) weights_block<true>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
+        else weights_block<false>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) p_cur[kb][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (blk_active(md_next, kb)) {
+        s_next[kb] = evidence_block<D>(kl, kb, qf);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.0f;
+      }
+    }
+    lstore_k(j + 3, kreg);
+    lstore_v(j + 1, vreg);
+    finish(j, alpha);
+  };
+
+  // Steady-state iteration (tiles j-1, j, j+1 all strictly left of the wave's
+  // rows): half-steps of 2 MFMAs (transport of tile j-1, then evidence of tile
+  // j+1), each with a slice of VALU work and the LDS reads of the operands two
+  // half-steps ahead. Half-steps 0-1 form tile j's stabiliser, the rest the
+  // weights of tile j: block 0 before the evidence chain of the next tile's
+  // block 0 starts (so that chain can take over its registers), block 1 after.
+  // The staged tiles go to LDS at the end of the transport half, which frees
+  // their registers for the evidence half.
+  auto steady_iteration = [&](int j) __attribute__((always_inline)) {
+    const char* kl = kslot(j + 1);
+    const char* vl = vslot(j + 2);               // slot of V tile j-1
+    u32x4 kreg[C::kLoads], vreg[C::kLoads];
+    gload(P2, j + 3, kreg);
+    gload(V, j + 1, vreg);
+    rescale<D>(o, alpha_prev);
+    float alpha, mx;
+    constexpr int kNH = 2 * C::kSteps;           // half-steps
+    constexpr int kH = C::kPV / 2;               // first evidence half-step
+    auto frag = [&](int i) -> bf16x8 {
+      if (i < C::kPV) return v_operand<D>(vl, i);
+      const int q = i - C::kPV;
+      return *reinterpret_cast<const bf16x8*>(kl + (q / C::kDs) * 32 * C::kPitchK + (q % C::kDs) * 32);
+    };
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < kNH; ++h) {
+      if (h + 2 < kNH) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) fr[(2 * (h + 2) + m) % kRing] = frag(2 * (h + 2) + m);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int i = 2 * h + m;
+        const bf16x8 a_op = fr[i % kRing];
+        if (i < C::kPV) {
+          const int kb = i / (2 * C::kDb), ks = (i / C::kDb) % 2, db = i % C::kDb;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, __builtin_bit_cast(bf16x8, p_prev[kb][ks]), o[db], 0, 0, 0);
+        } else {
+          const int q = i - C::kPV, kb = q / C::kDs, ds = q % C::kDs;
+          if (ds == 0) {
+            const f32x16 zero = {};
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, qf[0], zero, 0, 0, 0);
+          } else {
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, qf[ds], s_next[kb], 0, 0, 0);
+          }
+        }
+      }
+      if (h == 0) {
+        mx = fmaxf(block_max<false>(s_cur[0], hf, lq), block_max<false>(s_cur[1], hf, lq));
+      } else if (h == 1) {
+        alpha = stabilise(mx, k2, m2);
+        lsum *= alpha;
+      } else {
+        // Score pairs of this half-step (pair n = registers 2n, 2n+1 of block n / 8).
+        const int n0 = h < kH ? 8 * (h - 2) / (kH - 2) : 8 + 8 * (h - kH) / (kNH - kH);
+        const int n1 = h < kH ? 8 * (h - 1) / (kH - 2) : 8 + 8 * (h + 1 - kH) / (kNH - kH);
+#pragma unroll
+        for (int n = n0; n < n1; ++n) {
+          const int kb = n >> 3, r = 2 * (n & 7);
+          const float w0 = exch_weight(s_cur[kb][r], k2, m2);
+          const float w1 = exch_weight(s_cur[kb][r + 1], k2, m2);
+          acc[r & 3] += w0;
+          acc[(r + 1) & 3] += w1;
+          p_cur[kb][r >> 3][(r & 7) >> 1] = pack_bf16(w0, w1);
+        }
+      }
+      if (h == kH - 1) {
+        lstore_k(j + 3, kreg);
+        lstore_v(j + 1, vreg);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    finish(j, alpha);
+  };
+
+  // A wave's steady iterations are j = 1 .. jE-1: tile j+1 must lie strictly
+  // left of its diagonal block (2 (j+1) + 1 < dblk) and inside the history.
+  const int jE = dblk >= 2 ? max(1, min(ntiles - 1, (dblk - 2) / 2)) : 1;
+  generic_iteration(0);
+  int j = 1;
+  for (; j < jE; ++j) steady_iteration(j);
+  for (; j <= ntiles; ++j) generic_iteration(j);
 
   // ---- epilogue -------------------------------------------------------------
   lsum = lane_pair_sum(lsum);
-  float dself = 0.0f;
-#pragma unroll
-  for (int ds = 0; ds < kDs; ++ds) {
-    const bf16x8 kv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[e], dself);
-  }
   dself = lane_pair_sum(dself);
   const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
   const int roff = qrow * (D * 2) + hf * 8;
 #pragma unroll
-  for (int db = 0; db < kDb; ++db) {
+  for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int boff = roff + (32 * db + 8 * g4) * 2;
