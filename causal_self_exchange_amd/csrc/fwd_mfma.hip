@@ -67,7 +67,8 @@ constexpr int kBM = 256;          // query rows per work-group
 constexpr int kBN = 64;           // keys per LDS tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kSlots = 3;         // LDS ring depth of P2 and of V
+constexpr int kKSlots = 3;        // LDS ring depth of P2 (tile t in slot t % 3)
+constexpr int kVSlots = 4;        // LDS ring depth of V (tile t in slot t % 4)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
@@ -81,21 +82,27 @@ enum : int {
   kOff = 3     // the whole tile lies to the right (or past the history)
 };
 
+// LDS tiles are filled by direct global->LDS loads (buffer_load ... lds): one
+// wave instruction writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so a
+// tile is stored as blocks of 8 rows x 8 sixteen-byte chunks (8 x 128 bytes of
+// global memory per instruction). The order inside a block and the block
+// stride make every operand read a lane base plus an immediate and free of
+// bank conflicts:
+//   P2 block: position rr + 8 cc (chunk-major), block stride 1152 bytes, so
+//             the two 8-row blocks read by 16 lanes sit 128 bytes apart in the
+//             bank space;
+//   V block:  position 8 rr + (cc ^ 4 ((rr >> 1) & 1)) (row-major, chunk bit 2
+//             flipped on every other row pair), block stride 1024 bytes.
 template <int D>
 struct Cfg {
   static constexpr int kChunks = D / 8;              // 16-byte chunks per row
-  static constexpr int kRowBytes = D * 2;
-  // P2 rows: +16 B so 16 consecutive rows start in 16 different bank groups
-  // (conflict-free 16-byte evidence-operand reads by 16 lanes).
-  static constexpr int kPitchK = kRowBytes + 16;
-  // V rows: +64 B so the transposed 8-byte reads of 4 rows x 64 B by 32 lanes
-  // hit 32 different bank pairs.
-  static constexpr int kPitchV = kRowBytes + 64;
-  static constexpr int kKBytes = kBN * kPitchK;      // one P2 slot
-  static constexpr int kVBytes = kBN * kPitchV;      // one V slot
-  static constexpr int kLdsBytes = kSlots * (kKBytes + kVBytes);
-  static constexpr int kRowsPerPass = kThreads / kChunks;   // staging rows per pass
-  static constexpr int kLoads = kBN / kRowsPerPass;
+  static constexpr int kBlocks = kChunks;            // 8x8-chunk blocks per 64-row tile
+  static constexpr int kKBlock = 1152;               // P2 block stride
+  static constexpr int kVBlock = 1024;               // V block stride
+  static constexpr int kKBytes = kBlocks * kKBlock;  // one P2 slot
+  static constexpr int kVBytes = kBlocks * kVBlock;  // one V slot
+  static constexpr int kLdsBytes = kKSlots * kKBytes + kVSlots * kVBytes;
+  static constexpr int kDmaPerWave = kBlocks / kWaves;      // blocks per wave per tile and operand
   static constexpr int kDs = D / 16;                        // evidence MFMA k-steps
   static constexpr int kDb = D / 32;                        // 32-row blocks of O^T
   static constexpr int kPV = 2 * 2 * kDb;                   // transport MFMAs per tile
@@ -103,14 +110,45 @@ struct Cfg {
   static constexpr int kSteps = (kPV + kQK) / 4;            // steady-state steps
   static_assert(kPV >= 4 && (kPV + kQK) % 4 == 0, "step layout");
   static_assert(kPV == 4 * (kSteps / 2) && kSteps >= 4, "evidence chains start at step kSteps / 2");
+  static_assert(kBlocks % kWaves == 0, "each wave moves whole blocks");
+  // Byte offset of evidence operand (block kb, k-step ds) from the lane base.
+  static constexpr int k_imm(int kb, int ds) { return 8 * kKBlock * (ds / 4) + 4 * kKBlock * kb + 256 * (ds % 4); }
+  // Byte offset of the 8-row group `half` of transport operand (kb, ks, db).
+  static constexpr int v_imm(int kb, int ks, int db, int half) {
+    return kVBlock * (8 * (db >> 1) + 4 * kb + 2 * ks + half);
+  }
 };
 
-// s_waitcnt with only the LDS/scalar counter constrained (gfx9 encoding:
-// vmcnt 63, expcnt 7, lgkmcnt n).
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+// Lane read bases of one V slot: transport operands of even / odd 32-row O^T
+// blocks (db) differ in the flipped chunk bit.
+struct VBase {
+  const char* even;
+  const char* odd;
+};
+
+// s_waitcnt vmcnt(VM) lgkmcnt(LGKM), expcnt unconstrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Raw buffer descriptor as four words (base, stride 0, num_records, flags) for
+// use in inline assembly.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, (unsigned)(bytes > 0 ? bytes : 0), (unsigned)kBufFlags};
+}
+
+// One direct global->LDS load: lane l's 16 bytes at voffset go to LDS byte
+// address lds + 16 l (M0 holds lds). Written as inline assembly so that the
+// compiler does not guard every later LDS read with a wait for all
+// outstanding loads; the kernel waits for them explicitly before the barrier
+// that publishes the tile.
+__device__ __forceinline__ void dma16(const u32x4& r, const char* lds, int voffset) {
+  const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ float lane_pair_max(float v) {
@@ -170,7 +208,7 @@ __device__ __forceinline__ f32x16 evidence_block(const char* kl, int kb, const b
   f32x16 s;
 #pragma unroll
   for (int ds = 0; ds < C::kDs; ++ds) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kb * 32 * C::kPitchK + ds * 32);
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + C::k_imm(kb, ds));
     if (ds == 0) {
       const f32x16 zero = {};
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], zero, 0, 0, 0);
@@ -185,19 +223,19 @@ __device__ __forceinline__ f32x16 evidence_block(const char* kl, int kb, const b
 // the key order inside an MFMA k-step matches the register order of the
 // evidence tile.
 template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const char* vl, int i) {
+__device__ __forceinline__ bf16x8 v_operand(const VBase& vb, int i) {
   using C = Cfg<D>;
   const int kb = i / (2 * C::kDb), ks = (i / C::kDb) % 2, db = i % C::kDb;
-  const char* p = vl + (kb * 32 + 16 * ks) * C::kPitchV + 64 * db;
+  const char* p = (db & 1) ? vb.odd : vb.even;
   bf16x8 vf;
-  vf.lo = lds_tr_read(p);
-  vf.hi = lds_tr_read(p + 8 * C::kPitchV);
+  vf.lo = lds_tr_read(p + C::v_imm(kb, ks, db, 0));
+  vf.hi = lds_tr_read(p + C::v_imm(kb, ks, db, 1));
   return vf;
 }
 
 // Transport of one 32-key block: O^T[d][q] += V^T[d][key] P^T[key][q].
 template <int D>
-__device__ __forceinline__ void transport_block(const char* vl, int kb, const u32x4 (&pf)[2],
+__device__ __forceinline__ void transport_block(const VBase& vl, int kb, const u32x4 (&pf)[2],
                                                 f32x16 (&o)[D / 32]) {
   using C = Cfg<D>;
 #pragma unroll
@@ -284,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   char* const kbase = smem;                          // P2 ring: tile t in slot t % 3
-  char* const vbase = smem + kSlots * C::kKBytes;    // V ring:  tile t in slot t % 3
+  char* const vbase = smem + kKSlots * C::kKBytes;   // V ring:  tile t in slot t % 4
 
   const int T = a.T;
   const int nq = (T + kBM - 1) / kBM;
@@ -335,64 +373,68 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const int kend = min(q0 + kBM, T) - 1;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  // Staging: pass `it` moves rows it * kRowsPerPass + tid / kChunks, chunk tid % kChunks.
-  const int srow = tid / C::kChunks, sch = tid % C::kChunks;
-  const int goff = srow * (D * 2) + sch * 16;
-  const int kwoff = srow * C::kPitchK + sch * 16;
-  const int vwoff = srow * C::kPitchV + sch * 16;
+  // Staging: wave w moves blocks k = w + 8 u of a tile; lane l of a P2 block
+  // fetches row 8 (k % 8) + l % 8, chunk 8 (k / 8) + l / 8; lane l of a V block
+  // fetches row 8 (k % 8) + l / 8, chunk 8 (k / 8) + ((l % 8) ^ 4 ((l / 16) & 1)).
   // Tiles past the last one a work-group needs get an empty descriptor: the
-  // loads still issue (and return zeros) but move no data.
-  auto gload = [&](const __bf16* base, int t, u32x4 (&r)[C::kLoads]) {
-    const long long off = (long long)t * kBN * D * 2;
-    const auto rs = rsrc(base + (size_t)t * kBN * D, t < ntiles ? head_bytes - off : 0);
+  // loads still issue (and write zeros) but move no data from memory.
+  const int hb = (int)head_bytes;
+  int dma_koff[C::kDmaPerWave], dma_voff[C::kDmaPerWave];
 #pragma unroll
-    for (int it = 0; it < C::kLoads; ++it)
-      r[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, goff + it * C::kRowsPerPass * D * 2, 0, 0);
+  for (int u = 0; u < C::kDmaPerWave; ++u) {
+    const int k = wave + kWaves * u;
+    dma_koff[u] = (8 * (k % 8) + (lane & 7)) * (D * 2) + 16 * (8 * (k / 8) + (lane >> 3));
+    const int rr = lane >> 3;
+    dma_voff[u] = (8 * (k % 8) + rr) * (D * 2) + 16 * (8 * (k / 8) + ((lane & 7) ^ (4 * ((rr >> 1) & 1))));
+  }
+  auto tile_rsrc = [&](const __bf16* base, int t) {
+    return rsrc_words(base + (size_t)t * kBN * D, t < ntiles ? hb - t * kBN * D * 2 : 0);
   };
-  auto lstore_k = [&](int t, const u32x4 (&r)[C::kLoads]) {
-    char* b = kbase + (t % kSlots) * C::kKBytes + kwoff;
+  auto dma_k = [&](int t) {
+    const auto rs = tile_rsrc(P2, t);
+    char* slot = kbase + (t % kKSlots) * C::kKBytes;
 #pragma unroll
-    for (int it = 0; it < C::kLoads; ++it) *reinterpret_cast<u32x4*>(b + it * C::kRowsPerPass * C::kPitchK) = r[it];
+    for (int u = 0; u < C::kDmaPerWave; ++u) dma16(rs, slot + (wave + kWaves * u) * C::kKBlock, dma_koff[u]);
   };
-  auto lstore_v = [&](int t, const u32x4 (&r)[C::kLoads]) {
-    char* b = vbase + (t % kSlots) * C::kVBytes + vwoff;
+  auto dma_v = [&](int t) {
+    const auto rs = tile_rsrc(V, t);
+    char* slot = vbase + (t & (kVSlots - 1)) * C::kVBytes;
 #pragma unroll
-    for (int it = 0; it < C::kLoads; ++it) *reinterpret_cast<u32x4*>(b + it * C::kRowsPerPass * C::kPitchV) = r[it];
+    for (int u = 0; u < C::kDmaPerWave; ++u) dma16(rs, slot + (wave + kWaves * u) * C::kVBlock, dma_voff[u]);
   };
+  constexpr int kDmaIter = 2 * C::kDmaPerWave;   // direct loads a wave issues per iteration
 
-  // Lane-constant read offsets: evidence operand rows (lq, chunk hf) and the
-  // transposed V read (16-lane group g supplies rows 4 (g / 2) + i / 4 and
-  // columns 16 (g % 2) + 4 (i % 4), i = lane % 16).
-  const int koff = lq * C::kPitchK + hf * 16;
+  // Lane read bases: evidence operand rows (lq, chunk hf) and the transposed V
+  // read (16-lane group g supplies rows 4 (g / 2) + i / 4 and columns
+  // 16 (g % 2) + 4 (i % 4) of each 16-key half, i = lane % 16).
+  const int koff = C::kKBlock * (lq >> 3) + 16 * (lq & 7) + 128 * hf;
   const int tg = lane >> 4, ti = lane & 15;
-  const int voff = (4 * (tg >> 1) + (ti >> 2)) * C::kPitchV + (16 * (tg & 1) + 4 * (ti & 3)) * 2;
+  const int vrr = 4 * (tg >> 1) + (ti >> 2), vcc = 2 * (tg & 1) + ((ti & 3) >> 1), vsw = (vrr >> 1) & 1;
+  const int voff_even = 16 * (8 * vrr + 4 * vsw + vcc) + 8 * (ti & 1);
+  const int voff_odd = 16 * (8 * vrr + 4 * (vsw ^ 1) + vcc) + 8 * (ti & 1);
   // Per-lane read bases of the slot holding tile t. The base is formed once
   // per use site in a register (opaque to the optimiser), so every operand
   // read is that register plus an immediate; otherwise the compiler hoists a
   // separate loop-invariant address per immediate and runs out of registers.
   auto kslot = [&](int t) -> const char* {
-    unsigned off = (unsigned)(kbase - smem) + (unsigned)((t % kSlots) * C::kKBytes + koff);
+    unsigned off = (unsigned)(kbase - smem) + (unsigned)((t % kKSlots) * C::kKBytes + koff);
     asm volatile("" : "+v"(off));
     return smem + off;
   };
-  auto vslot = [&](int t) -> const char* {
-    unsigned off = (unsigned)(vbase - smem) + (unsigned)((t % kSlots) * C::kVBytes + voff);
-    asm volatile("" : "+v"(off));
-    return smem + off;
+  auto vslot = [&](int t) -> VBase {
+    const unsigned slot = (unsigned)(vbase - smem) + (unsigned)((t & (kVSlots - 1)) * C::kVBytes);
+    unsigned e = slot + voff_even, o = slot + voff_odd;
+    asm volatile("" : "+v"(e), "+v"(o));
+    return VBase{smem + e, smem + o};
   };
 
-  // Prologue: P2 tiles 0..2 and V tile 0 into their slots, evidence of tile 0.
-  {
-    u32x4 r0[C::kLoads], r1[C::kLoads], r2[C::kLoads], r3[C::kLoads];
-    gload(P2, 0, r0);
-    gload(P2, 1, r1);
-    gload(P2, 2, r2);
-    gload(V, 0, r3);
-    lstore_k(0, r0);
-    lstore_k(1, r1);
-    lstore_k(2, r2);
-    lstore_v(0, r3);
-  }
+  // Prologue: P2 tiles 0..2 and V tiles 0..1 into their slots, evidence of tile 0.
+  dma_k(0);
+  dma_k(1);
+  dma_k(2);
+  dma_v(0);
+  dma_v(1);
+  wait_vm_lgkm<0, 15>();
   __syncthreads();
   // Evidence of tile j (s_cur, per 32-key block) and packed bf16 weights of
   // tile j-1 (p_prev, per block and MFMA k-step) on entry to iteration j.
@@ -428,36 +470,38 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 
   // Iteration j = 0 .. ntiles (the last one only transports tile ntiles-1).
   // On entry: m2 = m_{j-1}; O holds tiles <= j-2 (at m_{j-1} once rescaled by
-  // alpha_prev at the start); the row sum holds
-  // tiles <= j-1 at m_{j-1}; LDS holds P2 tiles j+1, j+2 and V tiles j-1, j;
-  // fr[0..3] hold the first transport operands of the steady state.
-  // Every iteration stages two tiles and ends with one barrier, whichever of
-  // the two bodies a wave runs, so the waves of a work-group stay matched.
+  // alpha_prev at the start); the row sum holds tiles <= j-1 at m_{j-1};
+  // P2 tile j+1 and V tiles j-1, j are readable in LDS, P2 tile j+2 and V
+  // tile j+1 may still be arriving; fr[0..3] hold the first transport
+  // operands of the steady state.
+  // Every iteration issues the same direct loads and ends with one barrier,
+  // whichever of the two bodies a wave runs, so the waves stay matched.
   f32x16 s_next[2];
   u32x4 p_cur[2][2];
-  // O holds tile j-2 at m_{j-2} on entry to iteration j until it is multiplied
-  // by alpha_prev = 2^(m_{j-2} - m_{j-1}) at the start of the iteration (before
-  // the transport of tile j-1, so that no branch splits the iteration body).
+  // O is multiplied by alpha_prev = 2^(m_{j-2} - m_{j-1}) at the start of
+  // iteration j (before the transport of tile j-1, so that no branch splits
+  // the iteration body).
   float alpha_prev = 1.0f;
-  // Staging: iteration j writes P2 tile j+3 into the slot of tile j and V tile
-  // j+1 into the slot of tile j-2 (both last read in iteration j-1).
+  // Staging: iteration j issues the direct loads of P2 tile j+3 into the slot
+  // of tile j and of V tile j+2 into the slot of tile j-2 (both last read in
+  // iteration j-1); the end of iteration j+1 waits for them.
   // Iteration end: read the first transport operands of the next iteration,
-  // meet the other waves, and hand the tiles' values on.
+  // wait for the previous iteration's direct loads, meet the other waves, and
+  // hand the tiles' values on.
   auto finish = [&](int j, float alpha) __attribute__((always_inline)) {
     alpha_prev = alpha;
-    // The staging writes must not be reordered after the operand reads below:
-    // the wait before the barrier counts on them being the older LDS operations.
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     {
-      const char* vn = vslot(j);   // V tile j, published by the previous barrier
+      const VBase vn = vslot(j);   // V tile j, published by the previous barrier
 #pragma unroll
       for (int m = 0; m < 4; ++m) fr[m] = v_operand<D>(vn, m);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Each operand above is two LDS reads: wait for everything older (the
-    // writes), then meet the other waves.
-    wait_lgkm<8>();
+    // All but this iteration's direct loads have landed in LDS once vmcnt is
+    // down to kDmaIter (vector memory operations complete in order); the
+    // operand reads above (8 LDS reads) may still be in flight.
+    wait_vm_lgkm<kDmaIter, 8>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -472,10 +516,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // Boundary / diagonal iteration: per-block activity and masks.
   auto generic_iteration = [&](int j) __attribute__((always_inline)) {
     const char* kl = kslot(j + 1);
-    const char* vl = vslot(j + 2);               // slot of V tile j-1
-    u32x4 kreg[C::kLoads], vreg[C::kLoads];
-    gload(P2, j + 3, kreg);
-    gload(V, j + 1, vreg);
+    const VBase vl = vslot(j - 1);
+    dma_k(j + 3);
+    dma_v(j + 2);
     rescale<D>(o, alpha_prev);
     const int md_prev = tile_mode(j - 1, ntiles, dblk);
     const int md_cur = tile_mode(j, ntiles, dblk);
@@ -515,8 +558,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
         for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.0f;
       }
     }
-    lstore_k(j + 3, kreg);
-    lstore_v(j + 1, vreg);
     finish(j, alpha);
   };
 
@@ -530,10 +571,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // their registers for the evidence half.
   auto steady_iteration = [&](int j) __attribute__((always_inline)) {
     const char* kl = kslot(j + 1);
-    const char* vl = vslot(j + 2);               // slot of V tile j-1
-    u32x4 kreg[C::kLoads], vreg[C::kLoads];
-    gload(P2, j + 3, kreg);
-    gload(V, j + 1, vreg);
+    const VBase vl = vslot(j - 1);
+    dma_k(j + 3);
+    dma_v(j + 2);
     rescale<D>(o, alpha_prev);
     float alpha, mx;
     constexpr int kNH = 2 * C::kSteps;           // half-steps
@@ -541,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     auto frag = [&](int i) -> bf16x8 {
       if (i < C::kPV) return v_operand<D>(vl, i);
       const int q = i - C::kPV;
-      return *reinterpret_cast<const bf16x8*>(kl + (q / C::kDs) * 32 * C::kPitchK + (q % C::kDs) * 32);
+      return *reinterpret_cast<const bf16x8*>(kl + C::k_imm(q / C::kDs, q % C::kDs));
     };
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -586,10 +626,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
           p_cur[kb][r >> 3][(r & 7) >> 1] = pack_bf16(w0, w1);
         }
       }
-      if (h == kH - 1) {
-        lstore_k(j + 3, kreg);
-        lstore_v(j + 1, vreg);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -603,6 +639,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   int j = 1;
   for (; j < jE; ++j) steady_iteration(j);
   for (; j <= ntiles; ++j) generic_iteration(j);
+  // The last iterations' direct loads (of tiles past the end) must land
+  // before the work-group's LDS is released.
+  wait_vm_lgkm<0, 15>();
 
   // ---- epilogue -------------------------------------------------------------
   lsum = lane_pair_sum(lsum);
@@ -610,16 +649,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
   const int roff = qrow * (D * 2) + hf * 8;
+  // All V-row loads first, then the stores (stores count in vmcnt too, so an
+  // interleaved order would serialise the loads).
+  bf16x4 vv[C::kDb][4];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      vv[db][g4] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rV, roff + (32 * db + 8 * g4) * 2, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int boff = roff + (32 * db + 8 * g4) * 2;
-      const bf16x4 vv = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rV, boff, 0, 0));
       bf16x4 yy;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) yy[e] = (__bf16)(c.w_self * (float)vv[e] + c.w_hist * o[db][4 * g4 + e]);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yy), rY, boff, 0, 0);
+      for (int e = 0; e < 4; ++e) yy[e] = (__bf16)(c.w_self * (float)vv[db][g4][e] + c.w_hist * o[db][4 * g4 + e]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yy), rY, roff + (32 * db + 8 * g4) * 2, 0, 0);
     }
   }
 }
