@@ -564,11 +564,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // Steady-state iteration (tiles j-1, j, j+1 all strictly left of the wave's
   // rows): half-steps of 2 MFMAs (transport of tile j-1, then evidence of tile
   // j+1), each with a slice of VALU work and the LDS reads of the operands two
-  // half-steps ahead. Half-steps 0-1 form tile j's stabiliser, the rest the
-  // weights of tile j: block 0 before the evidence chain of the next tile's
-  // block 0 starts (so that chain can take over its registers), block 1 after.
-  // The staged tiles go to LDS at the end of the transport half, which frees
-  // their registers for the evidence half.
+  // half-steps ahead. Half-steps 0-1 form tile j's stabiliser; the weights of
+  // tile j run as a three-stage pipeline over all half-steps.
   auto steady_iteration = [&](int j) __attribute__((always_inline)) {
     const char* kl = kslot(j + 1);
     const VBase vl = vslot(j - 1);
@@ -583,7 +580,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
       const int q = i - C::kPV;
       return *reinterpret_cast<const bf16x8*>(kl + C::k_imm(q / C::kDs, q % C::kDs));
     };
+    // Half-steps 0 .. kNS-1 start score pairs; pair n starts in the half-step h
+    // with s1_begin(h) <= n < s1_begin(h + 1). Block 0's pairs all start before
+    // the evidence chain of the next tile's block 0 (half-step kH), which can
+    // then take over their registers.
+    constexpr int kNS = kNH - 2;
+    auto s1_begin = [](int h) { return 16 * h / kNS; };
+    static_assert(16 * kH / kNS >= 8, "block 0 consumed before its registers are reused");
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float av[16][2], rc[16][2];
 #pragma unroll
     for (int h = 0; h < kNH; ++h) {
       if (h + 2 < kNH) {
@@ -607,23 +612,42 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
           }
         }
       }
-      if (h == 0) {
-        mx = fmaxf(block_max<false>(s_cur[0], hf, lq), block_max<false>(s_cur[1], hf, lq));
-      } else if (h == 1) {
+      if (h == 0) mx = fmaxf(block_max<false>(s_cur[0], hf, lq), block_max<false>(s_cur[1], hf, lq));
+      if (h == 1) {
         alpha = stabilise(mx, k2, m2);
         lsum *= alpha;
-      } else {
-        // Score pairs of this half-step (pair n = registers 2n, 2n+1 of block n / 8).
-        const int n0 = h < kH ? 8 * (h - 2) / (kH - 2) : 8 + 8 * (h - kH) / (kNH - kH);
-        const int n1 = h < kH ? 8 * (h - 1) / (kH - 2) : 8 + 8 * (h + 1 - kH) / (kNH - kH);
+      }
+      // Weights of score pair n (registers 2n, 2n+1 of block n / 8) in three
+      // stages over consecutive half-steps, so that the instructions of one
+      // half-step do not depend on each other: a = s k2 and 2^-a; then
+      // 1 / (1 + 2^-a); then 2^(a / (1 + 2^-a) - m2) (after the stabiliser
+      // of half-step 1), its row-sum share and bf16 packing.
+      if (h >= 2) {
 #pragma unroll
-        for (int n = n0; n < n1; ++n) {
+        for (int n = s1_begin(h - 2); n < s1_begin(h - 1); ++n) {
           const int kb = n >> 3, r = 2 * (n & 7);
-          const float w0 = exch_weight(s_cur[kb][r], k2, m2);
-          const float w1 = exch_weight(s_cur[kb][r + 1], k2, m2);
+          const float w0 = __builtin_amdgcn_exp2f(av[n][0] * rc[n][0] - m2);
+          const float w1 = __builtin_amdgcn_exp2f(av[n][1] * rc[n][1] - m2);
           acc[r & 3] += w0;
           acc[(r + 1) & 3] += w1;
           p_cur[kb][r >> 3][(r & 7) >> 1] = pack_bf16(w0, w1);
+        }
+      }
+      if (h >= 1 && h - 1 < kNS) {
+#pragma unroll
+        for (int n = s1_begin(h - 1); n < s1_begin(h); ++n)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) rc[n][e] = __builtin_amdgcn_rcpf(1.0f + rc[n][e]);
+      }
+      if (h < kNS) {
+#pragma unroll
+        for (int n = s1_begin(h); n < s1_begin(h + 1); ++n) {
+          const int kb = n >> 3, r = 2 * (n & 7);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            av[n][e] = s_cur[kb][r + e] * k2;
+            rc[n][e] = __builtin_amdgcn_exp2f(-av[n][e]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
