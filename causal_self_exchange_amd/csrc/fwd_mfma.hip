@@ -101,7 +101,8 @@ struct Cfg {
   static constexpr int kVBlock = 1024;               // V block stride
   static constexpr int kKBytes = kBlocks * kKBlock;  // one P2 slot
   static constexpr int kVBytes = kBlocks * kVBlock;  // one V slot
-  static constexpr int kLdsBytes = kKSlots * kKBytes + kVSlots * kVBytes;
+  // + one block that absorbs direct loads of V tiles past the last one needed.
+  static constexpr int kLdsBytes = kKSlots * kKBytes + kVSlots * kVBytes + kVBlock;
   static constexpr int kDmaPerWave = kBlocks / kWaves;      // blocks per wave per tile and operand
   static constexpr int kDs = D / 16;                        // evidence MFMA k-steps
   static constexpr int kDb = D / 32;                        // 32-row blocks of O^T
@@ -171,17 +172,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufFlags);
 }
 
-// (query tile, b*H + h) of this work-group: heaviest tiles first; when the
-// head count allows, each XCD runs the query tiles of one head at a time.
-__device__ __forceinline__ void tile_of_block(int n, int nq, int BH, int& qt, int& bh) {
-  if ((BH & 7) == 0) {
-    const int per = BH >> 3;          // heads per XCD
-    const int xcd = n & 7, loc = n >> 3;
-    bh = xcd * per + loc / nq;
-    qt = nq - 1 - loc % nq;
+// Work item w = (b*H + h, pair pr): the query tiles nq-1-pr and pr of one
+// head, which together scan the same number of key tiles, so every item costs
+// the same. Work-groups are dealt to the 8 XCDs round-robin and a work-group
+// takes items w = blockIdx.x + k * gridDim.x; when both gridDim.x and B*H are
+// multiples of 8, the items an XCD runs all come from its own eighth of the
+// heads, so their P2/V stay in that XCD's L2.
+__device__ __forceinline__ void work_of(int w, int G, int npair, int BH, int& bh, int& pr) {
+  if ((BH & 7) == 0 && (G & 7) == 0) {
+    const int xcd = w & 7, i = w >> 3;
+    bh = xcd * (BH >> 3) + i / npair;
+    pr = i % npair;
   } else {
-    qt = nq - 1 - n / BH;
-    bh = n % BH;
+    bh = w / npair;
+    pr = w % npair;
   }
 }
 
@@ -326,8 +330,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 
   const int T = a.T;
   const int nq = (T + kBM - 1) / kBM;
-  int qt, bh;
-  tile_of_block(blockIdx.x, nq, a.B * a.H, qt, bh);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;                      // query (column) within the wave
+  const int hf = lane >> 5;                      // lane half
+
+  // One query tile (256 rows) of one head, start to finish.
+  auto run_tile = [&](int qt, int bh) __attribute__((always_inline)) {
   const int h = bh % a.H;
   const size_t head = (size_t)bh * (size_t)T * D;
   const long long head_bytes = (long long)T * D * 2;
@@ -337,14 +347,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   __bf16* Y = static_cast<__bf16*>(a.Y) + head;
   const auto rP1 = rsrc(P1, head_bytes);
   const auto rP2 = rsrc(P2, head_bytes);
-  const auto rV = rsrc(V, head_bytes);
   const auto rY = rsrc(Y, head_bytes);
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int lq = lane & 31;                      // query (column) within the wave
-  const int hf = lane >> 5;                      // lane half
   const int q0 = qt * kBM;
   const int qrow = q0 + wave * 32 + lq;          // may be >= T: loads give 0, stores drop
   const int dblk = q0 / 32 + wave;               // the wave's diagonal 32-key block
@@ -372,6 +376,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // Keys 0 .. kend-1 are history for some row of this tile.
   const int kend = min(q0 + kBM, T) - 1;
   const int ntiles = (kend + kBN - 1) / kBN;
+  // V tiles loaded: every key <= kend, so that the last four (which stay in
+  // the ring) hold the V rows of this tile's own queries for the Self term.
+  const int nvt = kend / kBN + 1;
 
   // Staging: wave w moves blocks k = w + 8 u of a tile; lane l of a P2 block
   // fetches row 8 (k % 8) + l % 8, chunk 8 (k / 8) + l / 8; lane l of a V block
@@ -387,20 +394,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     const int rr = lane >> 3;
     dma_voff[u] = (8 * (k % 8) + rr) * (D * 2) + 16 * (8 * (k / 8) + ((lane & 7) ^ (4 * ((rr >> 1) & 1))));
   }
-  auto tile_rsrc = [&](const __bf16* base, int t) {
-    return rsrc_words(base + (size_t)t * kBN * D, t < ntiles ? hb - t * kBN * D * 2 : 0);
-  };
   auto dma_k = [&](int t) {
-    const auto rs = tile_rsrc(P2, t);
+    const auto rs = rsrc_words(P2 + (size_t)t * kBN * D, t < ntiles ? hb - t * kBN * D * 2 : 0);
     char* slot = kbase + (t % kKSlots) * C::kKBytes;
 #pragma unroll
     for (int u = 0; u < C::kDmaPerWave; ++u) dma16(rs, slot + (wave + kWaves * u) * C::kKBlock, dma_koff[u]);
   };
+  // V tiles past nvt go to the sink block, so the ring keeps the last real ones.
+  char* const vsink = vbase + kVSlots * C::kVBytes;
   auto dma_v = [&](int t) {
-    const auto rs = tile_rsrc(V, t);
+    const auto rs = rsrc_words(V + (size_t)t * kBN * D, t < nvt ? hb - t * kBN * D * 2 : 0);
     char* slot = vbase + (t & (kVSlots - 1)) * C::kVBytes;
 #pragma unroll
-    for (int u = 0; u < C::kDmaPerWave; ++u) dma16(rs, slot + (wave + kWaves * u) * C::kVBlock, dma_voff[u]);
+    for (int u = 0; u < C::kDmaPerWave; ++u)
+      dma16(rs, t < nvt ? slot + (wave + kWaves * u) * C::kVBlock : vsink, dma_voff[u]);
   };
   constexpr int kDmaIter = 2 * C::kDmaPerWave;   // direct loads a wave issues per iteration
 
@@ -673,14 +680,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
   const int roff = qrow * (D * 2) + hf * 8;
-  // All V-row loads first, then the stores (stores count in vmcnt too, so an
-  // interleaved order would serialise the loads).
+  // V_i of this lane's row from the V ring (tile qrow / 64 is among the last
+  // four loaded): columns 32 db + 8 g4 + 4 hf .. +3, i.e. half hf of chunk
+  // 4 db + g4 of row qrow % 64 in the block layout.
   bf16x4 vv[C::kDb][4];
+  {
+    const int r = qrow & (kBN - 1);
+    const char* vrow = vbase + ((qrow / kBN) & (kVSlots - 1)) * C::kVBytes + C::kVBlock * (r >> 3) + 8 * hf;
+    const int sw = 4 * (((r & 7) >> 1) & 1);
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db)
+    for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      vv[db][g4] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rV, roff + (32 * db + 8 * g4) * 2, 0, 0));
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 4 * db + g4;
+        vv[db][g4] = *reinterpret_cast<const bf16x4*>(vrow + C::kVBlock * 8 * (c >> 3) + 16 * (8 * (r & 7) + ((c & 7) ^ sw)));
+      }
+  }
+  // Every wave's reads are done before the next tile's loads refill the ring.
+  wait_vm_lgkm<63, 0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) {
@@ -692,14 +711,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yy), rY, roff + (32 * db + 8 * g4) * 2, 0, 0);
     }
   }
+  };
+
+  const int npair = (nq + 1) / 2;
+  const int nwork = a.B * a.H * npair;
+  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
+    int bh, pr;
+    work_of(w, gridDim.x, npair, a.B * a.H, bh, pr);
+    // Heavier tile first; an odd tile count leaves the middle tile alone.
+#pragma nounroll
+    for (int k = 0; k < (pr == nq - 1 - pr ? 1 : 2); ++k) {
+      run_tile(k == 0 ? nq - 1 - pr : pr, bh);
+
+    }
+  }
 }
 
 template <int D>
 hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kBM - 1) / kBM;
-  const long long blocks = (long long)nq * a.B * a.H;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, hp);
+  const long long nwork = (long long)((nq + 1) / 2) * a.B * a.H;
+  if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
+  // One persistent work-group per compute unit (the LDS rings admit one).
+  static int cus[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus[dev] = n > 0 ? n : 1;
+  }
+  const long long grid = nwork < cus[dev] ? nwork : cus[dev];
+  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 
