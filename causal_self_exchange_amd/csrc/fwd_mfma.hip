@@ -1,11 +1,11 @@
 // bf16 MFMA FlashRelation forward for gfx950 ("Ask Self, Ask Others: Relation
 // Is All You Need", Sec. 5.1, Eq. (12)-(14); App. A.3).
 //
-// Work-group = 8 waves = 256 query rows of one (b, h); each wave owns 32 rows,
-// two waves share a SIMD. Key tiles of 64 rows of P2 and V are staged through
-// LDS rings of three slots each and shared by the 8 waves; rows are padded so
-// every LDS read is a lane base plus an immediate and conflict-free; global
-// loads go through buffer descriptors whose range check zero-fills rows >= T.
+// A persistent work-group (8 waves, one per compute unit) takes work items of
+// two query tiles of one head, 256 rows each; each wave owns 32 rows and two
+// waves share a SIMD. Key tiles of 64 rows of P2 and V are moved by direct
+// global->LDS loads into rings of 3 (P2) and 4 (V) slots shared by the 8
+// waves; buffer descriptors zero-fill rows >= T.
 //
 // Per 64-key tile and wave the work is
 //   evidence  S^T[key][query] = P2 . P1^T   (v_mfma_f32_32x32x16_bf16; the
@@ -16,36 +16,28 @@
 //             a = u log2 e, SiLU(u) log2 e = a / (1 + 2^-a); weights go to bf16
 //             for the transport and the row sum is accumulated in fp32;
 //   transport O^T[d][query] += V^T . P^T   (V^T operands come straight from
-//             the row-major LDS tile via ds_read_b64_tr_b16).
+//             the LDS tile via ds_read_b64_tr_b16).
 // The three are software-pipelined across tiles: in iteration j the matrix
 // cores run the transport of tile j-1 and the evidence of tile j+1 while the
 // VALU forms the stabiliser and then the weights of tile j. In the steady
-// state the issue order is fixed in steps of 4 MFMAs, each step also carrying
-// a slice of the VALU work and the LDS reads of the next step's operands.
-// The loop is unrolled by two so the evidence and weight registers of
-// consecutive tiles swap roles by name, not by copies.
-//
-// Staging: iteration j loads P2 tile j+3 and V tile j+1 from global memory and
-// writes them to LDS at its end; the barrier then only waits for those writes,
-// while the first transport operands of iteration j+1 (V tile j, written one
-// iteration earlier) are already being read.
+// state the issue order is fixed in half-steps of 2 MFMAs, each with a slice
+// of the VALU work and the LDS reads of the operands two half-steps ahead.
+// Steady and boundary (diagonal) iterations run in separate loops; each
+// iteration ends with one barrier that publishes the tiles loaded one
+// iteration earlier.
 //
 // Stabiliser: m (log2 domain) starts at 0, which is valid because
 // SiLU(u) <= max(u, 0) and SiLU >= -0.2785, so the largest weight of a
 // non-empty history is >= e^-0.2785; m moves only when a tile's maximum
-// exceeds it by > 8 (lazy rescaling, weights stay <= 2^8). O is brought to a
-// new stabiliser at the end of the iteration that set it, after the transport
-// of the last tile weighted with the old one.
-// Self entry S_i = sigmoid(U_ii / tau) from p1_i . p2_i in fp32 (computed in
-// the prologue), count term lambda log i, and the branch-free Self/Exchange
-// combination in the epilogue; the first row gets Y_1 = V_1 exactly.
+// exceeds it by > 8 (lazy rescaling, weights stay <= 2^8).
+// Self entry S_i = sigmoid(U_ii / tau) from p1_i . p2_i in fp32 (prologue),
+// count term lambda log i, and the branch-free Self/Exchange combination in
+// the epilogue, with V_i read from the V ring; the first row gets Y_1 = V_1
+// exactly.
 //
 // Causal tile skip: a work-group scans only key tiles left of its last row;
 // near the diagonal a wave skips 32-key blocks right of its diagonal block and
 // masks keys j >= i inside it.
-// Grid order: heaviest query tiles first; when B*H is a multiple of 8 the
-// query tiles of one head run together on one XCD (work-groups are dealt to
-// the 8 XCDs round-robin), so the head's P2/V stay in that XCD's L2.
 #include <type_traits>
 
 #include "rel_internal.h"

@@ -2,6 +2,9 @@
 
 kernel_stats(csv): per-kernel call count and average / min / max duration from
 a `rocprofv3 --kernel-trace --stats --output-format csv` kernel_stats file.
+trace_avg(csv, kernel_substr, last_n): mean duration (us) of the last `last_n`
+dispatches of one kernel from a `--kernel-trace` kernel_trace file (the timed
+launches of a run that first warms up).
 counter_avg(csv, kernel_substr, counter): a counter's mean over dispatches of
 one kernel from a `--pmc` counter_collection file.
 traffic(...): HBM bytes per launch of a kernel from FETCH_SIZE / WRITE_SIZE
@@ -23,6 +26,20 @@ def kernel_stats(path: str) -> list[dict]:
                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
                         "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
     return out
+
+
+def trace_avg(path: str, kernel_substr: str, last_n: int) -> dict:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"]:
+                rows.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    durs = [d for _, d in rows[-last_n:]]
+    if not durs:
+        raise ValueError(f"no dispatches of {kernel_substr} in {path}")
+    return {"dispatches": len(rows), "last_n": len(durs), "avg_us": sum(durs) / len(durs),
+            "min_us": min(durs), "max_us": max(durs)}
 
 
 def counter_avg(path: str, kernel_substr: str, counter: str) -> float:
