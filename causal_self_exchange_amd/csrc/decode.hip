@@ -3,10 +3,13 @@
 // cached P2 and information rows.
 //
 // The step is a stream over the cache, so it is split along the history:
-//   decode_partial: one work-group per (chunk of kDecodeChunk cached rows,
-//     head, sequence) scans its rows' Exchange entries and leaves a partial
-//     state (m, l, z[d_h]) in the workspace. Each row is read by d_h/VEC
-//     lanes with 16-byte loads, so a wave reads whole 256-byte rows.
+//   decode_partial: one work-group per (kDecodeRows cached rows, head,
+//     sequence) scans its rows' Exchange entries and leaves a partial state
+//     (m, l, z[d_h]) in the workspace. Each row is read by d_h/VEC lanes with
+//     16-byte loads, so a wave reads whole rows; every row group keeps kAhead
+//     rows of loads in flight. The scan uses the log2 domain and the lazy
+//     non-negative stabiliser of the forward kernel (m starts at 0 and moves
+//     only when a score exceeds it by more than 2^8).
 //   decode_merge: one wave per (head, sequence) merges the partial states
 //     (the scan update of Eq. (12) applied to whole chunks), adds the Self
 //     entry of the new token and the count term for position L + 1, and
@@ -20,6 +23,11 @@ namespace rel {
 namespace {
 
 constexpr int kPartialThreads = 256;
+constexpr int kDecodeRows = 4 * kDecodeChunk;   // cached rows per partial work-group
+constexpr int kAhead = 4;                       // rows per row group loaded ahead of use
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;
 
 template <typename Tin>
 struct Vec16 {
@@ -47,9 +55,9 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = clamp_len(a.len[b], a.L_cap);
-  const int j_begin = chunk * kDecodeChunk;
+  const int j_begin = chunk * kDecodeRows;
   if (j_begin >= L) return;                         // uniform for the block
-  const int j_end = min(L, j_begin + kDecodeChunk);
+  const int j_end = min(L, j_begin + kDecodeRows);
 
   const int tid = threadIdx.x;
   const int g = tid / LPR;
@@ -65,29 +73,43 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
 #pragma unroll
     for (int e = 0; e < VEC; ++e) { q[e] = to_f32(t.v[e]); z[e] = 0.0f; }
   }
-  float m = kEmptyMax, l = 0.0f;
+  const float k2 = hp.scale * kLog2e;               // raw dot -> log2-domain evidence
+  float m2 = 0.0f, l = 0.0f;                        // stabiliser (log2 domain), row sum
 
-  for (int j = j_begin + g; j < j_end; j += GROUPS) {
-    const Vec16<Tin> kp = load16(cP2 + (size_t)j * D);
-    const Vec16<Tin> kv = load16(cV + (size_t)j * D);
-    float part = 0.0f;
+  for (int j0 = j_begin + g; j0 < j_end; j0 += GROUPS * kAhead) {
+    Vec16<Tin> kp[kAhead], kv[kAhead];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) part = fmaf(q[e], to_f32(kp.v[e]), part);
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-    const float E = silu_f32(part * hp.scale);
-    if (E > m) {
-      const float s = expf(m - E);
-      l *= s;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) z[e] *= s;
-      m = E;
+    for (int u = 0; u < kAhead; ++u) {
+      // Rows past the end re-read the last row; their weight is zero below.
+      const int j = min(j0 + u * GROUPS, j_end - 1);
+      kp[u] = load16(cP2 + (size_t)j * D);
+      kv[u] = load16(cV + (size_t)j * D);
     }
-    const float p = expf(E - m);
-    l += p;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) z[e] = fmaf(p, to_f32(kv.v[e]), z[e]);
+    for (int u = 0; u < kAhead; ++u) {
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part = fmaf(q[e], to_f32(kp[u].v[e]), part);
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+      // SiLU(u) log2 e = a / (1 + 2^-a), a = u log2 e.
+      const float av = part * k2;
+      const float e2 = av * __builtin_amdgcn_rcpf(1.0f + exp2f(-av));
+      const bool valid = j0 + u * GROUPS < j_end;
+      if (valid && e2 > m2 + kLazy) {
+        const float al = exp2f(m2 - e2);
+        l *= al;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) z[e] *= al;
+        m2 = e2;
+      }
+      const float p = valid ? exp2f(e2 - m2) : 0.0f;
+      l += p;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) z[e] = fmaf(p, to_f32(kv[u].v[e]), z[e]);
+    }
   }
+  const float m = m2 * kLn2;                        // natural-log stabiliser of this group
 
   if (sl == 0) { s_m[g] = m; s_l[g] = l; }
 #pragma unroll
@@ -114,38 +136,51 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, HeadPara
   constexpr int PER = (D + 63) / 64;
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int L = clamp_len(a.len[b], a.L_cap);
-  const int nch = (L + kDecodeChunk - 1) / kDecodeChunk;
   const size_t bh = (size_t)b * a.H + h;
-  const float* ws = a.ws + bh * a.n_chunks * (size_t)(D + 2);
-
-  float M = kEmptyMax;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, ws[c * (D + 2)]);
-  float lsum = 0.0f;
-  float zsum[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) zsum[t] = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float* st = ws + c * (D + 2);
-    const float w = expf(st[0] - M);
-    lsum = fmaf(w, st[1], lsum);
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int k = lane + 64 * t;
-      if (k < D) zsum[t] = fmaf(w, st[2 + k], zsum[t]);
-    }
-  }
-
+  // The new token's states do not depend on the partials: load them first.
   const Tin* p1 = static_cast<const Tin*>(a.p1) + bh * D;
   const Tin* p2 = static_cast<const Tin*>(a.p2) + bh * D;
   const Tin* v = static_cast<const Tin*>(a.v) + bh * D;
-  Tin* y = static_cast<Tin*>(a.y) + bh * D;
-  float dself = 0.0f;
+  float p1v[PER], p2v[PER], vv[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int k = lane + 64 * t;
-    if (k < D) dself = fmaf(to_f32(p1[k]), to_f32(p2[k]), dself);
+    p1v[t] = k < D ? to_f32(p1[k]) : 0.0f;
+    p2v[t] = k < D ? to_f32(p2[k]) : 0.0f;
+    vv[t] = k < D ? to_f32(v[k]) : 0.0f;
   }
+  const int L = clamp_len(a.len[b], a.L_cap);
+  const int nch = (L + kDecodeRows - 1) / kDecodeRows;
+  const float* ws = a.ws + bh * a.n_chunks * (size_t)(D + 2);
+
+  // Online merge of the chunk states (the scan update of Eq. (12) applied to
+  // whole chunks); unrolled so that several chunks' loads are in flight.
+  float M = kEmptyMax, lsum = 0.0f;
+  float zsum[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) zsum[t] = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < nch; ++c) {
+    const float* st = ws + c * (D + 2);
+    const float mc = st[0], lc = st[1];
+    float zc[PER];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int k = lane + 64 * t;
+      zc[t] = k < D ? st[2 + k] : 0.0f;
+    }
+    const float Mn = fmaxf(M, mc);
+    const float wo = expf(M - Mn), wc = expf(mc - Mn);
+    lsum = lsum * wo + lc * wc;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) zsum[t] = zsum[t] * wo + zc[t] * wc;
+    M = Mn;
+  }
+
+  Tin* y = static_cast<Tin*>(a.y) + bh * D;
+  float dself = 0.0f;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) dself = fmaf(p1v[t], p2v[t], dself);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dself += __shfl_xor(dself, off);
   const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
@@ -153,7 +188,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, HeadPara
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int k = lane + 64 * t;
-    if (k < D) y[k] = from_f32<Tin>(cmb.w_self * to_f32(v[k]) + cmb.w_hist * zsum[t]);
+    if (k < D) y[k] = from_f32<Tin>(cmb.w_self * vv[t] + cmb.w_hist * zsum[t]);
   }
 }
 
@@ -177,7 +212,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(Tin* cP2, Tin* cV, in
 
 template <typename Tin, int D>
 hipError_t launch_decode_typed(const DecodeArgs& a, const HeadParams& hp, hipStream_t s) {
-  dim3 g1(a.n_chunks, a.H, a.B);
+  // The workspace holds n_chunks (one per kDecodeChunk rows) states per
+  // (b, h); a work-group covers kDecodeRows rows and uses the first entries.
+  dim3 g1((a.L_cap + kDecodeRows - 1) / kDecodeRows, a.H, a.B);
   hipLaunchKernelGGL((decode_partial_kernel<Tin, D>), g1, dim3(kPartialThreads), 0, s, a, hp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
