@@ -3,9 +3,12 @@
 // cached P2 and information rows.
 //
 // The step is a stream over the cache, so it is split along the history:
-//   decode_partial: one work-group per (kDecodeRows cached rows, head,
-//     sequence) scans its rows' Exchange entries and leaves a partial state
-//     (m, l, z[d_h]) in the workspace. Each row is read by d_h/VEC lanes with
+//   decode_partial: n_chunks work-groups per (head, sequence); work-group c
+//     scans the blocks of GROUPS cached rows c, c + n_chunks, c + 2 n_chunks,
+//     ... and leaves a partial state (m, l, z[d_h]) in the workspace. The
+//     interleaving keeps the work-groups of one head sweeping the same part of
+//     the cache together, which streams from HBM faster than each work-group
+//     reading a separate stretch. Each row is read by d_h/VEC lanes with
 //     16-byte loads, so a wave reads whole rows; every row group keeps kAhead
 //     rows of loads in flight. The scan uses the log2 domain and the lazy
 //     non-negative stabiliser of the forward kernel (m starts at 0 and moves
@@ -23,7 +26,6 @@ namespace rel {
 namespace {
 
 constexpr int kPartialThreads = 256;
-constexpr int kDecodeRows = 4 * kDecodeChunk;   // cached rows per partial work-group
 constexpr int kAhead = 4;                       // rows per row group loaded ahead of use
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -54,10 +56,9 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
   __shared__ float s_z[GROUPS][D + 1];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nc = gridDim.x;                         // work-groups per (b, h) = n_chunks
   const int L = clamp_len(a.len[b], a.L_cap);
-  const int j_begin = chunk * kDecodeRows;
-  if (j_begin >= L) return;                         // uniform for the block
-  const int j_end = min(L, j_begin + kDecodeRows);
+  if (chunk * GROUPS >= L) return;                  // no rows here; uniform for the block
 
   const int tid = threadIdx.x;
   const int g = tid / LPR;
@@ -76,12 +77,13 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
   const float k2 = hp.scale * kLog2e;               // raw dot -> log2-domain evidence
   float m2 = 0.0f, l = 0.0f;                        // stabiliser (log2 domain), row sum
 
-  for (int j0 = j_begin + g; j0 < j_end; j0 += GROUPS * kAhead) {
+  const int step = nc * GROUPS;                     // rows between this work-group's blocks
+  for (int j0 = chunk * GROUPS + g; j0 < L; j0 += step * kAhead) {
     Vec16<Tin> kp[kAhead], kv[kAhead];
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       // Rows past the end re-read the last row; their weight is zero below.
-      const int j = min(j0 + u * GROUPS, j_end - 1);
+      const int j = min(j0 + u * step, L - 1);
       kp[u] = load16(cP2 + (size_t)j * D);
       kv[u] = load16(cV + (size_t)j * D);
     }
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
       // SiLU(u) log2 e = a / (1 + 2^-a), a = u log2 e.
       const float av = part * k2;
       const float e2 = av * __builtin_amdgcn_rcpf(1.0f + exp2f(-av));
-      const bool valid = j0 + u * GROUPS < j_end;
+      const bool valid = j0 + u * step < L;
       if (valid && e2 > m2 + kLazy) {
         const float al = exp2f(m2 - e2);
         l *= al;
@@ -149,8 +151,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, HeadPara
     p2v[t] = k < D ? to_f32(p2[k]) : 0.0f;
     vv[t] = k < D ? to_f32(v[k]) : 0.0f;
   }
+  constexpr int GROUPS = kPartialThreads / (D / (16 / (int)sizeof(Tin)));   // rows per block
   const int L = clamp_len(a.len[b], a.L_cap);
-  const int nch = (L + kDecodeRows - 1) / kDecodeRows;
+  // Work-groups that found rows (and wrote a state).
+  const int nch = min(a.n_chunks, (L + GROUPS - 1) / GROUPS);
   const float* ws = a.ws + bh * a.n_chunks * (size_t)(D + 2);
 
   // Online merge of the chunk states (the scan update of Eq. (12) applied to
@@ -212,9 +216,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(Tin* cP2, Tin* cV, in
 
 template <typename Tin, int D>
 hipError_t launch_decode_typed(const DecodeArgs& a, const HeadParams& hp, hipStream_t s) {
-  // The workspace holds n_chunks (one per kDecodeChunk rows) states per
-  // (b, h); a work-group covers kDecodeRows rows and uses the first entries.
-  dim3 g1((a.L_cap + kDecodeRows - 1) / kDecodeRows, a.H, a.B);
+  dim3 g1(a.n_chunks, a.H, a.B);
   hipLaunchKernelGGL((decode_partial_kernel<Tin, D>), g1, dim3(kPartialThreads), 0, s, a, hp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

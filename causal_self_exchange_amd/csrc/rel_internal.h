@@ -35,7 +35,8 @@ struct DecodeArgs {
   int B, H, L_cap, d_h, n_chunks;
 };
 
-// Rows of cache history one decode work-group scans.
+// Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
+// states per (b, h), one per partial work-group.
 constexpr int kDecodeChunk = 256;
 
 // Launchers (return the hipError_t of the launch).
