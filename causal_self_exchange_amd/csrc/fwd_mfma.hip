@@ -38,6 +38,7 @@
 // Causal tile skip: a work-group scans only key tiles left of its last row;
 // near the diagonal a wave skips 32-key blocks right of its diagonal block and
 // masks keys j >= i inside it.
+#include <atomic>
 #include <type_traits>
 
 #include "rel_internal.h"
@@ -348,20 +349,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // P1 rows as the evidence MFMA's B operand: lane holds p1[qrow][16 ds + 8 hf + 0..7];
   // the same chunks of p2[qrow] give the Self evidence p1_i . p2_i.
   const int qoff = qrow * (D * 2) + hf * 16;
-  bf16x8 qf[C::kDs];
-  float dself = 0.0f;
-  {
-    bf16x8 kv[C::kDs];
+  // (The dot product waits until the prologue's tile loads are issued too.)
+  bf16x8 qf[C::kDs], kv[C::kDs];
 #pragma unroll
-    for (int ds = 0; ds < C::kDs; ++ds) {
-      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
-      kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
-    }
-#pragma unroll
-    for (int ds = 0; ds < C::kDs; ++ds)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[ds][e], dself);
+  for (int ds = 0; ds < C::kDs; ++ds) {
+    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
+    kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
   }
+  const float inv_tau = hp.inv_tau[h];
 
   const float k2 = hp.scale * kLog2e;            // raw dot -> log2-domain evidence
 
@@ -433,6 +428,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   dma_k(2);
   dma_v(0);
   dma_v(1);
+  float dself = 0.0f;
+#pragma unroll
+  for (int ds = 0; ds < C::kDs; ++ds)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[ds][e], dself);
   wait_vm_lgkm<0, 15>();
   __syncthreads();
   // Evidence of tile j (s_cur, per 32-key block) and packed bf16 weights of
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // ---- epilogue -------------------------------------------------------------
   lsum = lane_pair_sum(lsum);
   dself = lane_pair_sum(dself);
-  const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
+  const float S = sigmoid_f32(dself * hp.scale * inv_tau);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
   const int roff = qrow * (D * 2) + hf * 8;
   // V_i of this lane's row from the V ring (tile qrow / 64 is among the last
@@ -724,19 +724,22 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kBM - 1) / kBM;
   const long long nwork = (long long)((nq + 1) / 2) * a.B * a.H;
   if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
-  // One persistent work-group per compute unit (the LDS rings admit one).
-  static int cus[64];
+  // One persistent work-group per compute unit (the LDS rings admit one). The
+  // count is cached per device; concurrent first calls store the same value.
+  static std::atomic<int> cus[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cus[dev] == 0) {
+  int n_cu = cus[dev].load(std::memory_order_relaxed);
+  if (n_cu == 0) {
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    cus[dev] = n > 0 ? n : 1;
+    n_cu = n > 0 ? n : 1;
+    cus[dev].store(n_cu, std::memory_order_relaxed);
   }
-  const long long grid = nwork < cus[dev] ? nwork : cus[dev];
+  const long long grid = nwork < n_cu ? nwork : n_cu;
   hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
   return hipGetLastError();
 }
