@@ -27,6 +27,18 @@ Readings taken where the pages leave a choice open:
     its row is the definition's last row on [cache rows; new token]
     ([paper] Eq. (18), App. A.5).
 
+Gradients (``relation_head_bwd`` / ``relation_bwd``): the derivatives of
+sum(Y * dY) with respect to P1, P2, V, tau_S and lambda, by the chain rule
+through the same three equations (the pages give no backward pass; this is
+plain calculus on the definition, written out on the materialised matrices):
+  dV = F^T dY;  dF_ij = dY_i . V_j;  D_i = dY_i . Y_i;  dR = F * (dF - D)
+  dU_ii = dR_ii S_i (1 - S_i) / tau;   dU_ij = dR_ij SiLU'(U_ij)  (j < i)
+  dP1 = dU P2 / sqrt(d_h);  dP2 = dU^T P1 / sqrt(d_h)
+  dtau = -sum_i dR_ii S_i (1 - S_i) U_ii / tau^2;  dlambda = -sum_{j<i} dR_ij log i
+with SiLU'(u) = sigmoid(u) (1 + u (1 - sigmoid(u))). ``row_lse`` gives the
+per-row log normaliser LSE_i = log sum_{j<=i} exp(R_ij) that a training
+forward hands to its backward.
+
 Cross-check routes (exact algebra per the paper; used only to pin this file):
   * ``factorized_head``: Eq. (6)-(9) / App. A.1.2-A.1.6.
   * ``flash_scan_head``: the tiled (m, l, z) Exchange scan, Eq. (12)-(14) /
@@ -39,9 +51,9 @@ import math
 import numpy as np
 
 __all__ = [
-    "sigmoid", "silu", "evidence", "relation_matrix", "flow", "relation_head",
-    "relation_fwd", "relation_rows", "relation_decode", "factorized_head",
-    "flash_scan_head",
+    "sigmoid", "silu", "silu_grad", "evidence", "relation_matrix", "flow", "relation_head",
+    "relation_fwd", "relation_rows", "relation_decode", "row_lse", "relation_head_bwd",
+    "relation_bwd", "factorized_head", "flash_scan_head",
 ]
 
 
@@ -60,6 +72,13 @@ def silu(x):
     """SiLU(x) = x * sigmoid(x): the Exchange map ([paper] Eq. (2))."""
     x = np.asarray(x, dtype=np.float64)
     return x * sigmoid(x)
+
+
+def silu_grad(x):
+    """d SiLU(x) / dx = sigmoid(x) (1 + x (1 - sigmoid(x)))."""
+    x = np.asarray(x, dtype=np.float64)
+    s = sigmoid(x)
+    return s * (1.0 + x * (1.0 - s))
 
 
 def evidence(p1, p2):
@@ -148,6 +167,59 @@ def relation_decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam=0.0):
             P1row[L] = p1[b, h]
             y[b, h] = relation_rows(P1row, P2seq, Vseq, tau[h], lam, [L])[0]
     return y
+
+
+def row_lse(p1, p2, tau, lam=0.0):
+    """LSE_i = log sum_{j<=i} exp(R_ij) per row of one head (natural log)."""
+    R = relation_matrix(p1, p2, tau, lam)
+    mx = np.max(R, axis=1)
+    return mx + np.log(np.sum(np.exp(R - mx[:, None]), axis=1))
+
+
+def relation_head_bwd(p1, p2, v, tau, lam, dy):
+    """Gradients of sum(Y * dy) for one head: (dP1, dP2, dV, dtau, dlambda).
+
+    Chain rule through [paper] Eq. (1)-(3) on the materialised U, R, F.
+    """
+    T, d_h = p1.shape
+    tau = float(tau)
+    U = evidence(p1, p2)
+    F = flow(relation_matrix(p1, p2, tau, lam))
+    Y = F @ v
+    dV = F.T @ dy                                    # Y = F V
+    dF = dy @ v.T
+    D = np.sum(dy * Y, axis=1)                       # sum_j F_ij dF_ij
+    dR = F * (dF - D[:, None])                       # softmax backward; 0 above the diagonal
+    below = np.tril(np.ones((T, T), dtype=bool), k=-1)
+    diag = np.arange(T)
+    dU = np.zeros((T, T))
+    dU[below] = (dR * silu_grad(U))[below]           # Exchange: R_ij = SiLU(U_ij) - lambda log i
+    s = sigmoid(U[diag, diag] / tau)                 # Self: R_ii = sigmoid(U_ii / tau)
+    dU[diag, diag] = dR[diag, diag] * s * (1.0 - s) / tau
+    dP1 = dU @ p2 / math.sqrt(d_h)                   # U = P1 P2^T / sqrt(d_h)
+    dP2 = dU.T @ p1 / math.sqrt(d_h)
+    dtau = float(np.sum(dR[diag, diag] * s * (1.0 - s) * (-U[diag, diag] / tau ** 2)))
+    log_i = np.log(np.arange(1, T + 1, dtype=np.float64))
+    dlam = float(-np.sum(np.where(below, dR, 0.0) * log_i[:, None]))
+    return dP1, dP2, dV, dtau, dlam
+
+
+def relation_bwd(P1, P2, V, tau, lam, dY):
+    """Multi-head gradients: dP1, dP2, dV [B, H, T, d_h], dtau [H] (tau is
+    shared across the batch), dlambda (scalar, shared by every head)."""
+    B, H, T, _ = P1.shape
+    dP1 = np.empty(P1.shape)
+    dP2 = np.empty(P2.shape)
+    dV = np.empty(V.shape)
+    dtau = np.zeros(H)
+    dlam = 0.0
+    for b in range(B):
+        for h in range(H):
+            g = relation_head_bwd(P1[b, h], P2[b, h], V[b, h], tau[h], lam, dY[b, h])
+            dP1[b, h], dP2[b, h], dV[b, h] = g[0], g[1], g[2]
+            dtau[h] += g[3]
+            dlam += g[4]
+    return dP1, dP2, dV, dtau, dlam
 
 
 # ---------------------------------------------------------------------------
