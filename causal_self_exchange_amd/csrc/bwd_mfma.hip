@@ -1,0 +1,448 @@
+// bf16 MFMA backward of the causal Self-Exchange Relation for gfx950
+// ("Ask Self, Ask Others: Relation Is All You Need", Eq. (1)-(3); the
+// FlashRelation backward of App. A.3 recomputes the evidence per tile from the
+// stored per-row log normaliser instead of keeping U, R or F).
+//
+// Two kernels share the tile machinery of the forward (mfma_tile.h); both
+// recompute the Exchange evidence u = p1_i . p2_j / sqrt(d_h) and
+// g = dY_i . V_j per tile and form, for j < i,
+//   F_ij = 2^(SiLU(u) log2 e - L2_i),  L2_i = (LSE_i + lambda log i) log2 e,
+//   W_ij = F_ij (g - D_i) SiLU'(u)      (= dU_ij; SiLU'(u) = s (1 + u (1 - s)))
+// with the row statistics L2_i and D_i = dY_i . Y_i from the prep kernel.
+//
+// dq (query gradient): 8 waves x 32 query rows, key tiles of 64 rows; per tile
+//   U^T[key][q] = P2 . P1^T and G^T[key][q] = V . dY^T (evidence; P1 and dY
+//   rows of the wave's queries in registers), then
+//   dP1^T[d][q] += P2^T[d][key] W^T[key][q] (transport).
+//   LDS per key tile: P2 in the row layout and the transposed layout, V in
+//   the row layout; a ring of 3 tiles, one barrier per tile.
+// dkv (key/value gradients): 4 waves x 32 key rows, query tiles of 64 rows;
+//   per tile U[q][key] = P1 . P2^T and G[q][key] = dY . V^T (P2 and V rows of
+//   the wave's keys in registers), then
+//   dV^T[d][key] += dY^T[d][q] F[q][key] and dP2^T[d][key] += P1^T[d][q] W[q][key].
+//   LDS per query tile: P1 and dY in both layouts plus the tile's row
+//   statistics; a ring of 2 tiles. Two d_h x 32 fp32 accumulators per wave
+//   need one wave per SIMD.
+// The Self entries (diagonal) enter in the epilogues from the prep's
+// statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
+// dV_j += F_jj dY_j.
+#include "mfma_tile.h"
+#include "rel_internal.h"
+#include "rel_device.h"
+
+namespace rel {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = kDqWaves * 64;
+constexpr int kDqRows = kDqWaves * 32;     // query rows per dq work-group
+constexpr int kDqSlots = 3;
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKvRows = kKvWaves * 32;     // key rows per dkv work-group
+constexpr int kKvSlots = 2;
+
+template <int D>
+struct DqCfg : TileLayout<D> {
+  using L = TileLayout<D>;
+  // Slot: [P2 row layout][V row layout][P2 transposed layout].
+  static constexpr int kSlotBytes = 2 * L::kKBytes + L::kVBytes;
+  static constexpr int kLdsBytes = kDqSlots * kSlotBytes;
+  static constexpr int kPer = L::kBlocks / kDqWaves;    // blocks per wave, tile and layout
+  static constexpr int kDmaTile = 3 * kPer;              // direct loads per wave and tile
+  static_assert(L::kBlocks % kDqWaves == 0, "each wave moves whole blocks");
+};
+
+template <int D>
+struct KvCfg : TileLayout<D> {
+  using L = TileLayout<D>;
+  // Slot: [P1 row][dY row][P1 transposed][dY transposed][statistics, 1 KB].
+  static constexpr int kStatOff = 2 * L::kKBytes + 2 * L::kVBytes;
+  static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
+  static constexpr int kLdsBytes = kKvSlots * kSlotBytes;
+  static constexpr int kPer = L::kBlocks / kKvWaves;
+  // Direct loads per wave and tile (wave 0 also moves the statistics; the
+  // waits use the smaller count, which is conservative for wave 0).
+  static constexpr int kDmaTile = 4 * kPer;
+  static_assert(L::kBlocks % kKvWaves == 0, "each wave moves whole blocks");
+  static_assert(kStatTile * 4 == 1024, "statistics of one tile = one direct load");
+};
+
+// Mode of a 32-row block of the scanned operand for a wave whose own 32-row
+// block is `own`: 0 = no pair (i, j) with j < i, 1 = all pairs, 2 = diagonal
+// block (masked inside).
+__device__ __forceinline__ int mode_keys_below(int blk, int own) { return blk < own ? 1 : (blk == own ? 2 : 0); }
+__device__ __forceinline__ int mode_queries_above(int blk, int own) { return blk > own ? 1 : (blk == own ? 2 : 0); }
+
+__device__ __forceinline__ int64_t stat_at(int64_t bh, int nt, int r, int k) {
+  return ((bh * nt + r / kStatRows) * 4 + k) * kStatRows + (r % kStatRows);
+}
+
+// s (1 + u (1 - s)) with s = sigmoid(u): SiLU'(u); and SiLU(u) log2 e.
+struct SiluTerms {
+  float silu2, dsilu;
+  __device__ __forceinline__ SiluTerms(float x, float k2, float c) {
+    const float a2 = x * k2;                                      // u log2 e
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a2));
+    silu2 = a2 * sg;
+    dsilu = sg * fmaf(x * c, 1.0f - sg, 1.0f);
+  }
+};
+
+// dq weights of one 32-key block: W^T[key][q] for this lane's query (row lq),
+// register r <-> key 8 (r / 4) + 4 hf + r % 4 of the block.
+template <bool kMasked>
+__device__ __forceinline__ void dq_weights(const f32x16& s, const f32x16& g, float k2, float c, float L2,
+                                           float Dq, int hf, int lq, u32x4 (&pw)[2]) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    float w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const SiluTerms t(s[r + e], k2, c);
+      const float F = __builtin_amdgcn_exp2f(t.silu2 - L2);
+      float v = F * (g[r + e] - Dq) * t.dsilu;
+      if (kMasked) v = (8 * ((r + e) >> 2) + 4 * hf + ((r + e) & 3)) < lq ? v : 0.0f;
+      w[e] = v;
+    }
+    pw[r >> 3][(r & 7) >> 1] = pack_bf16(w[0], w[1]);
+  }
+}
+
+// dkv weights of one 32-query block: F[q][key] and W[q][key] for this lane's
+// key (row lq), register r <-> query 8 (r / 4) + 4 hf + r % 4 of the block;
+// st points at the tile's statistics in LDS, qb0 = first query of the block
+// within the tile.
+template <bool kMasked>
+__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& g, float k2, float c, const float* st,
+                                           int qb0, int hf, int lq, u32x4 (&pf)[2], u32x4 (&pw)[2]) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int q = qb0 + 8 * g4 + 4 * hf;
+    const float4 L2 = *reinterpret_cast<const float4*>(st + q);
+    const float4 Dq = *reinterpret_cast<const float4*>(st + kStatRows + q);
+    const float l2v[4] = {L2.x, L2.y, L2.z, L2.w};
+    const float dv[4] = {Dq.x, Dq.y, Dq.z, Dq.w};
+    float f[4], w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g4 + e;
+      const SiluTerms t(s[r], k2, c);
+      float F = __builtin_amdgcn_exp2f(t.silu2 - l2v[e]);
+      if (kMasked) F = lq < 8 * g4 + 4 * hf + e ? F : 0.0f;
+      f[e] = F;
+      w[e] = F * (g[r] - dv[e]) * t.dsilu;
+    }
+    pf[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(f[0], f[1]);
+    pf[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(f[2], f[3]);
+    pw[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(w[0], w[1]);
+    pw[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(w[2], w[3]);
+  }
+}
+
+// Store 4 consecutive bf16 of a row (8 bytes).
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16(a, b), pack_bf16(c, d)};
+}
+__device__ __forceinline__ void load4(const __bf16* p, float (&x)[4]) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+}
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadParams hp) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
+
+  const int T = a.T;
+  const int nq = (T + kDqRows - 1) / kDqRows;
+  const int BH = a.B * a.H;
+  const int qt = nq - 1 - (int)blockIdx.x / BH;       // longest histories first
+  const int bh = (int)blockIdx.x % BH;
+  const int nt = (T + kStatRows - 1) / kStatRows;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+
+  const size_t head = (size_t)bh * (size_t)T * D;
+  const long long head_bytes = (long long)T * D * 2;
+  const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
+  const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + head;
+  const __bf16* dY = static_cast<const __bf16*>(a.dY) + head;
+  __bf16* dP1 = static_cast<__bf16*>(a.dP1) + head;
+
+  const int q0 = qt * kDqRows;
+  const int qrow = q0 + wave * 32 + lq;               // may be >= T: loads give 0, stores drop
+  const int own = q0 / 32 + wave;                     // the wave's 32-row block
+
+  // Rows of P1 and dY as evidence B operands: lane holds row qrow, columns
+  // 16 ds + 8 hf + 0..7.
+  bf16x8 qf[C::kDs], yf[C::kDs];
+  {
+    const auto rP1 = rsrc(P1, head_bytes);
+    const auto rdY = rsrc(dY, head_bytes);
+    const int qoff = qrow * (D * 2) + hf * 16;
+#pragma unroll
+    for (int ds = 0; ds < C::kDs; ++ds) {
+      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
+      yf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdY, qoff + ds * 32, 0, 0));
+    }
+  }
+  const bool valid = qrow < T;
+  const float L2 = valid ? a.stats[stat_at(bh, nt, qrow, 0)] : INFINITY;
+  const float Dq = valid ? a.stats[stat_at(bh, nt, qrow, 1)] : 0.0f;
+  const float c = hp.scale;
+  const float k2 = c * kLog2e;
+
+  // Keys 0 .. kend-1 are history for some row of this work-group.
+  const int kend = min(q0 + kDqRows, T) - 1;
+  const int ntiles = (kend + kTileRows - 1) / kTileRows;
+
+  // Staging: wave w moves blocks w + 8 u of each of the three layouts.
+  const int hb = (int)head_bytes;
+  int src_row[C::kPer], src_tr[C::kPer];
+#pragma unroll
+  for (int u = 0; u < C::kPer; ++u) {
+    src_row[u] = C::row_src(wave + kDqWaves * u, lane);
+    src_tr[u] = C::tr_src(wave + kDqWaves * u, lane);
+  }
+  auto dma = [&](int t) {
+    const int left = hb - t * kTileRows * D * 2;
+    const auto rk = rsrc_words(P2 + (size_t)t * kTileRows * D, left);
+    const auto rv = rsrc_words(V + (size_t)t * kTileRows * D, left);
+    char* slot = smem + (t % kDqSlots) * C::kSlotBytes;
+#pragma unroll
+    for (int u = 0; u < C::kPer; ++u) {
+      const int k = wave + kDqWaves * u;
+      dma16(rk, slot + k * C::kKBlock, src_row[u]);
+      dma16(rv, slot + C::kKBytes + k * C::kKBlock, src_row[u]);
+      dma16(rk, slot + 2 * C::kKBytes + k * C::kVBlock, src_tr[u]);
+    }
+  };
+  const int row_base = C::row_base(lane);
+  const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
+
+  f32x16 acc[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  if (ntiles > 0) dma(0);
+  if (ntiles > 1) dma(1);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) wait_vm_lgkm<C::kDmaTile, 15>();
+    else wait_vm_lgkm<0, 15>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Slot (t + 2) % 3 was last read in iteration t - 1, which every wave has
+    // finished once it passed the barrier above.
+    if (t + 2 < ntiles) dma(t + 2);
+    unsigned so = (unsigned)((t % kDqSlots) * C::kSlotBytes);
+    unsigned ok = so + row_base, ov = so + C::kKBytes + row_base;
+    unsigned oe = so + 2 * C::kKBytes + tr_even, oo = so + 2 * C::kKBytes + tr_odd;
+    asm volatile("" : "+v"(ok), "+v"(ov), "+v"(oe), "+v"(oo));
+    const VBase p2t{smem + oe, smem + oo};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int md = mode_keys_below(2 * t + kb, own);
+      if (md == 0) continue;
+      const f32x16 s = evidence_block<D>(smem + ok, kb, qf);
+      const f32x16 g = evidence_block<D>(smem + ov, kb, yf);
+      u32x4 pw[2];
+      if (md == 2) dq_weights<true>(s, g, k2, c, L2, Dq, hf, lq, pw);
+      else dq_weights<false>(s, g, k2, c, L2, Dq, hf, lq, pw);
+      transport_block<D>(p2t, kb, pw, acc);
+    }
+  }
+
+  if (!valid) return;
+  // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h); the statistic holds
+  // dU_ii / sqrt(d_h). Lane holds columns 32 db + 8 g4 + 4 hf + 0..3.
+  const float us = a.stats[stat_at(bh, nt, qrow, 3)];
+  const size_t ro = (size_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int col = 32 * db + 8 * g4 + 4 * hf;
+      float p[4];
+      load4(P2 + ro + col, p);
+      const int r = 4 * g4;
+      store4(dP1 + ro + col, fmaf(acc[db][r + 0], c, us * p[0]), fmaf(acc[db][r + 1], c, us * p[1]),
+             fmaf(acc[db][r + 2], c, us * p[2]), fmaf(acc[db][r + 3], c, us * p[3]));
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
+  using C = KvCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
+
+  const int T = a.T;
+  const int BH = a.B * a.H;
+  const int kt = (int)blockIdx.x / BH;                 // earliest keys (longest futures) first
+  const int bh = (int)blockIdx.x % BH;
+  const int nt = (T + kStatRows - 1) / kStatRows;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+
+  const size_t head = (size_t)bh * (size_t)T * D;
+  const long long head_bytes = (long long)T * D * 2;
+  const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
+  const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + head;
+  const __bf16* dY = static_cast<const __bf16*>(a.dY) + head;
+  __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
+  __bf16* dV = static_cast<__bf16*>(a.dV) + head;
+  const float* stats = a.stats + (size_t)bh * nt * kStatTile;
+
+  const int k0 = kt * kKvRows;
+  const int krow = k0 + wave * 32 + lq;                // may be >= T: loads give 0, stores drop
+  const int own = k0 / 32 + wave;
+
+  bf16x8 kf[C::kDs], vf[C::kDs];
+  {
+    const auto rP2 = rsrc(P2, head_bytes);
+    const auto rV = rsrc(V, head_bytes);
+    const int koff = krow * (D * 2) + hf * 16;
+#pragma unroll
+    for (int ds = 0; ds < C::kDs; ++ds) {
+      kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, koff + ds * 32, 0, 0));
+      vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
+    }
+  }
+  const float c = hp.scale;
+  const float k2 = c * kLog2e;
+
+  // Query tiles t0 .. nt-1 hold every query i > j of this work-group's keys.
+  const int t0 = k0 / kTileRows;
+  const int hb = (int)head_bytes;
+  int src_row[C::kPer], src_tr[C::kPer];
+#pragma unroll
+  for (int u = 0; u < C::kPer; ++u) {
+    src_row[u] = C::row_src(wave + kKvWaves * u, lane);
+    src_tr[u] = C::tr_src(wave + kKvWaves * u, lane);
+  }
+  auto dma = [&](int t) {
+    const int left = hb - t * kTileRows * D * 2;
+    const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * D, left);
+    const auto ry = rsrc_words(dY + (size_t)t * kTileRows * D, left);
+    char* slot = smem + ((t - t0) % kKvSlots) * C::kSlotBytes;
+#pragma unroll
+    for (int u = 0; u < C::kPer; ++u) {
+      const int k = wave + kKvWaves * u;
+      dma16(rq, slot + k * C::kKBlock, src_row[u]);
+      dma16(ry, slot + C::kKBytes + k * C::kKBlock, src_row[u]);
+      dma16(rq, slot + 2 * C::kKBytes + k * C::kVBlock, src_tr[u]);
+      dma16(ry, slot + 2 * C::kKBytes + C::kVBytes + k * C::kVBlock, src_tr[u]);
+    }
+    if (wave == 0) {
+      const auto rs = rsrc_words(stats + (size_t)t * kStatTile, kStatTile * 4);
+      dma16(rs, slot + C::kStatOff, 16 * lane);
+    }
+  };
+  const int row_base = C::row_base(lane);
+  const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
+
+  f32x16 accv[C::kDb], accp[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      accv[db][r] = 0.0f;
+      accp[db][r] = 0.0f;
+    }
+
+  if (t0 < nt) dma(t0);
+  if (t0 + 1 < nt) dma(t0 + 1);
+  for (int t = t0; t < nt; ++t) {
+    if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
+    else wait_vm_lgkm<0, 15>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
+    unsigned oq = so + row_base, oy = so + C::kKBytes + row_base;
+    unsigned qe = so + 2 * C::kKBytes + tr_even, qo = so + 2 * C::kKBytes + tr_odd;
+    unsigned ye = qe + C::kVBytes, yo = qo + C::kVBytes;
+    asm volatile("" : "+v"(oq), "+v"(oy), "+v"(qe), "+v"(qo), "+v"(ye), "+v"(yo));
+    const VBase p1t{smem + qe, smem + qo};
+    const VBase dyt{smem + ye, smem + yo};
+    const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int md = mode_queries_above(2 * t + qb, own);
+      if (md == 0) continue;
+      const f32x16 s = evidence_block<D>(smem + oq, qb, kf);
+      const f32x16 g = evidence_block<D>(smem + oy, qb, vf);
+      u32x4 pf[2], pw[2];
+      if (md == 2) kv_weights<true>(s, g, k2, c, st, 32 * qb, hf, lq, pf, pw);
+      else kv_weights<false>(s, g, k2, c, st, 32 * qb, hf, lq, pf, pw);
+      transport_block<D>(dyt, qb, pf, accv);
+      transport_block<D>(p1t, qb, pw, accp);
+    }
+    // Every wave is done with this slot before it is refilled.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < nt) dma(t + 2);
+  }
+
+  if (krow >= T) return;
+  const float fs = stats[stat_at(0, nt, krow, 2)];
+  const float us = stats[stat_at(0, nt, krow, 3)];
+  const size_t ro = (size_t)krow * D;
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int col = 32 * db + 8 * g4 + 4 * hf;
+      const int r = 4 * g4;
+      float y[4], p[4];
+      load4(dY + ro + col, y);
+      load4(P1 + ro + col, p);
+      store4(dV + ro + col, fmaf(fs, y[0], accv[db][r + 0]), fmaf(fs, y[1], accv[db][r + 1]),
+             fmaf(fs, y[2], accv[db][r + 2]), fmaf(fs, y[3], accv[db][r + 3]));
+      store4(dP2 + ro + col, fmaf(accp[db][r + 0], c, us * p[0]), fmaf(accp[db][r + 1], c, us * p[1]),
+             fmaf(accp[db][r + 2], c, us * p[2]), fmaf(accp[db][r + 3], c, us * p[3]));
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int nq = (a.T + kDqRows - 1) / kDqRows;
+  const int nk = (a.T + kKvRows - 1) / kKvRows;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(int d_h, int T) {
+  // Buffer descriptors address one head with 31-bit byte offsets, including
+  // the rows past T of the last tile.
+  return (d_h == 64 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
+}
+
+hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
+  switch (a.d_h) {
+    case 64: return launch_typed<64>(a, hp, s);
+    case 128: return launch_typed<128>(a, hp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rel

@@ -41,6 +41,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "mfma_tile.h"
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -48,24 +49,15 @@ namespace rel {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int kBM = 256;          // query rows per work-group
-constexpr int kBN = 64;           // keys per LDS tile
+constexpr int kBN = kTileRows;    // keys per LDS tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKSlots = 3;        // LDS ring depth of P2 (tile t in slot t % 3)
 constexpr int kVSlots = 4;        // LDS ring depth of V (tile t in slot t % 4)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;     // rescale only when the max grows by > 2^8
-constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9)
 
 // Block modes of a 64-key tile for one wave (blocks kb0 = keys 0..31, kb1 = 32..63).
 enum : int {
@@ -75,95 +67,21 @@ enum : int {
   kOff = 3     // the whole tile lies to the right (or past the history)
 };
 
-// LDS tiles are filled by direct global->LDS loads (buffer_load ... lds): one
-// wave instruction writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so a
-// tile is stored as blocks of 8 rows x 8 sixteen-byte chunks (8 x 128 bytes of
-// global memory per instruction). The order inside a block and the block
-// stride make every operand read a lane base plus an immediate and free of
-// bank conflicts:
-//   P2 block: position rr + 8 cc (chunk-major), block stride 1152 bytes, so
-//             the two 8-row blocks read by 16 lanes sit 128 bytes apart in the
-//             bank space;
-//   V block:  position 8 rr + (cc ^ 4 ((rr >> 1) & 1)) (row-major, chunk bit 2
-//             flipped on every other row pair), block stride 1024 bytes.
+// P2 tiles are kept in the row layout (evidence operands), V tiles in the
+// transposed layout (transport operands).
 template <int D>
-struct Cfg {
-  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
-  static constexpr int kBlocks = kChunks;            // 8x8-chunk blocks per 64-row tile
-  static constexpr int kKBlock = 1152;               // P2 block stride
-  static constexpr int kVBlock = 1024;               // V block stride
-  static constexpr int kKBytes = kBlocks * kKBlock;  // one P2 slot
-  static constexpr int kVBytes = kBlocks * kVBlock;  // one V slot
+struct Cfg : TileLayout<D> {
+  using L = TileLayout<D>;
   // + one block that absorbs direct loads of V tiles past the last one needed.
-  static constexpr int kLdsBytes = kKSlots * kKBytes + kVSlots * kVBytes + kVBlock;
-  static constexpr int kDmaPerWave = kBlocks / kWaves;      // blocks per wave per tile and operand
-  static constexpr int kDs = D / 16;                        // evidence MFMA k-steps
-  static constexpr int kDb = D / 32;                        // 32-row blocks of O^T
-  static constexpr int kPV = 2 * 2 * kDb;                   // transport MFMAs per tile
-  static constexpr int kQK = 2 * kDs;                       // evidence MFMAs per tile
+  static constexpr int kLdsBytes = kKSlots * L::kKBytes + kVSlots * L::kVBytes + L::kVBlock;
+  static constexpr int kDmaPerWave = L::kBlocks / kWaves;   // blocks per wave per tile and operand
+  static constexpr int kPV = 2 * 2 * L::kDb;                // transport MFMAs per tile
+  static constexpr int kQK = 2 * L::kDs;                    // evidence MFMAs per tile
   static constexpr int kSteps = (kPV + kQK) / 4;            // steady-state steps
   static_assert(kPV >= 4 && (kPV + kQK) % 4 == 0, "step layout");
   static_assert(kPV == 4 * (kSteps / 2) && kSteps >= 4, "evidence chains start at step kSteps / 2");
-  static_assert(kBlocks % kWaves == 0, "each wave moves whole blocks");
-  // Byte offset of evidence operand (block kb, k-step ds) from the lane base.
-  static constexpr int k_imm(int kb, int ds) { return 8 * kKBlock * (ds / 4) + 4 * kKBlock * kb + 256 * (ds % 4); }
-  // Byte offset of the 8-row group `half` of transport operand (kb, ks, db).
-  static constexpr int v_imm(int kb, int ks, int db, int half) {
-    return kVBlock * (8 * (db >> 1) + 4 * kb + 2 * ks + half);
-  }
+  static_assert(L::kBlocks % kWaves == 0, "each wave moves whole blocks");
 };
-
-// Lane read bases of one V slot: transport operands of even / odd 32-row O^T
-// blocks (db) differ in the flipped chunk bit.
-struct VBase {
-  const char* even;
-  const char* odd;
-};
-
-// s_waitcnt vmcnt(VM) lgkmcnt(LGKM), expcnt unconstrained (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int VM, int LGKM>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
-}
-
-// Raw buffer descriptor as four words (base, stride 0, num_records, flags) for
-// use in inline assembly.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
-  const unsigned long long a = (unsigned long long)base;
-  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, (unsigned)(bytes > 0 ? bytes : 0), (unsigned)kBufFlags};
-}
-
-// One direct global->LDS load: lane l's 16 bytes at voffset go to LDS byte
-// address lds + 16 l (M0 holds lds). Written as inline assembly so that the
-// compiler does not guard every later LDS read with a wait for all
-// outstanding loads; the kernel waits for them explicitly before the barrier
-// that publishes the tile.
-__device__ __forceinline__ void dma16(const u32x4& r, const char* lds, int voffset) {
-  const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
-}
-
-__device__ __forceinline__ float lane_pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float lane_pair_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bf16x4 lds_tr_read(const char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long long bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufFlags);
-}
 
 // Work item w = (b*H + h, pair pr): the query tiles nq-1-pr and pr of one
 // head, which together scan the same number of key tiles, so every item costs
@@ -198,64 +116,11 @@ __device__ __forceinline__ bool blk_diag(int mode, int kb) {
   return (mode == kDiag1 && kb == 1) || (mode == kDiag0 && kb == 0);
 }
 
-// Evidence of one 32-key block: s = P2[kb] . P1^T.
-template <int D>
-__device__ __forceinline__ f32x16 evidence_block(const char* kl, int kb, const bf16x8 (&qf)[D / 16]) {
-  using C = Cfg<D>;
-  f32x16 s;
-#pragma unroll
-  for (int ds = 0; ds < C::kDs; ++ds) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + C::k_imm(kb, ds));
-    if (ds == 0) {
-      const f32x16 zero = {};
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], zero, 0, 0, 0);
-    } else {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s, 0, 0, 0);
-    }
-  }
-  return s;
-}
-
-// Transposed V operand of transport MFMA i = (block kb, k-step ks, O^T block db);
-// the key order inside an MFMA k-step matches the register order of the
-// evidence tile.
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const VBase& vb, int i) {
-  using C = Cfg<D>;
-  const int kb = i / (2 * C::kDb), ks = (i / C::kDb) % 2, db = i % C::kDb;
-  const char* p = (db & 1) ? vb.odd : vb.even;
-  bf16x8 vf;
-  vf.lo = lds_tr_read(p + C::v_imm(kb, ks, db, 0));
-  vf.hi = lds_tr_read(p + C::v_imm(kb, ks, db, 1));
-  return vf;
-}
-
-// Transport of one 32-key block: O^T[d][q] += V^T[d][key] P^T[key][q].
-template <int D>
-__device__ __forceinline__ void transport_block(const VBase& vl, int kb, const u32x4 (&pf)[2],
-                                                f32x16 (&o)[D / 32]) {
-  using C = Cfg<D>;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-    for (int db = 0; db < C::kDb; ++db) {
-      const bf16x8 vf = v_operand<D>(vl, kb * 2 * C::kDb + ks * C::kDb + db);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pf[ks]), o[db], 0, 0, 0);
-    }
-  }
-}
-
 // Exchange weight of one score (log2 domain): 2^(a / (1 + 2^-a) - m2), a = s k2.
 __device__ __forceinline__ float exch_weight(float s, float k2, float m2) {
   const float av = s * k2;
   const float den = 1.0f + __builtin_amdgcn_exp2f(-av);
   return __builtin_amdgcn_exp2f(av * __builtin_amdgcn_rcpf(den) - m2);
-}
-
-// Two weights as one packed bf16 pair (round to nearest even).
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(unsigned, v);
 }
 
 // Exchange weights of one 32-key block into packed bf16 transport operands
@@ -367,9 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // the ring) hold the V rows of this tile's own queries for the Self term.
   const int nvt = kend / kBN + 1;
 
-  // Staging: wave w moves blocks k = w + 8 u of a tile; lane l of a P2 block
-  // fetches row 8 (k % 8) + l % 8, chunk 8 (k / 8) + l / 8; lane l of a V block
-  // fetches row 8 (k % 8) + l / 8, chunk 8 (k / 8) + ((l % 8) ^ 4 ((l / 16) & 1)).
+  // Staging: wave w moves blocks k = w + 8 u of a P2 tile (row layout) and
+  // of a V tile (transposed layout).
   // Tiles past the last one a work-group needs get an empty descriptor: the
   // loads still issue (and write zeros) but move no data from memory.
   const int hb = (int)head_bytes;
@@ -377,9 +241,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 #pragma unroll
   for (int u = 0; u < C::kDmaPerWave; ++u) {
     const int k = wave + kWaves * u;
-    dma_koff[u] = (8 * (k % 8) + (lane & 7)) * (D * 2) + 16 * (8 * (k / 8) + (lane >> 3));
-    const int rr = lane >> 3;
-    dma_voff[u] = (8 * (k % 8) + rr) * (D * 2) + 16 * (8 * (k / 8) + ((lane & 7) ^ (4 * ((rr >> 1) & 1))));
+    dma_koff[u] = C::row_src(k, lane);
+    dma_voff[u] = C::tr_src(k, lane);
   }
   auto dma_k = [&](int t) {
     const auto rs = rsrc_words(P2 + (size_t)t * kBN * D, t < ntiles ? hb - t * kBN * D * 2 : 0);
@@ -398,14 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   };
   constexpr int kDmaIter = 2 * C::kDmaPerWave;   // direct loads a wave issues per iteration
 
-  // Lane read bases: evidence operand rows (lq, chunk hf) and the transposed V
-  // read (16-lane group g supplies rows 4 (g / 2) + i / 4 and columns
-  // 16 (g % 2) + 4 (i % 4) of each 16-key half, i = lane % 16).
-  const int koff = C::kKBlock * (lq >> 3) + 16 * (lq & 7) + 128 * hf;
-  const int tg = lane >> 4, ti = lane & 15;
-  const int vrr = 4 * (tg >> 1) + (ti >> 2), vcc = 2 * (tg & 1) + ((ti & 3) >> 1), vsw = (vrr >> 1) & 1;
-  const int voff_even = 16 * (8 * vrr + 4 * vsw + vcc) + 8 * (ti & 1);
-  const int voff_odd = 16 * (8 * vrr + 4 * (vsw ^ 1) + vcc) + 8 * (ti & 1);
+  // Lane read bases: evidence operand rows of P2 and the transposed V reads.
+  const int koff = C::row_base(lane);
+  const int voff_even = C::tr_base(lane, false);
+  const int voff_odd = C::tr_base(lane, true);
   // Per-lane read bases of the slot holding tile t. The base is formed once
   // per use site in a register (opaque to the optimiser), so every operand
   // read is that register plus an immediate; otherwise the compiler hoists a
@@ -671,6 +530,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   dself = lane_pair_sum(dself);
   const float S = sigmoid_f32(dself * hp.scale * inv_tau);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
+  if (a.lse != nullptr && hf == 0 && qrow < T) a.lse[(size_t)bh * T + qrow] = c.lse;
   const int roff = qrow * (D * 2) + hf * 8;
   // V_i of this lane's row from the V ring (tile qrow / 64 is among the last
   // four loaded): columns 32 db + 8 g4 + 4 hf .. +3, i.e. half hf of chunk

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kRows) void fwd_scan_kernel(FwdArgs a, HeadParams h
   for (int k = 0; k < D; ++k) dself = fmaf(q[k], to_f32(P2[(size_t)r * D + k]), dself);
   const float S = sigmoid_f32(dself * hp.scale * hp.inv_tau[h]);
   const RowCombine c(S, m, l, hp.lambda * logf((float)(r + 1)));
+  if (a.lse) a.lse[((size_t)b * a.H + h) * (size_t)a.T + r] = c.lse;
 #pragma unroll
   for (int k = 0; k < D; ++k) {
     const float vi = to_f32(V[(size_t)r * D + k]);

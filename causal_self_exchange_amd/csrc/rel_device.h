@@ -33,6 +33,7 @@ __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)
 // On the first row c = 0, the Self weight is a / a = 1 exactly and Y = V_i.
 struct RowCombine {
   float w_self, w_hist;
+  float lse;   // log of the row's full normaliser e^S + e^{m - count} l
   __device__ __forceinline__ RowCombine(float S, float m, float l, float count) {
     const float mp = m - count;
     const float M = fmaxf(mp, S);
@@ -41,6 +42,7 @@ struct RowCombine {
     const float den = a + c * l;
     w_self = a / den;
     w_hist = c / den;
+    lse = M + logf(den);
   }
 };
 

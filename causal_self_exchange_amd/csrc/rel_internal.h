@@ -21,6 +21,7 @@ struct FwdArgs {
   const void* V;
   void* Y;
   int B, H, T, d_h;
+  float* lse;           // optional [B][H][T] row log normalisers (null: not written)
 };
 
 struct DecodeArgs {
@@ -35,6 +36,39 @@ struct DecodeArgs {
   int B, H, L_cap, d_h, n_chunks;
 };
 
+// Backward of the forward above. Row statistics are stored per 64-row tile
+// of each (b, h) as four arrays of 64 floats, so that one 1 KB direct load
+// brings a tile's values into LDS:
+//   [0]  (LSE_i + lambda log i) log2 e   (+inf on padding rows past T)
+//   [1]  D_i = dY_i . Y_i
+//   [2]  F_ii  (the Self weight of row i)
+//   [3]  dU_ii / sqrt(d_h)  (Self gradient of the evidence, scaled)
+// Partials of dtau / dlambda are written per (b, h, 256-row chunk) and summed
+// in a fixed order by the reduce kernel, so every output is deterministic.
+constexpr int kStatRows = 64;
+constexpr int kStatTile = 4 * kStatRows;   // floats per 64-row tile of statistics
+constexpr int kPrepRows = 256;             // rows per prep work-group (one partial)
+
+struct BwdArgs {
+  const void* P1;
+  const void* P2;
+  const void* V;
+  const void* Y;
+  const void* dY;
+  const float* lse;     // [B][H][T] natural-log row normalisers from the forward
+  void* dP1;
+  void* dP2;
+  void* dV;
+  float* dtau;          // [H]
+  float* dlambda;       // [1]
+  float* stats;         // [B*H][ceil(T/64)][4][64]
+  float* part;          // [B*H][ceil(T/256)][2]
+  int B, H, T, d_h;
+};
+
+inline int64_t bwd_stat_floats(int64_t BH, int64_t T) { return BH * ((T + kStatRows - 1) / kStatRows) * kStatTile; }
+inline int64_t bwd_part_floats(int64_t BH, int64_t T) { return BH * ((T + kPrepRows - 1) / kPrepRows) * 2; }
+
 // Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
 // states per (b, h), one per partial work-group.
 constexpr int kDecodeChunk = 256;
@@ -43,6 +77,13 @@ constexpr int kDecodeChunk = 256;
 hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s);
 bool fwd_mfma_supported(int d_h, int T);
+// Backward: prep (row statistics, dtau / dlambda partials) then the query and
+// key/value gradient kernels, then the fixed-order reduce.
+hipError_t launch_bwd_prep(const BwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
+hipError_t launch_bwd_scan(const BwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
+hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s);
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
+bool bwd_mfma_supported(int d_h, int T);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
                                int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s);

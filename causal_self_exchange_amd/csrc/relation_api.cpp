@@ -15,6 +15,7 @@ namespace {
 using rel::HeadParams;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -63,6 +64,44 @@ bool use_mfma(rel_dtype dt, int d_h, int T) {
   return !(env && std::strcmp(env, "scan") == 0);
 }
 
+// Forward with an optional row log-normaliser output (lse may be null).
+rel_status fwd_impl(const void* P1, const void* P2, const void* V, const float* tau_s, float lambda,
+                    void* Y, float* lse, int B, int H, int T, int d_h, rel_dtype dt, hipStream_t stream) {
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  HeadParams hp;
+  const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
+  if (st != REL_OK) return st;
+  if (!aligned16(P1) || !aligned16(P2) || !aligned16(V) || !aligned16(Y)) return REL_E_ALIGN;
+  const size_t bytes = static_cast<size_t>(n) * elem_size(dt);
+  if (overlaps(Y, bytes, P1, bytes) || overlaps(Y, bytes, P2, bytes) || overlaps(Y, bytes, V, bytes))
+    return REL_E_ALIAS;
+  if (lse) {
+    if (!aligned4(lse)) return REL_E_ALIGN;
+    const size_t lb = static_cast<size_t>(B) * H * T * sizeof(float);
+    if (overlaps(lse, lb, P1, bytes) || overlaps(lse, lb, P2, bytes) || overlaps(lse, lb, V, bytes) ||
+        overlaps(lse, lb, Y, bytes))
+      return REL_E_ALIAS;
+  }
+
+  rel::FwdArgs a{P1, P2, V, Y, B, H, T, d_h, lse};
+  const hipError_t e = use_mfma(dt, d_h, T) ? rel::launch_fwd_mfma_bf16(a, hp, stream)
+                                         : rel::launch_fwd_scan(a, hp, dt == REL_BF16, stream);
+  return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+// Which backward runs: the MFMA kernels for bf16 where they exist, else the
+// row-scan kernels. RELATION_BWD_KERNEL=scan forces the row-scan kernels.
+bool use_bwd_mfma(rel_dtype dt, int d_h, int T) {
+  if (dt != REL_BF16 || !rel::bwd_mfma_supported(d_h, T)) return false;
+  const char* env = std::getenv("RELATION_BWD_KERNEL");
+  return !(env && std::strcmp(env, "scan") == 0);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 }  // namespace
 
 extern "C" {
@@ -76,8 +115,8 @@ const char* relation_status_str(rel_status s) {
     case REL_E_HEADDIM: return "unsupported head dimension";
     case REL_E_TAU: return "tau must be finite and > 0";
     case REL_E_LAMBDA: return "lambda must be finite";
-    case REL_E_ALIGN: return "pointer not 16-byte aligned";
-    case REL_E_ALIAS: return "output overlaps an input";
+    case REL_E_ALIGN: return "pointer misaligned (16 bytes; 4 for float arrays)";
+    case REL_E_ALIAS: return "output overlaps an input or another output";
     case REL_E_WORKSPACE: return "workspace missing or too small";
     case REL_E_LAUNCH: return "kernel launch failed";
   }
@@ -88,6 +127,31 @@ rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V, const 
                            float lambda, void* Y, int B, int H, int T, int d_h, rel_dtype dt,
                            hipStream_t stream) {
   if (!P1 || !P2 || !V || !tau_s || !Y) return REL_E_NULL;
+  return fwd_impl(P1, P2, V, tau_s, lambda, Y, nullptr, B, H, T, d_h, dt, stream);
+}
+
+rel_status relation_fwd_lse(const void* P1, const void* P2, const void* V, const float* tau_s,
+                            float lambda, void* Y, float* LSE, int B, int H, int T, int d_h,
+                            rel_dtype dt, hipStream_t stream) {
+  if (!P1 || !P2 || !V || !tau_s || !Y || !LSE) return REL_E_NULL;
+  return fwd_impl(P1, P2, V, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
+}
+
+size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h) {
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h)) return 0;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  return align256(static_cast<size_t>(rel::bwd_stat_floats(BH, T)) * sizeof(float)) +
+         align256(static_cast<size_t>(rel::bwd_part_floats(BH, T)) * sizeof(float));
+}
+
+rel_status relation_bwd(const void* P1, const void* P2, const void* V, const float* tau_s,
+                        float lambda, const void* Y, const float* LSE, const void* dY, void* dP1,
+                        void* dP2, void* dV, float* dtau, float* dlambda, int B, int H, int T,
+                        int d_h, rel_dtype dt, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!P1 || !P2 || !V || !tau_s || !Y || !LSE || !dY || !dP1 || !dP2 || !dV || !dtau || !dlambda)
+    return REL_E_NULL;
   int64_t n = 0;
   if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
@@ -95,14 +159,35 @@ rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V, const 
   HeadParams hp;
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
-  if (!aligned16(P1) || !aligned16(P2) || !aligned16(V) || !aligned16(Y)) return REL_E_ALIGN;
-  const size_t bytes = static_cast<size_t>(n) * elem_size(dt);
-  if (overlaps(Y, bytes, P1, bytes) || overlaps(Y, bytes, P2, bytes) || overlaps(Y, bytes, V, bytes))
-    return REL_E_ALIAS;
+  const size_t need = relation_bwd_workspace_bytes(B, H, T, d_h);
+  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  if (!aligned16(P1) || !aligned16(P2) || !aligned16(V) || !aligned16(Y) || !aligned16(dY) ||
+      !aligned16(dP1) || !aligned16(dP2) || !aligned16(dV) || !aligned16(workspace) || !aligned4(LSE) ||
+      !aligned4(dtau) || !aligned4(dlambda))
+    return REL_E_ALIGN;
+  const size_t tb = static_cast<size_t>(n) * elem_size(dt);
+  const size_t lb = static_cast<size_t>(B) * H * T * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{P1, tb}, {P2, tb}, {V, tb}, {Y, tb}, {LSE, lb}, {dY, tb}};
+  const Range outs[] = {{dP1, tb}, {dP2, tb}, {dV, tb}, {dtau, H * sizeof(float)},
+                        {dlambda, sizeof(float)}, {workspace, need}};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return REL_E_ALIAS;
+  for (size_t x = 0; x < sizeof(outs) / sizeof(outs[0]); ++x)
+    for (size_t y = x + 1; y < sizeof(outs) / sizeof(outs[0]); ++y)
+      if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return REL_E_ALIAS;
 
-  rel::FwdArgs a{P1, P2, V, Y, B, H, T, d_h};
-  const hipError_t e = use_mfma(dt, d_h, T) ? rel::launch_fwd_mfma_bf16(a, hp, stream)
-                                         : rel::launch_fwd_scan(a, hp, dt == REL_BF16, stream);
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  char* ws = static_cast<char*>(workspace);
+  float* stats = reinterpret_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::bwd_stat_floats(BH, T)) * sizeof(float)));
+  rel::BwdArgs a{P1, P2, V, Y, dY, LSE, dP1, dP2, dV, dtau, dlambda, stats, part, B, H, T, d_h};
+  const bool bf16 = dt == REL_BF16;
+  hipError_t e = rel::launch_bwd_prep(a, hp, bf16, stream);
+  if (e == hipSuccess)
+    e = use_bwd_mfma(dt, d_h, T) ? rel::launch_bwd_mfma_bf16(a, hp, stream) : rel::launch_bwd_scan(a, hp, bf16, stream);
+  if (e == hipSuccess) e = rel::launch_bwd_reduce(a, stream);
   return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
 

@@ -1,6 +1,6 @@
 """Thin Python binding over librelation.so (ctypes).
 
-Argument marshalling only: every step of the forward and decode runs in the
+Argument marshalling only: every step of the forward, backward and decode runs in the
 HIP kernels behind the C ABI (include/relation.h). PyTorch supplies device
 memory and the current stream. There is no CPU fallback: if the library is
 missing or a call fails, an exception is raised.
@@ -41,6 +41,12 @@ def lib() -> ctypes.CDLL:
         L.relation_fwd.restype = i
         L.relation_fwd_ex.argtypes = [vp, vp, vp, fp, f, vp, i, i, i, i, i, vp]
         L.relation_fwd_ex.restype = i
+        L.relation_fwd_lse.argtypes = [vp, vp, vp, fp, f, vp, vp, i, i, i, i, i, vp]
+        L.relation_fwd_lse.restype = i
+        L.relation_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.relation_bwd_workspace_bytes.restype = sz
+        L.relation_bwd.argtypes = [vp, vp, vp, fp, f, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.relation_bwd.restype = i
         L.relation_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.relation_decode_workspace_bytes.restype = sz
         L.relation_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp, sz, vp]
@@ -53,8 +59,9 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_decode_workspace_bytes",
-           "relation_decode", "relation_cache_append", "relation_status_str")
+EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_workspace_bytes",
+           "relation_bwd", "relation_decode_workspace_bytes", "relation_decode",
+           "relation_cache_append", "relation_status_str")
 
 
 def _ptr(t) -> int | None:
@@ -103,6 +110,57 @@ def fwd(P1, P2, V, tau, lam: float = 0.0, out=None, stream=None):
     del tau_keep
     _check("relation_fwd_ex", st)
     return out
+
+
+def fwd_lse(P1, P2, V, tau, lam: float = 0.0, out=None, lse=None, stream=None):
+    """Training forward: (Y, LSE) with LSE the fp32 [B, H, T] row log normaliser."""
+    _require_cuda(P1, P2, V)
+    B, H, T, D = P1.shape
+    if P2.shape != P1.shape or V.shape != P1.shape or P2.dtype != P1.dtype or V.dtype != P1.dtype:
+        raise ValueError("P1, P2, V must share shape and dtype")
+    if out is None:
+        out = torch.empty_like(V)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=P1.device)
+    _require_cuda(out, lse)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_fwd_lse(_ptr(P1), _ptr(P2), _ptr(V), tau_p, float(lam), _ptr(out), _ptr(lse),
+                                B, H, T, D, _dtype_code(P1), _stream(stream))
+    del tau_keep
+    _check("relation_fwd_lse", st)
+    return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, T: int, d_h: int) -> int:
+    return int(lib().relation_bwd_workspace_bytes(B, H, T, d_h))
+
+
+def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None):
+    """Gradients (dP1, dP2, dV, dtau [H] fp32, dlambda [1] fp32) of sum(Y * dY),
+    from the forward's inputs and its outputs Y, LSE (fwd_lse)."""
+    _require_cuda(P1, P2, V, Y, lse, dY)
+    B, H, T, D = P1.shape
+    for t in (P2, V, Y, dY):
+        if t.shape != P1.shape or t.dtype != P1.dtype:
+            raise ValueError("P1, P2, V, Y, dY must share shape and dtype")
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, T]")
+    if grads is None:
+        grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
+                 torch.empty(H, dtype=torch.float32, device=P1.device),
+                 torch.empty(1, dtype=torch.float32, device=P1.device))
+    dP1, dP2, dV, dtau, dlam = grads
+    _require_cuda(dP1, dP2, dV, dtau, dlam)
+    need = bwd_workspace_bytes(B, H, T, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_bwd(_ptr(P1), _ptr(P2), _ptr(V), tau_p, float(lam), _ptr(Y), _ptr(lse), _ptr(dY),
+                            _ptr(dP1), _ptr(dP2), _ptr(dV), _ptr(dtau), _ptr(dlam), B, H, T, D,
+                            _dtype_code(P1), _ptr(workspace), workspace.numel(), _stream(stream))
+    del tau_keep
+    _check("relation_bwd", st)
+    return dP1, dP2, dV, dtau, dlam
 
 
 def decode_workspace_bytes(B: int, H: int, L_cap: int, d_h: int) -> int:

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the causal Self-Exchange Relation forward and decode.
+"""Seeded synthetic workloads for the causal Self-Exchange Relation forward, backward and decode.
 
 This module only draws and stores numbers. It holds none of the operator's
 arithmetic, so both the HIP path and the CPU oracle can consume what it makes
@@ -15,6 +15,8 @@ Recipe (all draws float32 from numpy's PCG64 ``default_rng(seed)``):
   forward: P1, P2, V ~ scale * N(0, 1) drawn in that order, then tau
            (a per-head uniform draw when ``tau`` is "uniform"), then rounded
            to the storage dtype with round-to-nearest-even.
+  backward: the forward's draws, then dY ~ N(0, 1) [B, H, T, d_h] from
+           ``default_rng(seed + 1000003)``, rounded to the storage dtype.
   decode : cache lengths L_b ~ U{lo..hi}, then for each sequence b in order
            its cached P2 rows [H, L_b, d_h] and cached V rows; then the new
            token's p1, p2, v [B, H, d_h]. Cache rows past L_b hold NaN.
@@ -97,6 +99,17 @@ def make_fwd_inputs(cfg: FwdConfig, seed: int):
         tau = np.full(cfg.H, cfg.tau, dtype=np.float32)
     return dict(P1=_store(P1, cfg.dtype), P2=_store(P2, cfg.dtype),
                 V=_store(V, cfg.dtype), tau=tau, lam=float(cfg.lam))
+
+
+def make_bwd_inputs(cfg: FwdConfig, seed: int):
+    """make_fwd_inputs plus an upstream gradient dY ~ N(0, 1) [B,H,T,d_h] in
+    the storage dtype, drawn from its own stream (seed + 1000003) so that the
+    forward inputs are the same as make_fwd_inputs(cfg, seed)."""
+    inp = make_fwd_inputs(cfg, seed)
+    rng = np.random.default_rng(seed + 1000003)
+    dY = rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.d_h), dtype=np.float32)
+    inp["dY"] = _store(dY, cfg.dtype)
+    return inp
 
 
 def make_decode_inputs(cfg: DecodeConfig, seed: int):

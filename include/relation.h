@@ -1,7 +1,7 @@
 /*
  * relation.h - C ABI of librelation.so: the causal Self-Exchange Relation
- * forward (FlashRelation form) and its Relation Cache decode step on AMD
- * Instinct MI355X (gfx950).
+ * forward (FlashRelation form), its backward, and its Relation Cache decode
+ * step on AMD Instinct MI355X (gfx950).
  *
  * Operator ("Ask Self, Ask Others: Relation Is All You Need", Eq. (1)-(3)),
  * per batch entry b and head h, for query row i (one-based) of T:
@@ -30,8 +30,9 @@
  *     nothing is launched and no memory is touched.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
  *     caller synchronises. REL_E_LAUNCH reports a launch failure.
- *   - Pointers must be 16-byte aligned; an output range may not overlap any
- *     input range.
+ *   - Tensor pointers must be 16-byte aligned, float arrays (LSE, dtau,
+ *     dlambda) 4-byte aligned; an output range may not overlap any input
+ *     range or another output range.
  *   - Supported: d_h in {32, 64, 128}; 1 <= H <= REL_MAX_HEADS; B <= 65535.
  */
 #ifndef RELATION_H
@@ -55,8 +56,8 @@ typedef enum {
   REL_E_HEADDIM = 4,   /* d_h not supported                                  */
   REL_E_TAU = 5,       /* a tau is NaN, infinite or <= 0                     */
   REL_E_LAMBDA = 6,    /* lambda is NaN or infinite                          */
-  REL_E_ALIGN = 7,     /* a pointer is not 16-byte aligned                   */
-  REL_E_ALIAS = 8,     /* an output range overlaps an input range           */
+  REL_E_ALIGN = 7,     /* a pointer is misaligned (see conventions)          */
+  REL_E_ALIAS = 8,     /* an output range overlaps an input or output range  */
   REL_E_WORKSPACE = 9, /* workspace missing or smaller than required         */
   REL_E_LAUNCH = 10    /* a kernel launch failed                             */
 } rel_status;
@@ -89,6 +90,61 @@ rel_status relation_fwd_ex(const void* P1, const void* P2, const void* V,
                            const float* tau_s, float lambda, void* Y, int B,
                            int H, int T, int d_h, rel_dtype dt,
                            hipStream_t stream);
+
+/*
+ * relation_fwd_lse - the training forward: relation_fwd_ex plus the per-row
+ * log normaliser the backward needs,
+ *   LSE[b, h, i] = log( e^{S_i} + sum_{j<i} e^{SiLU(U_ij) - lambda log i} )
+ *               = log sum_{j<=i} e^{R_ij}       (natural log, fp32)
+ * i.e. log of the partition e^{S_i} + e^{A_i} of Eq. (6)-(7); row 1 gives S_1.
+ *
+ *   LSE : out, device float[B, H, T]
+ * Y is identical to relation_fwd_ex's for the same arguments.
+ */
+rel_status relation_fwd_lse(const void* P1, const void* P2, const void* V,
+                            const float* tau_s, float lambda, void* Y,
+                            float* LSE, int B, int H, int T, int d_h,
+                            rel_dtype dt, hipStream_t stream);
+
+/*
+ * relation_bwd_workspace_bytes - bytes of device workspace relation_bwd needs
+ * for these sizes (per-row statistics and per-chunk scalar partials). 0 on
+ * invalid sizes.
+ */
+size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h);
+
+/*
+ * relation_bwd - gradients of the forward (Eq. (1)-(3) with the count term of
+ * Eq. (2)) for an upstream gradient dY = dL/dY:
+ *   dP1, dP2, dV : dL/dP1, dL/dP2, dL/dV, device [B, H, T, d_h], dtype dt
+ *   dtau         : dL/dtau_h summed over the batch, device float[H]
+ *   dlambda      : dL/dlambda summed over batch and heads, device float[1]
+ * The evidence is recomputed per tile from the saved row log normaliser (the
+ * FlashRelation backward, App. A.3); with F = softmax(R) per row:
+ *   dR_ij = F_ij (dY_i . V_j - dY_i . Y_i),
+ *   dU_ij = dR_ij SiLU'(U_ij) (j < i),  dU_ii = dR_ii S_i (1 - S_i) / tau_h,
+ *   dP1 = dU P2 / sqrt(d_h), dP2 = dU^T P1 / sqrt(d_h), dV = F^T dY,
+ *   dtau_h = -sum_i dR_ii S_i (1 - S_i) U_ii / tau_h^2,
+ *   dlambda = -sum_i log i sum_{j<i} dR_ij.
+ *
+ *   P1, P2, V, tau_s, lambda : the forward's inputs
+ *   Y, LSE       : in, the forward's outputs from relation_fwd_lse with the
+ *                  same inputs
+ *   dY           : in, device [B, H, T, d_h], dtype dt
+ *   workspace    : device scratch of >= relation_bwd_workspace_bytes bytes
+ * Every output is overwritten (not accumulated into). The result is
+ * deterministic: no atomics, scalar sums in a fixed order (fp64 across rows
+ * chunks, heads and batch).
+ * Numerics: REL_BF16 with d_h in {64, 128} recomputes both evidence products
+ * on bf16 MFMA and rounds F and dU to bf16 as operands of the gradient
+ * products (fp32 accumulation); other cases compute in fp32 throughout.
+ */
+rel_status relation_bwd(const void* P1, const void* P2, const void* V,
+                        const float* tau_s, float lambda, const void* Y,
+                        const float* LSE, const void* dY, void* dP1, void* dP2,
+                        void* dV, float* dtau, float* dlambda, int B, int H,
+                        int T, int d_h, rel_dtype dt, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
 
 /*
  * relation_decode_workspace_bytes - bytes of device workspace relation_decode

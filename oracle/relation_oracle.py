@@ -176,10 +176,13 @@ def row_lse(p1, p2, tau, lam=0.0):
     return mx + np.log(np.sum(np.exp(R - mx[:, None]), axis=1))
 
 
-def relation_head_bwd(p1, p2, v, tau, lam, dy):
+def relation_head_bwd(p1, p2, v, tau, lam, dy, return_terms=False):
     """Gradients of sum(Y * dy) for one head: (dP1, dP2, dV, dtau, dlambda).
 
     Chain rule through [paper] Eq. (1)-(3) on the materialised U, R, F.
+    With return_terms, also a dict of per-row quantities behind the two
+    scalars: tau_terms (row i's share of dtau), lam_terms (row i's share of
+    dlambda), F_self (F_ii), U_self (U_ii), S (S_i), dR_self (dR_ii).
     """
     T, d_h = p1.shape
     tau = float(tau)
@@ -201,6 +204,12 @@ def relation_head_bwd(p1, p2, v, tau, lam, dy):
     dtau = float(np.sum(dR[diag, diag] * s * (1.0 - s) * (-U[diag, diag] / tau ** 2)))
     log_i = np.log(np.arange(1, T + 1, dtype=np.float64))
     dlam = float(-np.sum(np.where(below, dR, 0.0) * log_i[:, None]))
+    if return_terms:
+        terms = dict(tau_terms=dR[diag, diag] * s * (1.0 - s) * (-U[diag, diag] / tau ** 2),
+                     lam_terms=-log_i * np.sum(np.where(below, dR, 0.0), axis=1),
+                     F_self=F[diag, diag].copy(), U_self=U[diag, diag].copy(), S=s,
+                     dR_self=dR[diag, diag].copy())
+        return dP1, dP2, dV, dtau, dlam, terms
     return dP1, dP2, dV, dtau, dlam
 
 

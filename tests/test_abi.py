@@ -120,3 +120,62 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 1, 4, 32)
     with pytest.raises(ValueError):
         R.fwd(x, x, x, 1.0)
+
+
+# Fake addresses for the training forward / backward (far apart, aligned).
+LSE_, DY_, G1, G2, G3, DT, DL, WS = (0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000,
+                                     0xA0000000, 0xA0001000, 0xB0000000)
+
+
+def fwd_lse(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, B=1, H=2, T=16, D=64, dt=R.REL_BF16):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    return R.lib().relation_fwd_lse(P1, P2, V, tp, lam, Yp, L, B, H, T, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=None), E_NULL), (dict(P1=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=48), E_HEADDIM),
+    (dict(tau=(1.0, 0.0)), E_TAU), (dict(L=LSE_ + 2), E_ALIGN), (dict(L=A + 64), E_ALIAS),
+    (dict(L=Y + 4), E_ALIAS), (dict(L=Y - 4), E_ALIAS),
+])
+def test_fwd_lse_rejects_invalid_arguments(kw, code):
+    assert fwd_lse(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    lib = R.lib()
+    # statistics: B*H*ceil(T/64)*256 floats; partials: B*H*ceil(T/256)*2 floats; each 256-aligned
+    def want(B, H, T):
+        a = B * H * ((T + 63) // 64) * 256 * 4
+        b = B * H * ((T + 255) // 256) * 2 * 4
+        return ((a + 255) // 256) * 256 + ((b + 255) // 256) * 256
+    assert lib.relation_bwd_workspace_bytes(1, 32, 8192, 128) == want(1, 32, 8192)
+    assert lib.relation_bwd_workspace_bytes(2, 3, 1, 32) == want(2, 3, 1)
+    assert lib.relation_bwd_workspace_bytes(4, 16, 2049, 64) == want(4, 16, 2049)
+    assert lib.relation_bwd_workspace_bytes(0, 3, 10, 64) == 0
+    assert lib.relation_bwd_workspace_bytes(1, 1, 10, 48) == 0
+
+
+def bwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, dY=DY_, dP1=G1, dP2=G2, dV=G3,
+        dtau=DT, dlam=DL, B=1, H=2, T=16, D=64, dt=R.REL_BF16, ws=WS, ws_bytes=None):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    if ws_bytes is None:
+        ws_bytes = R.lib().relation_bwd_workspace_bytes(B, H, T, D) if T > 0 and B > 0 else 0
+    return R.lib().relation_bwd(P1, P2, V, tp, lam, Yp, L, dY, dP1, dP2, dV, dtau, dlam, B, H, T, D, dt,
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dY=None), E_NULL), (dict(L=None), E_NULL), (dict(dtau=None), E_NULL), (dict(dlam=None), E_NULL),
+    (dict(dP2=None), E_NULL), (dict(tau=None), E_NULL),
+    (dict(T=0), E_SHAPE), (dict(B=70000), E_SHAPE), (dict(H=257, tau=[1.0] * 257), E_SHAPE),
+    (dict(dt=3), E_DTYPE), (dict(D=80), E_HEADDIM), (dict(tau=(1.0, float("nan"))), E_TAU),
+    (dict(lam=float("inf")), E_LAMBDA),
+    (dict(ws=None), E_WS), (dict(ws_bytes=1000), E_WS),
+    (dict(dP1=G1 + 8), E_ALIGN), (dict(ws=WS + 8), E_ALIGN), (dict(dtau=DT + 2), E_ALIGN),
+    (dict(L=LSE_ + 1), E_ALIGN),
+    (dict(dP1=A), E_ALIAS), (dict(dV=DY_ + 16), E_ALIAS), (dict(dtau=LSE_ + 4), E_ALIAS),
+    (dict(dP2=G1 + 16), E_ALIAS), (dict(dlam=DT + 4), E_ALIAS), (dict(ws=G3), E_ALIAS),
+    (dict(dV=Y - 16), E_ALIAS),
+])
+def test_bwd_rejects_invalid_arguments(kw, code):
+    assert bwd(**kw) == code

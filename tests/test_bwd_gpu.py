@@ -1,0 +1,209 @@
+"""GPU parity of the training forward (Y, LSE) and the backward (dP1, dP2, dV,
+dtau, dlambda) through the C ABI against the fp64 CPU oracle on the same
+seeded inputs (the oracle's gradients are pinned separately, on the CPU).
+
+Tolerances (the pages fix none for gradients; these follow the forward's bar):
+  tensors, per row i of each gradient g:
+      ||g_i - g*_i||_inf <= tol * max(1, ||g*_i||_inf)
+    tol = 2e-2 for bf16 (the forward's absolute bar, relative once a row's
+    gradient exceeds 1 -- the bf16 output rounding alone is 2^-9 relative),
+    tol = 1e-5 for fp32.
+  scalars: each row's share of dtau / dlambda is formed from F_ii, dY_i . V_i
+    and D_i = dY_i . Y_i, so the bar is tol times the sum over rows of
+      |d R_ii / d theta| * F_ii * sum_d |dY_id| (|V_id| + |Y_id|)
+    (theta = tau: S_i (1 - S_i) |U_ii| / tau^2; theta = lambda: log i), the
+    size of the quantities each share is computed from.
+  LSE: absolute 1e-4 (fp32 exponent sums over up to T terms; |LSE| ~ log T).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from causal_self_exchange_amd import relation as R
+from causal_self_exchange_amd import workloads as W
+from oracle import relation_oracle as O
+from tests._helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+LSE_ATOL = 1e-4
+
+
+class _Env:
+    def __init__(self, **kv):
+        self.kv = kv
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        for k, v in self.kv.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+    def __exit__(self, *a):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _dev(inp, keys=("P1", "P2", "V", "dY")):
+    return [inp[k].to(DEV).contiguous() for k in keys]
+
+
+def _gpu_train(inp, lam, bwd_kernel=None):
+    P1, P2, V, dY = _dev(inp)
+    with _Env(RELATION_BWD_KERNEL=bwd_kernel):
+        Y, L = R.fwd_lse(P1, P2, V, inp["tau"], lam)
+        g = R.bwd(P1, P2, V, inp["tau"], lam, Y, L, dY)
+    torch.cuda.synchronize()
+    return Y, L, g
+
+
+def row_err(g, ref):
+    """max_i ||g_i - ref_i||_inf / max(1, ||ref_i||_inf) over the last axis."""
+    num = np.max(np.abs(g - ref), axis=-1)
+    den = np.maximum(1.0, np.max(np.abs(ref), axis=-1))
+    return float(np.max(num / den))
+
+
+def _oracle(inp, lam):
+    P1, P2, V, dY = (f64(inp[k]) for k in ("P1", "P2", "V", "dY"))
+    tau = inp["tau"].astype(np.float64)
+    B, H, T, D = P1.shape
+    out = dict(dP1=np.empty(P1.shape), dP2=np.empty(P1.shape), dV=np.empty(P1.shape),
+               dtau=np.zeros(H), dlam=0.0, lse=np.empty((B, H, T)),
+               tau_scale=np.zeros(H), lam_scale=0.0)
+    log_i = np.log(np.arange(1, T + 1, dtype=np.float64))
+    for b in range(B):
+        for h in range(H):
+            *g, t = O.relation_head_bwd(P1[b, h], P2[b, h], V[b, h], tau[h], lam, dY[b, h], return_terms=True)
+            out["dP1"][b, h], out["dP2"][b, h], out["dV"][b, h] = g[0], g[1], g[2]
+            out["dtau"][h] += g[3]
+            out["dlam"] += g[4]
+            out["lse"][b, h] = O.row_lse(P1[b, h], P2[b, h], tau[h], lam)
+            Y = O.relation_head(P1[b, h], P2[b, h], V[b, h], tau[h], lam)
+            size = t["F_self"] * np.sum(np.abs(dY[b, h]) * (np.abs(V[b, h]) + np.abs(Y)), axis=1)
+            out["tau_scale"][h] += np.sum(size * t["S"] * (1 - t["S"]) * np.abs(t["U_self"]) / tau[h] ** 2)
+            out["lam_scale"] += np.sum(size * log_i)
+    return out
+
+
+def _check(inp, lam, dt, Y, L, g, what):
+    ref = _oracle(inp, lam)
+    tol = TOL[dt]
+    errs = {}
+    lse_err = float(np.max(np.abs(f64(L) - ref["lse"])))
+    errs["lse"] = lse_err
+    for name, got in zip(("dP1", "dP2", "dV"), g[:3]):
+        x = f64(got)
+        assert np.all(np.isfinite(x)), f"{what}: non-finite {name}"
+        errs[name] = row_err(x, ref[name])
+    dtau = f64(g[3])
+    dlam = float(f64(g[4])[0])
+    errs["dtau"] = float(np.max(np.abs(dtau - ref["dtau"]) / (ref["tau_scale"] + 1e-30)))
+    errs["dlam"] = abs(dlam - ref["dlam"]) / (ref["lam_scale"] + 1e-30)
+    print(f"\n{what}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert lse_err <= LSE_ATOL, f"{what}: LSE error {lse_err:.3e}"
+    for name in ("dP1", "dP2", "dV"):
+        assert errs[name] <= tol, f"{what}: {name} row error {errs[name]:.3e} > {tol}"
+    assert np.all(np.abs(dtau - ref["dtau"]) <= tol * ref["tau_scale"] + 1e-6), (what, dtau, ref["dtau"])
+    assert abs(dlam - ref["dlam"]) <= tol * ref["lam_scale"] + 1e-6, (what, dlam, ref["dlam"])
+    return errs
+
+
+SHAPES = [
+    # B, H, T, d_h, dtype  (bf16 d_h 64/128: MFMA kernels; the rest: row-scan kernels)
+    (1, 1, 1, 64, "bf16"), (1, 2, 2, 128, "bf16"), (1, 1, 65, 128, "bf16"), (2, 3, 100, 64, "bf16"),
+    (1, 2, 129, 128, "bf16"), (3, 1, 191, 64, "bf16"), (1, 2, 300, 128, "bf16"), (1, 1, 513, 128, "bf16"),
+    (2, 2, 100, 32, "bf16"), (1, 2, 77, 32, "f32"), (1, 1, 64, 64, "f32"), (1, 1, 150, 128, "f32"),
+    (1, 1, 1, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_ragged_shapes(shape, lam):
+    B, H, T, D, dt = shape
+    cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0), lam=lam)
+    inp = W.make_bwd_inputs(cfg, 11 + T)
+    Y, L, g = _gpu_train(inp, lam)
+    _check(inp, lam, dt, Y, L, g, f"{shape} lam={lam}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_bwd_config_full(name):
+    """Tiny (fp32, row-scan kernels) and Small (bf16, MFMA kernels) in full."""
+    cfg = W.CONFIGS[name]
+    inp = W.make_bwd_inputs(cfg, 42)
+    Y, L, g = _gpu_train(inp, 0.0)
+    _check(inp, 0.0, cfg.dtype, Y, L, g, name)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_scan_kernels_bf16(D):
+    """The row-scan backward forced for bf16 meets the same bar."""
+    cfg = W.FwdConfig("t", 1, 2, 200, D, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_bwd_inputs(cfg, 5)
+    Y, L, g = _gpu_train(inp, 0.5, bwd_kernel="scan")
+    _check(inp, 0.5, "bf16", Y, L, g, f"scan D={D}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fwd_lse_output_equals_plain_forward(dt):
+    """relation_fwd_lse returns the same Y as relation_fwd_ex, bit for bit."""
+    cfg = W.FwdConfig("t", 2, 3, 333, 128, dt, tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_fwd_inputs(cfg, 3)
+    P1, P2, V = _dev(inp, ("P1", "P2", "V"))
+    Y1 = R.fwd(P1, P2, V, inp["tau"], 0.5)
+    Y2, _ = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_bwd_single_token_passes_dY_to_dV():
+    """T = 1: Y_1 = V_1, so dV = dY exactly and every other gradient is 0."""
+    cfg = W.FwdConfig("t", 2, 2, 1, 128, "bf16", tau=("uniform", 0.5, 2.0))
+    inp = W.make_bwd_inputs(cfg, 9)
+    Y, L, (dP1, dP2, dV, dtau, dlam) = _gpu_train(inp, 0.5)
+    dY = inp["dY"].to(DEV)
+    assert torch.equal(dV, dY)
+    assert float(dP1.abs().max()) == 0.0 and float(dP2.abs().max()) == 0.0
+    assert float(dtau.abs().max()) == 0.0 and float(dlam.abs().max()) == 0.0
+
+
+def test_bwd_zero_upstream_gives_zero_gradients():
+    cfg = W.FwdConfig("t", 1, 2, 300, 128, "bf16")
+    inp = W.make_bwd_inputs(cfg, 2)
+    inp["dY"] = torch.zeros_like(inp["dY"])
+    _, _, g = _gpu_train(inp, 0.5)
+    for x in g:
+        assert float(x.abs().max()) == 0.0
+
+
+def test_bwd_deterministic():
+    """Two calls on the same inputs give identical bits (no atomics)."""
+    cfg = W.FwdConfig("t", 2, 4, 700, 128, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_bwd_inputs(cfg, 4)
+    P1, P2, V, dY = _dev(inp)
+    Y, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
+    g1 = R.bwd(P1, P2, V, inp["tau"], 0.5, Y, L, dY)
+    g2 = R.bwd(P1, P2, V, inp["tau"], 0.5, Y, L, dY)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_gradients_of_the_future_do_not_reach_the_past():
+    """dY zero on rows < k: dP1 is exactly 0 there (row i's query feeds only Y_i)."""
+    cfg = W.FwdConfig("t", 1, 2, 400, 64, "bf16")
+    inp = W.make_bwd_inputs(cfg, 6)
+    inp["dY"][:, :, :150] = 0
+    _, _, (dP1, *_rest) = _gpu_train(inp, 0.0)
+    assert float(dP1[:, :, :150].abs().max()) == 0.0

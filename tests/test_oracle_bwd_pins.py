@@ -171,3 +171,19 @@ def test_row_lse_is_the_paper_partition(lam):
     want = np.logaddexp(fz["S"], fz["A"])
     np.testing.assert_allclose(O.row_lse(p1, p2, 1.2, lam), want, rtol=1e-13, atol=1e-13)
     assert O.row_lse(p1, p2, 1.2, lam)[0] == pytest.approx(fz["S"][0], abs=1e-15)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+def test_row_terms_sum_to_the_scalars_and_rows_of_dR_sum_to_zero(lam):
+    """The per-row terms add up to dtau / dlambda, and since every row of F
+    sums to one, sum_j dR_ij = D_i - D_i = 0: row i's dlambda share
+    -log i sum_{j<i} dR_ij equals log i dR_ii (the form the kernels use)."""
+    rng = np.random.default_rng(13)
+    p1, p2, v, dy = _head(rng, 11, 4, scale=1.3)
+    *g, terms = O.relation_head_bwd(p1, p2, v, 0.7, lam, dy, return_terms=True)
+    assert math.isclose(np.sum(terms["tau_terms"]), g[3], rel_tol=1e-12, abs_tol=1e-14)
+    assert math.isclose(np.sum(terms["lam_terms"]), g[4], rel_tol=1e-12, abs_tol=1e-14)
+    log_i = np.log(np.arange(1, 12))
+    np.testing.assert_allclose(terms["lam_terms"], log_i * terms["dR_self"], rtol=1e-9, atol=1e-13)
+    # and the Self weight is e^{S_i - LSE_i}
+    np.testing.assert_allclose(terms["F_self"], np.exp(terms["S"] - O.row_lse(p1, p2, 0.7, lam)), rtol=1e-12)
