@@ -8,9 +8,10 @@ The default warm-up (200 launches, ~0.15 s) lets the engine clock reach its
 sustained level under MFMA load before the timed region; the paper likewise
 reports steady-state throughput with warm-up excluded.
 
-Prints ONE JSON line. Also reported (not the headline): one Relation Cache
-decode step (B=64, H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of
-algorithmic cache traffic, and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line. Also reported (not the headline): the backward
+(relation_bwd) on the same workload, one Relation Cache decode step (B=64,
+H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of algorithmic cache
+traffic, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -115,6 +116,33 @@ def bench_decode(torch, R, W, steps, warmup):
             "algorithmic_bytes": bytes_alg}
 
 
+def bench_backward(torch, R, W, steps, warmup):
+    """relation_bwd on the T = 8192 workload with a seeded N(0, 1) upstream
+    gradient; LSE and Y from relation_fwd_lse (outside the timed region).
+    Throughput counts the 5 causal products of the gradient (recomputed U,
+    dY V^T, F^T dY, dU P2, dU^T P1): 5 B H T^2 d_h FLOPs, 2.5x the forward's."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_bwd_inputs(cfg, 42)
+    P1, P2, V, dY = (inp[k].cuda() for k in ("P1", "P2", "V", "dY"))
+    tau = inp["tau"]
+    Y, L = R.fwd_lse(P1, P2, V, tau, 0.0)
+    grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
+             torch.empty(cfg.H, dtype=torch.float32, device="cuda"),
+             torch.empty(1, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(R.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        R.bwd(P1, P2, V, tau, 0.0, Y, L, dY, grads=grads, workspace=ws)
+
+    per, total, _ = time_launches(fn, steps, warmup, torch)
+    ms = total / steps
+    flops = 5.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.d_h
+    return {"workload": "backward: B=1 H=32 T=8192 d_h=128 bf16, dY ~ N(0,1), seed 42 (prep + dq + dkv + reduce)",
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "flops_counted": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +150,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
                          "5 times: the reference kernel for scaling HBM byte counters")
@@ -181,6 +210,8 @@ def main():
                      "min_launch_us": round(float(np.min(per)) * 1e3, 2)},
         "wall_s_timed_region": round(wall, 4),
     }
+    if not args.no_backward:
+        out["backward"] = bench_backward(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, R, W, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu_baseline:
