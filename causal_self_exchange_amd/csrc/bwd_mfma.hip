@@ -8,7 +8,8 @@
 // g = dY_i . V_j per tile and form, for j < i,
 //   F_ij = 2^(SiLU(u) log2 e - L2_i),  L2_i = (LSE_i + lambda log i) log2 e,
 //   W_ij = F_ij (g - D_i) SiLU'(u)      (= dU_ij; SiLU'(u) = s (1 + u (1 - s)))
-// with the row statistics L2_i and D_i = dY_i . Y_i from the prep kernel.
+// with the row statistics L2_i and D_i = dY_i . Y_i from the prep kernel
+// (the G accumulators start at -D_i, so the MFMA yields g - D_i directly).
 //
 // dq (query gradient): 8 waves x 32 query rows, key tiles of 64 rows; per tile
 //   U^T[key][q] = P2 . P1^T and G^T[key][q] = V . dY^T (evidence; P1 and dY
@@ -16,16 +17,18 @@
 //   dP1^T[d][q] += P2^T[d][key] W^T[key][q] (transport).
 //   LDS per key tile: P2 in the row layout and the transposed layout, V in
 //   the row layout; a ring of 3 tiles, one barrier per tile.
-// dkv (key/value gradients): 4 waves x 32 key rows, query tiles of 64 rows;
-//   per tile U[q][key] = P1 . P2^T and G[q][key] = dY . V^T (P2 and V rows of
-//   the wave's keys in registers), then
-//   dV^T[d][key] += dY^T[d][q] F[q][key] and dP2^T[d][key] += P1^T[d][q] W[q][key].
-//   LDS per query tile: P1 and dY in both layouts plus the tile's row
-//   statistics; a ring of 2 tiles. Two d_h x 32 fp32 accumulators per wave
-//   need one wave per SIMD.
+// dkv (key/value gradients): 128 key rows, query tiles of 64 rows, 8 waves in
+//   two roles over the same keys and tiles: per 32 keys one wave forms
+//   U[q][key] = P1 . P2^T, F and dV^T[d][key] += dY^T[d][q] F[q][key], the
+//   other U, G[q][key] = dY . V^T, W and dP2^T[d][key] += P1^T[d][q] W[q][key]
+//   (P2 / V rows of the keys in registers). One d_h x 32 accumulator per wave
+//   lets two waves share a SIMD. LDS per query tile: P1 and dY in both
+//   layouts plus the tile's row statistics; a ring of 2 tiles.
 // The Self entries (diagonal) enter in the epilogues from the prep's
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
+#include <type_traits>
+
 #include "mfma_tile.h"
 #include "rel_internal.h"
 #include "rel_device.h"
@@ -40,9 +43,9 @@ constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
 constexpr int kDqRows = kDqWaves * 32;     // query rows per dq work-group
 constexpr int kDqSlots = 3;
-constexpr int kKvWaves = 4;
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kKvRows = kKvWaves * 32;     // key rows per dkv work-group
+constexpr int kKvRows = 4 * 32;            // key rows per dkv work-group (two waves per 32 keys)
 constexpr int kKvSlots = 2;
 
 template <int D>
@@ -81,66 +84,76 @@ __device__ __forceinline__ int64_t stat_at(int64_t bh, int nt, int r, int k) {
   return ((bh * nt + r / kStatRows) * 4 + k) * kStatRows + (r % kStatRows);
 }
 
-// s (1 + u (1 - s)) with s = sigmoid(u): SiLU'(u); and SiLU(u) log2 e.
-struct SiluTerms {
-  float silu2, dsilu;
-  __device__ __forceinline__ SiluTerms(float x, float k2, float c) {
-    const float a2 = x * k2;                                      // u log2 e
+// Weight terms of one raw evidence value x = p1 . p2 (k2 = log2 e / sqrt(d_h),
+// c = 1 / sqrt(d_h), L2 = the row's (LSE + lambda log i) log2 e):
+//   s = sigmoid(u), u = x c;  F = 2^(u s log2 e - L2);  SiLU'(u) = s + u (s - s^2).
+struct Terms {
+  float F, dsilu;
+  __device__ __forceinline__ Terms(float x, float k2, float c, float L2) {
+    const float a2 = x * k2;
     const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a2));
-    silu2 = a2 * sg;
-    dsilu = sg * fmaf(x * c, 1.0f - sg, 1.0f);
+    F = __builtin_amdgcn_exp2f(fmaf(a2, sg, -L2));
+    dsilu = fmaf(x * c, fmaf(-sg, sg, sg), sg);
   }
 };
 
 // dq weights of one 32-key block: W^T[key][q] for this lane's query (row lq),
-// register r <-> key 8 (r / 4) + 4 hf + r % 4 of the block.
-template <bool kMasked>
-__device__ __forceinline__ void dq_weights(const f32x16& s, const f32x16& g, float k2, float c, float L2,
-                                           float Dq, int hf, int lq, u32x4 (&pw)[2]) {
+// register r <-> key 8 (r / 4) + 4 hf + r % 4 of the block; gm holds
+// dY_q . V_key - D_q.
+__device__ __forceinline__ void dq_weights(const f32x16& s, const f32x16& gm, float k2, float c, float L2,
+                                           bool diag, int hf, int lq, u32x4 (&pw)[2]) {
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
     float w[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const SiluTerms t(s[r + e], k2, c);
-      const float F = __builtin_amdgcn_exp2f(t.silu2 - L2);
-      float v = F * (g[r + e] - Dq) * t.dsilu;
-      if (kMasked) v = (8 * ((r + e) >> 2) + 4 * hf + ((r + e) & 3)) < lq ? v : 0.0f;
+      const Terms t(s[r + e], k2, c, L2);
+      float v = t.F * gm[r + e] * t.dsilu;
+      if (diag) v = (8 * ((r + e) >> 2) + 4 * hf + ((r + e) & 3)) < lq ? v : 0.0f;
       w[e] = v;
     }
     pw[r >> 3][(r & 7) >> 1] = pack_bf16(w[0], w[1]);
   }
 }
 
-// dkv weights of one 32-query block: F[q][key] and W[q][key] for this lane's
-// key (row lq), register r <-> query 8 (r / 4) + 4 hf + r % 4 of the block;
-// st points at the tile's statistics in LDS, qb0 = first query of the block
-// within the tile.
-template <bool kMasked>
-__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& g, float k2, float c, const float* st,
-                                           int qb0, int hf, int lq, u32x4 (&pf)[2], u32x4 (&pw)[2]) {
+// dkv weights of one 32-query block for this lane's key (row lq), register r
+// <-> query 8 (r / 4) + 4 hf + r % 4 of the block (qb0 = first query of the
+// block within the tile; st = the tile's statistics in LDS): F[q][key], or
+// with kW the gradient weight W[q][key] = F (dY_q . V_key - D_q) SiLU'(u)
+// (gm holds dY_q . V_key - D_q).
+template <bool kW>
+__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& gm, float k2, float c, const float* st,
+                                           int qb0, bool diag, int hf, int lq, u32x4 (&out)[2]) {
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
-    const int q = qb0 + 8 * g4 + 4 * hf;
-    const float4 L2 = *reinterpret_cast<const float4*>(st + q);
-    const float4 Dq = *reinterpret_cast<const float4*>(st + kStatRows + q);
+    const float4 L2 = *reinterpret_cast<const float4*>(st + qb0 + 8 * g4 + 4 * hf);
     const float l2v[4] = {L2.x, L2.y, L2.z, L2.w};
-    const float dv[4] = {Dq.x, Dq.y, Dq.z, Dq.w};
-    float f[4], w[4];
+    float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g4 + e;
-      const SiluTerms t(s[r], k2, c);
-      float F = __builtin_amdgcn_exp2f(t.silu2 - l2v[e]);
-      if (kMasked) F = lq < 8 * g4 + 4 * hf + e ? F : 0.0f;
-      f[e] = F;
-      w[e] = F * (g[r] - dv[e]) * t.dsilu;
+      const Terms t(s[r], k2, c, l2v[e]);
+      float x = kW ? t.F * gm[r] * t.dsilu : t.F;
+      if (diag) x = lq < 8 * g4 + 4 * hf + e ? x : 0.0f;
+      v[e] = x;
     }
-    pf[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(f[0], f[1]);
-    pf[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(f[2], f[3]);
-    pw[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(w[0], w[1]);
-    pw[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(w[2], w[3]);
+    out[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(v[0], v[1]);
+    out[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(v[2], v[3]);
   }
+}
+
+// -D_q of the 16 queries of a 32-query block in C-layout register order.
+__device__ __forceinline__ f32x16 neg_d_block(const float* st, int qb0, int hf) {
+  f32x16 v;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const float4 d = *reinterpret_cast<const float4*>(st + kStatRows + qb0 + 8 * g4 + 4 * hf);
+    v[4 * g4 + 0] = d.x;
+    v[4 * g4 + 1] = d.y;
+    v[4 * g4 + 2] = d.z;
+    v[4 * g4 + 3] = d.w;
+  }
+  return v;
 }
 
 // Store 4 consecutive bf16 of a row (8 bytes).
@@ -152,6 +165,9 @@ __device__ __forceinline__ void load4(const __bf16* p, float (&x)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
 }
+
+template <bool B>
+using Tag = std::integral_constant<bool, B>;
 
 template <int D>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadParams hp) {
@@ -197,13 +213,18 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   }
   const bool valid = qrow < T;
   const float L2 = valid ? a.stats[stat_at(bh, nt, qrow, 0)] : INFINITY;
-  const float Dq = valid ? a.stats[stat_at(bh, nt, qrow, 1)] : 0.0f;
+  const float negD = valid ? a.stats[stat_at(bh, nt, qrow, 1)] : 0.0f;
+  f32x16 negDv;                                       // G^T accumulators start at -D_q
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negDv[r] = negD;
   const float c = hp.scale;
   const float k2 = c * kLog2e;
 
-  // Keys 0 .. kend-1 are history for some row of this work-group.
+  // Keys 0 .. kend-1 are history for some row of this work-group; tiles
+  // before q0 / 64 are strictly left of every row of it.
   const int kend = min(q0 + kDqRows, T) - 1;
   const int ntiles = (kend + kTileRows - 1) / kTileRows;
+  const int nsteady = min(ntiles, q0 / kTileRows);
 
   // Staging: wave w moves blocks w + 8 u of each of the three layouts.
   const int hb = (int)head_bytes;
@@ -235,9 +256,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  if (ntiles > 0) dma(0);
-  if (ntiles > 1) dma(1);
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile: publish it, refill the slot read two tiles ago, then
+  // evidence, weights and transport per 32-key block. Steady tiles (every
+  // block strictly left of every row) skip the block modes and masks.
+  auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
     if (t + 1 < ntiles) wait_vm_lgkm<C::kDmaTile, 15>();
     else wait_vm_lgkm<0, 15>();
     __builtin_amdgcn_s_barrier();
@@ -252,16 +274,25 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
     const VBase p2t{smem + oe, smem + oo};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int md = mode_keys_below(2 * t + kb, own);
-      if (md == 0) continue;
+      bool diag = false;
+      if constexpr (!decltype(steady)::value) {
+        const int md = mode_keys_below(2 * t + kb, own);
+        if (md == 0) continue;
+        diag = md == 2;
+      }
       const f32x16 s = evidence_block<D>(smem + ok, kb, qf);
-      const f32x16 g = evidence_block<D>(smem + ov, kb, yf);
+      const f32x16 g = evidence_block_from<D>(smem + ov, kb, yf, negDv);
       u32x4 pw[2];
-      if (md == 2) dq_weights<true>(s, g, k2, c, L2, Dq, hf, lq, pw);
-      else dq_weights<false>(s, g, k2, c, L2, Dq, hf, lq, pw);
+      dq_weights(s, g, k2, c, L2, diag, hf, lq, pw);
       transport_block<D>(p2t, kb, pw, acc);
     }
-  }
+  };
+
+  if (ntiles > 0) dma(0);
+  if (ntiles > 1) dma(1);
+  int t = 0;
+  for (; t < nsteady; ++t) tile(t, Tag<true>{});
+  for (; t < ntiles; ++t) tile(t, Tag<false>{});
 
   if (!valid) return;
   // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h); the statistic holds
@@ -282,6 +313,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   }
 }
 
+// Key/value gradients. Waves w and w + 4 own the same 32 keys: waves 0-3
+// form F and accumulate dV^T += dY^T F, waves 4-7 form W and accumulate
+// dP2^T += P1^T W. Each role runs in its own code region (separate register
+// allocation, one d_h x 32 accumulator each), so two waves fit per SIMD.
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
   using C = KvCfg<D>;
@@ -294,6 +329,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const int nt = (T + kStatRows - 1) / kStatRows;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;                             // the wave's 32-key group
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int hf = lane >> 5;
@@ -304,29 +340,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
   const __bf16* V = static_cast<const __bf16*>(a.V) + head;
   const __bf16* dY = static_cast<const __bf16*>(a.dY) + head;
-  __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
-  __bf16* dV = static_cast<__bf16*>(a.dV) + head;
   const float* stats = a.stats + (size_t)bh * nt * kStatTile;
 
   const int k0 = kt * kKvRows;
-  const int krow = k0 + wave * 32 + lq;                // may be >= T: loads give 0, stores drop
-  const int own = k0 / 32 + wave;
-
-  bf16x8 kf[C::kDs], vf[C::kDs];
-  {
-    const auto rP2 = rsrc(P2, head_bytes);
-    const auto rV = rsrc(V, head_bytes);
-    const int koff = krow * (D * 2) + hf * 16;
-#pragma unroll
-    for (int ds = 0; ds < C::kDs; ++ds) {
-      kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, koff + ds * 32, 0, 0));
-      vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
-    }
-  }
+  const int krow = k0 + kw * 32 + lq;                  // may be >= T: loads give 0, stores drop
+  const int own = k0 / 32 + kw;
+  const int koff = krow * (D * 2) + hf * 16;
   const float c = hp.scale;
   const float k2 = c * kLog2e;
 
-  // Query tiles t0 .. nt-1 hold every query i > j of this work-group's keys.
+  // Query tiles t0 .. nt-1 hold every query i > j of this work-group's keys;
+  // from t0 + 2 on, every block lies strictly below every key block.
   const int t0 = k0 / kTileRows;
   const int hb = (int)head_bytes;
   int src_row[C::kPer], src_tr[C::kPer];
@@ -356,67 +380,110 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const int row_base = C::row_base(lane);
   const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
 
-  f32x16 accv[C::kDb], accp[C::kDb];
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool kP = decltype(role)::value;        // true: dP2 waves, false: dV waves
+    bf16x8 kf[C::kDs], vf[kP ? C::kDs : 1];
+    {
+      const auto rP2 = rsrc(P2, head_bytes);
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db)
+      for (int ds = 0; ds < C::kDs; ++ds)
+        kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, koff + ds * 32, 0, 0));
+      if constexpr (kP) {
+        const auto rV = rsrc(V, head_bytes);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      accv[db][r] = 0.0f;
-      accp[db][r] = 0.0f;
+        for (int ds = 0; ds < C::kDs; ++ds)
+          vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
+      }
     }
+    // The first two query tiles (issued after the key rows, so that the
+    // first wait covers both).
+    if (t0 < nt) dma(t0);
+    if (t0 + 1 < nt) dma(t0 + 1);
+    f32x16 acc[C::kDb];
+#pragma unroll
+    for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  if (t0 < nt) dma(t0);
-  if (t0 + 1 < nt) dma(t0 + 1);
-  for (int t = t0; t < nt; ++t) {
-    if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
-    else wait_vm_lgkm<0, 15>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
-    unsigned oq = so + row_base, oy = so + C::kKBytes + row_base;
-    unsigned qe = so + 2 * C::kKBytes + tr_even, qo = so + 2 * C::kKBytes + tr_odd;
-    unsigned ye = qe + C::kVBytes, yo = qo + C::kVBytes;
-    asm volatile("" : "+v"(oq), "+v"(oy), "+v"(qe), "+v"(qo), "+v"(ye), "+v"(yo));
-    const VBase p1t{smem + qe, smem + qo};
-    const VBase dyt{smem + ye, smem + yo};
-    const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
+    auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
+      if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
+      else wait_vm_lgkm<0, 15>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
+      unsigned orow = so + row_base;                                        // P1 row layout
+      unsigned oy = so + C::kKBytes + row_base;                             // dY row layout
+      unsigned te = so + 2 * C::kKBytes + (kP ? 0 : C::kVBytes) + tr_even;  // P1^T (dP2) or dY^T (dV)
+      unsigned to = so + 2 * C::kKBytes + (kP ? 0 : C::kVBytes) + tr_odd;
+      asm volatile("" : "+v"(orow), "+v"(oy), "+v"(te), "+v"(to));
+      const VBase xt{smem + te, smem + to};
+      const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int md = mode_queries_above(2 * t + qb, own);
-      if (md == 0) continue;
-      const f32x16 s = evidence_block<D>(smem + oq, qb, kf);
-      const f32x16 g = evidence_block<D>(smem + oy, qb, vf);
-      u32x4 pf[2], pw[2];
-      if (md == 2) kv_weights<true>(s, g, k2, c, st, 32 * qb, hf, lq, pf, pw);
-      else kv_weights<false>(s, g, k2, c, st, 32 * qb, hf, lq, pf, pw);
-      transport_block<D>(dyt, qb, pf, accv);
-      transport_block<D>(p1t, qb, pw, accp);
-    }
-    // Every wave is done with this slot before it is refilled.
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + 2 < nt) dma(t + 2);
-  }
+      for (int qb = 0; qb < 2; ++qb) {
+        bool diag = false;
+        if constexpr (!decltype(steady)::value) {
+          const int md = mode_queries_above(2 * t + qb, own);
+          if (md == 0) continue;
+          diag = md == 2;
+        }
+        const f32x16 s = evidence_block<D>(smem + orow, qb, kf);
+        u32x4 pw[2];
+        if constexpr (kP) {
+          const f32x16 g = evidence_block_from<D>(smem + oy, qb, vf, neg_d_block(st, 32 * qb, hf));
+          kv_weights<true>(s, g, k2, c, st, 32 * qb, diag, hf, lq, pw);
+        } else {
+          kv_weights<false>(s, s, k2, c, st, 32 * qb, diag, hf, lq, pw);
+        }
+        transport_block<D>(xt, qb, pw, acc);
+      }
+      // Every wave is done with this slot before it is refilled.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 2 < nt) dma(t + 2);
+    };
 
-  if (krow >= T) return;
-  const float fs = stats[stat_at(0, nt, krow, 2)];
-  const float us = stats[stat_at(0, nt, krow, 3)];
-  const size_t ro = (size_t)krow * D;
+    int t = t0;
+    for (; t < min(t0 + 2, nt); ++t) tile(t, Tag<false>{});
+    for (; t < nt; ++t) tile(t, Tag<true>{});
+
+    if (krow >= T) return;
+    const size_t ro = (size_t)krow * D;
+    if constexpr (kP) {
+      // dP2_j = (sum_i dU_ij p1_i + dU_jj p1_j) / sqrt(d_h).
+      __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
+      const float us = stats[stat_at(0, nt, krow, 3)];
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db) {
+      for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int col = 32 * db + 8 * g4 + 4 * hf;
-      const int r = 4 * g4;
-      float y[4], p[4];
-      load4(dY + ro + col, y);
-      load4(P1 + ro + col, p);
-      store4(dV + ro + col, fmaf(fs, y[0], accv[db][r + 0]), fmaf(fs, y[1], accv[db][r + 1]),
-             fmaf(fs, y[2], accv[db][r + 2]), fmaf(fs, y[3], accv[db][r + 3]));
-      store4(dP2 + ro + col, fmaf(accp[db][r + 0], c, us * p[0]), fmaf(accp[db][r + 1], c, us * p[1]),
-             fmaf(accp[db][r + 2], c, us * p[2]), fmaf(accp[db][r + 3], c, us * p[3]));
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * db + 8 * g4 + 4 * hf;
+          const int r = 4 * g4;
+          float p[4];
+          load4(P1 + ro + col, p);
+          store4(dP2 + ro + col, fmaf(acc[db][r + 0], c, us * p[0]), fmaf(acc[db][r + 1], c, us * p[1]),
+                 fmaf(acc[db][r + 2], c, us * p[2]), fmaf(acc[db][r + 3], c, us * p[3]));
+        }
+      }
+    } else {
+      // dV_j = sum_i F_ij dY_i + F_jj dY_j.
+      __bf16* dV = static_cast<__bf16*>(a.dV) + head;
+      const float fs = stats[stat_at(0, nt, krow, 2)];
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * db + 8 * g4 + 4 * hf;
+          const int r = 4 * g4;
+          float y[4];
+          load4(dY + ro + col, y);
+          store4(dV + ro + col, fmaf(fs, y[0], acc[db][r + 0]), fmaf(fs, y[1], acc[db][r + 1]),
+                 fmaf(fs, y[2], acc[db][r + 2]), fmaf(fs, y[3], acc[db][r + 3]));
+        }
+      }
     }
-  }
+  };
+  if (wave >= 4) run(Tag<true>{});
+  else run(Tag<false>{});
 }
 
 template <int D>

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a, HeadP
         const float dR = Fs * (dyv - dyy);              // dR_ii
         const float sp = S * (1.0f - S);
         st[0] = (lse + hp.lambda * logi) * kLog2eF;
-        st[1] = dyy;
+        st[1] = -dyy;
         st[2] = Fs;
         st[3] = dR * sp * inv_tau * hp.scale;
         part_tau += dR * sp * (-u * inv_tau * inv_tau);
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kRows) void bwd_scan_dq_kernel(BwdArgs a, HeadParam
     acc[k] = 0.0f;
   }
   const float L2 = valid ? a.stats[stat_index(bh, nt, r, 0)] : 0.0f;
-  const float Dr = valid ? a.stats[stat_index(bh, nt, r, 1)] : 0.0f;
+  const float negD = valid ? a.stats[stat_index(bh, nt, r, 1)] : 0.0f;
 
   const int last = min(T - 1, row0 + kRows - 1);
   for (int j0 = 0; j0 < last; j0 += kKeys) {
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kRows) void bwd_scan_dq_kernel(BwdArgs a, HeadParam
         const float u = s * hp.scale;
         const float sg = sigmoid_f32(u);
         const float F = exp2f(u * sg * kLog2eF - L2);
-        const float w = F * (g - Dr) * (sg * (1.0f + u * (1.0f - sg)));
+        const float w = F * (g + negD) * (sg * (1.0f + u * (1.0f - sg)));
 #pragma unroll
         for (int k = 0; k < D; ++k) acc[k] = fmaf(w, sP2[jj][k], acc[k]);
       }
@@ -244,7 +244,7 @@ template <typename Tin, int D, bool kDV>
 __global__ __launch_bounds__(kRows) void bwd_scan_dkv_kernel(BwdArgs a, HeadParams hp) {
   __shared__ float sP1[kKeys][D];
   __shared__ float sdY[kKeys][D];
-  __shared__ float sL2[kKeys], sD[kKeys];
+  __shared__ float sL2[kKeys], snD[kKeys];
   const int lane = threadIdx.x;
   const int bh = blockIdx.z * a.H + blockIdx.y;
   const int T = a.T;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kRows) void bwd_scan_dkv_kernel(BwdArgs a, HeadPara
     if (lane < kKeys) {
       const int i = i0 + lane;
       sL2[lane] = i < T ? a.stats[stat_index(bh, nt, i, 0)] : INFINITY;
-      sD[lane] = i < T ? a.stats[stat_index(bh, nt, i, 1)] : 0.0f;
+      snD[lane] = i < T ? a.stats[stat_index(bh, nt, i, 1)] : 0.0f;
     }
     __syncthreads();
     for (int ii = 0; ii < kKeys; ++ii) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kRows) void bwd_scan_dkv_kernel(BwdArgs a, HeadPara
 #pragma unroll
           for (int k = 0; k < D; ++k) acc[k] = fmaf(F, sdY[ii][k], acc[k]);
         } else {
-          const float w = F * (g - sD[ii]) * (sg * (1.0f + u * (1.0f - sg)));
+          const float w = F * (g + snD[ii]) * (sg * (1.0f + u * (1.0f - sg)));
 #pragma unroll
           for (int k = 0; k < D; ++k) acc[k] = fmaf(w, sP1[ii][k], acc[k]);
         }

@@ -163,6 +163,20 @@ __device__ __forceinline__ f32x16 evidence_block(const char* kl, int kb, const b
   return s;
 }
 
+// As evidence_block, with the accumulator starting at `init` instead of 0.
+template <int D>
+__device__ __forceinline__ f32x16 evidence_block_from(const char* kl, int kb, const bf16x8 (&z)[D / 16],
+                                                      const f32x16& init) {
+  using L = TileLayout<D>;
+  f32x16 s = init;
+#pragma unroll
+  for (int ds = 0; ds < L::kDs; ++ds) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + L::k_imm(kb, ds));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, z[ds], s, 0, 0, 0);
+  }
+  return s;
+}
+
 // Transposed operand of transport MFMA i = (block kb, k-step ks, O^T block db);
 // the row order inside an MFMA k-step matches the register order of the
 // evidence tile.

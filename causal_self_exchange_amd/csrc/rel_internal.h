@@ -40,7 +40,7 @@ struct DecodeArgs {
 // of each (b, h) as four arrays of 64 floats, so that one 1 KB direct load
 // brings a tile's values into LDS:
 //   [0]  (LSE_i + lambda log i) log2 e   (+inf on padding rows past T)
-//   [1]  D_i = dY_i . Y_i
+//   [1]  -D_i,  D_i = dY_i . Y_i
 //   [2]  F_ii  (the Self weight of row i)
 //   [3]  dU_ii / sqrt(d_h)  (Self gradient of the evidence, scaled)
 // Partials of dtau / dlambda are written per (b, h, 256-row chunk) and summed
