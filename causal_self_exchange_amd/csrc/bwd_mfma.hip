@@ -17,13 +17,15 @@
 //   dP1^T[d][q] += P2^T[d][key] W^T[key][q] (transport).
 //   LDS per key tile: P2 in the row layout and the transposed layout, V in
 //   the row layout; a ring of 3 tiles, one barrier per tile.
-// dkv (key/value gradients): 128 key rows, query tiles of 64 rows, 8 waves in
-//   two roles over the same keys and tiles: per 32 keys one wave forms
-//   U[q][key] = P1 . P2^T, F and dV^T[d][key] += dY^T[d][q] F[q][key], the
-//   other U, G[q][key] = dY . V^T, W and dP2^T[d][key] += P1^T[d][q] W[q][key]
-//   (P2 / V rows of the keys in registers). One d_h x 32 accumulator per wave
-//   lets two waves share a SIMD. LDS per query tile: P1 and dY in both
-//   layouts plus the tile's row statistics; a ring of 2 tiles.
+// dkv (key/value gradients): 128 key rows, query tiles of 64 rows, 8 waves;
+//   per 32 keys two waves split each tile by 32-query block and form
+//   U[q][key] = P1 . P2^T, G[q][key] = dY . V^T (P2 and V rows of the keys in
+//   registers), F and W of their block; one accumulates
+//   dV^T[d][key] += dY^T[d][q] F[q][key], the other
+//   dP2^T[d][key] += P1^T[d][q] W[q][key], each taking the partner's block's
+//   operand through LDS. One d_h x 32 accumulator per wave lets two waves
+//   share a SIMD. LDS per query tile: P1 and dY in both layouts plus the
+//   tile's row statistics; a ring of 2 tiles and a 16 KB exchange area.
 // The Self entries (diagonal) enter in the epilogues from the prep's
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
@@ -65,7 +67,10 @@ struct KvCfg : TileLayout<D> {
   // Slot: [P1 row][dY row][P1 transposed][dY transposed][statistics, 1 KB].
   static constexpr int kStatOff = 2 * L::kKBytes + 2 * L::kVBytes;
   static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
-  static constexpr int kLdsBytes = kKvSlots * kSlotBytes;
+  // Exchange area: per 32-key group and 32-query block, one packed bf16
+  // transport operand (64 lanes x 32 bytes).
+  static constexpr int kXBytes = 4 * 2 * 64 * 32;
+  static constexpr int kLdsBytes = kKvSlots * kSlotBytes + kXBytes;
   static constexpr int kPer = L::kBlocks / kKvWaves;
   // Direct loads per wave and tile (wave 0 also moves the statistics; the
   // waits use the smaller count, which is conservative for wave 0).
@@ -118,27 +123,29 @@ __device__ __forceinline__ void dq_weights(const f32x16& s, const f32x16& gm, fl
 
 // dkv weights of one 32-query block for this lane's key (row lq), register r
 // <-> query 8 (r / 4) + 4 hf + r % 4 of the block (qb0 = first query of the
-// block within the tile; st = the tile's statistics in LDS): F[q][key], or
-// with kW the gradient weight W[q][key] = F (dY_q . V_key - D_q) SiLU'(u)
-// (gm holds dY_q . V_key - D_q).
-template <bool kW>
+// block within the tile; st = the tile's statistics in LDS): the flow
+// F[q][key] and the gradient weight W[q][key] = F (dY_q . V_key - D_q) SiLU'(u)
+// (gm holds dY_q . V_key - D_q), as packed bf16 transport operands.
 __device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& gm, float k2, float c, const float* st,
-                                           int qb0, bool diag, int hf, int lq, u32x4 (&out)[2]) {
+                                           int qb0, bool diag, int hf, int lq, u32x4 (&pf)[2], u32x4 (&pw)[2]) {
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const float4 L2 = *reinterpret_cast<const float4*>(st + qb0 + 8 * g4 + 4 * hf);
     const float l2v[4] = {L2.x, L2.y, L2.z, L2.w};
-    float v[4];
+    float f[4], w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g4 + e;
       const Terms t(s[r], k2, c, l2v[e]);
-      float x = kW ? t.F * gm[r] * t.dsilu : t.F;
-      if (diag) x = lq < 8 * g4 + 4 * hf + e ? x : 0.0f;
-      v[e] = x;
+      float F = t.F;
+      if (diag) F = lq < 8 * g4 + 4 * hf + e ? F : 0.0f;
+      f[e] = F;
+      w[e] = F * gm[r] * t.dsilu;
     }
-    out[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(v[0], v[1]);
-    out[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(v[2], v[3]);
+    pf[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(f[0], f[1]);
+    pf[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(f[2], f[3]);
+    pw[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(w[0], w[1]);
+    pw[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(w[2], w[3]);
   }
 }
 
@@ -313,10 +320,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   }
 }
 
-// Key/value gradients. Waves w and w + 4 own the same 32 keys: waves 0-3
-// form F and accumulate dV^T += dY^T F, waves 4-7 form W and accumulate
-// dP2^T += P1^T W. Each role runs in its own code region (separate register
-// allocation, one d_h x 32 accumulator each), so two waves fit per SIMD.
+// Key/value gradients. Waves w and w + 4 own the same 32 keys (group kg = w % 4)
+// and split each 64-query tile by 32-query block: wave w forms U, G, F and W
+// of block 0, wave w + 4 those of block 1. Each keeps one accumulator (waves
+// 0-3 dV^T, waves 4-7 dP2^T), transports its own block at once and hands the
+// other operand (W of block 0, F of block 1) to its partner through LDS; after
+// a barrier each transports the partner's block. Both roles do the same MFMA
+// and VALU work, and each runs in its own code region so that two waves fit
+// per SIMD.
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
   using C = KvCfg<D>;
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const int nt = (T + kStatRows - 1) / kStatRows;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = wave & 3;                             // the wave's 32-key group
+  const int kg = wave & 3;                             // the wave's 32-key group
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int hf = lane >> 5;
@@ -343,8 +354,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const float* stats = a.stats + (size_t)bh * nt * kStatTile;
 
   const int k0 = kt * kKvRows;
-  const int krow = k0 + kw * 32 + lq;                  // may be >= T: loads give 0, stores drop
-  const int own = k0 / 32 + kw;
+  const int krow = k0 + kg * 32 + lq;                  // may be >= T: loads give 0, stores drop
+  const int own = k0 / 32 + kg;
   const int koff = krow * (D * 2) + hf * 16;
   const float c = hp.scale;
   const float k2 = c * kLog2e;
@@ -379,20 +390,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   };
   const int row_base = C::row_base(lane);
   const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
+  // Exchange slots of this key group: [block 0: W][block 1: F], 32 bytes per lane.
+  char* const xw = smem + kKvSlots * C::kSlotBytes + (kg * 2 + 0) * 2048 + 32 * lane;
+  char* const xf = smem + kKvSlots * C::kSlotBytes + (kg * 2 + 1) * 2048 + 32 * lane;
 
   auto run = [&](auto role) __attribute__((always_inline)) {
-    constexpr bool kP = decltype(role)::value;        // true: dP2 waves, false: dV waves
-    bf16x8 kf[C::kDs], vf[kP ? C::kDs : 1];
+    constexpr bool kP = decltype(role)::value;        // false: block 0 and dV; true: block 1 and dP2
+    constexpr int qb = kP ? 1 : 0;                     // the block this wave forms
+    bf16x8 kf[C::kDs], vf[C::kDs];
     {
       const auto rP2 = rsrc(P2, head_bytes);
+      const auto rV = rsrc(V, head_bytes);
 #pragma unroll
-      for (int ds = 0; ds < C::kDs; ++ds)
+      for (int ds = 0; ds < C::kDs; ++ds) {
         kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, koff + ds * 32, 0, 0));
-      if constexpr (kP) {
-        const auto rV = rsrc(V, head_bytes);
-#pragma unroll
-        for (int ds = 0; ds < C::kDs; ++ds)
-          vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
+        vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
       }
     }
     // The first two query tiles (issued after the key rows, so that the
@@ -418,25 +430,37 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
       asm volatile("" : "+v"(orow), "+v"(oy), "+v"(te), "+v"(to));
       const VBase xt{smem + te, smem + to};
       const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        bool diag = false;
-        if constexpr (!decltype(steady)::value) {
-          const int md = mode_queries_above(2 * t + qb, own);
-          if (md == 0) continue;
-          diag = md == 2;
-        }
-        const f32x16 s = evidence_block<D>(smem + orow, qb, kf);
-        u32x4 pw[2];
-        if constexpr (kP) {
-          const f32x16 g = evidence_block_from<D>(smem + oy, qb, vf, neg_d_block(st, 32 * qb, hf));
-          kv_weights<true>(s, g, k2, c, st, 32 * qb, diag, hf, lq, pw);
-        } else {
-          kv_weights<false>(s, s, k2, c, st, 32 * qb, diag, hf, lq, pw);
-        }
-        transport_block<D>(xt, qb, pw, acc);
+      bool mine = true, other = true, diag = false;
+      if constexpr (!decltype(steady)::value) {
+        const int md = mode_queries_above(2 * t + qb, own);
+        mine = md != 0;
+        diag = md == 2;
+        other = mode_queries_above(2 * t + (1 - qb), own) != 0;
       }
-      // Every wave is done with this slot before it is refilled.
+      if (mine) {
+        const f32x16 s = evidence_block<D>(smem + orow, qb, kf);
+        const f32x16 g = evidence_block_from<D>(smem + oy, qb, vf, neg_d_block(st, 32 * qb, hf));
+        u32x4 pf[2], pw[2];
+        kv_weights(s, g, k2, c, st, 32 * qb, diag, hf, lq, pf, pw);
+        // Hand the partner its operand, then transport this block.
+        const u32x4(&give)[2] = kP ? pf : pw;
+        char* const xo = kP ? xf : xw;
+        *reinterpret_cast<u32x4*>(xo) = give[0];
+        *reinterpret_cast<u32x4*>(xo + 16) = give[1];
+        transport_block<D>(xt, qb, kP ? pw : pf, acc);
+      }
+      wait_vm_lgkm<63, 0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (other) {
+        const char* xi = kP ? xw : xf;
+        u32x4 op[2];
+        op[0] = *reinterpret_cast<const u32x4*>(xi);
+        op[1] = *reinterpret_cast<const u32x4*>(xi + 16);
+        transport_block<D>(xt, 1 - qb, op, acc);
+      }
+      // Every wave is done with this slot (and the exchange area) before
+      // either is rewritten.
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if (t + 2 < nt) dma(t + 2);
