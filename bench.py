@@ -9,7 +9,9 @@ sustained level under MFMA load before the timed region; the paper likewise
 reports steady-state throughput with warm-up excluded.
 
 Prints ONE JSON line. Also reported (not the headline): the backward
-(relation_bwd) on the same workload, one Relation Cache decode step (B=64,
+(relation_bwd) on the same workload, the model-side pre-steps (RoPE + Givens,
+relation_prestep) and the forward on raw projections (relation_fwd_model) on
+its shape, one Relation Cache decode step (B=64,
 H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of algorithmic cache
 traffic, and the CPU oracle timed on a bounded sample.
 """
@@ -143,6 +145,38 @@ def bench_backward(torch, R, W, steps, warmup):
             "flops_counted": flops}
 
 
+def bench_prestep(torch, R, W, steps, warmup):
+    """relation_prestep (RoPE on P1/P2 + Givens mixing of I, one HBM pass) and
+    relation_fwd_model (pre-step + forward) on the T = 8192 workload's shape,
+    interleaved rotary pairs, base 1e4, pairing A, seeded angles."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_fwd_inputs(cfg, 42)
+    P1, P2, I = (inp[k].cuda() for k in ("P1", "P2", "V"))
+    theta = np.random.default_rng(43).uniform(-np.pi, np.pi, cfg.H // 2).astype(np.float32)
+    out = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(I))
+
+    def pre():
+        R.prestep(P1, P2, I, None, "interleaved", 1e4, theta, "A", out=out)
+
+    per, total, _ = time_launches(pre, steps, warmup, torch)
+    ms = total / steps
+    nbytes = 6.0 * cfg.B * cfg.H * cfg.T * cfg.d_h * 2      # read P1, P2, I; write three outputs
+    Y = torch.empty_like(I)
+    ws = torch.empty(R.lib().relation_fwd_model_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h, R.REL_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def model():
+        R.fwd_model(P1, P2, I, inp["tau"], 0.0, None, "interleaved", 1e4, theta, "A", out=Y, workspace=ws)
+
+    _, mtotal, _ = time_launches(model, steps, warmup, torch)
+    mms = mtotal / steps
+    return {"workload": "pre-steps: B=1 H=32 T=8192 d_h=128 bf16, interleaved RoPE base 1e4, Givens pairing A",
+            "prestep_us": round(ms * 1e3, 2), "prestep_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "prestep_frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "fwd_model_ms": round(mms, 4),
+            "fwd_model_TFLOP/s": round(cfg.flops / (mms * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +185,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-prestep", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
                          "5 times: the reference kernel for scaling HBM byte counters")
@@ -212,6 +247,8 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = bench_backward(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_prestep:
+        out["prestep"] = bench_prestep(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, R, W, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu_baseline:

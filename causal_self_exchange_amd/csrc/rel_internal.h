@@ -69,6 +69,28 @@ struct BwdArgs {
 inline int64_t bwd_stat_floats(int64_t BH, int64_t T) { return BH * ((T + kStatRows - 1) / kStatRows) * kStatTile; }
 inline int64_t bwd_part_floats(int64_t BH, int64_t T) { return BH * ((T + kPrepRows - 1) / kPrepRows) * 2; }
 
+// Model-side pre-steps: rotary encoding of P1 / P2 and Givens mixing of the
+// information heads (one HBM pass; outputs may be the inputs).
+struct PrestepArgs {
+  const void* P1;
+  const void* P2;
+  const void* I;
+  const int32_t* pos0;  // optional device int32[B]: position of row 0 per sequence
+  void* P1o;
+  void* P2o;
+  void* Io;
+  int B, H, T, d_h;
+  int rope;             // 0 none, 1 interleaved pairs, 2 half split
+  int pairing;          // 0: (1,2),(3,4),...; 1: (2,3),...,(H,1) (one-based heads)
+  int mix;              // 1: Givens mixing of I, 0: copy
+};
+
+struct PrestepParams {
+  double inv_freq[64];  // base^(-2k/d_h), k < d_h / 2
+  float cos_theta[128]; // per Givens pair
+  float sin_theta[128];
+};
+
 // Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
 // states per (b, h), one per partial work-group.
 constexpr int kDecodeChunk = 256;
@@ -84,6 +106,7 @@ hipError_t launch_bwd_scan(const BwdArgs& a, const HeadParams& hp, bool bf16, hi
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(int d_h, int T);
+hipError_t launch_prestep(const PrestepArgs& a, const PrestepParams& pp, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
                                int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s);

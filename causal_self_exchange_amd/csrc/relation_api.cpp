@@ -102,6 +102,50 @@ bool use_bwd_mfma(rel_dtype dt, int d_h, int T) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Validates a pre-step call and fills its launch arguments (no HIP call).
+rel_status prestep_setup(rel::PrestepArgs& a, rel::PrestepParams& pp, const void* P1, const void* P2,
+                         const void* I, const int32_t* pos0, rel_rope rope, float rope_base,
+                         const float* theta, rel_pairing pairing, void* P1o, void* P2o, void* Io, int B,
+                         int H, int T, int d_h, rel_dtype dt) {
+  if (!P1 || !P2 || !I || !P1o || !P2o || !Io) return REL_E_NULL;
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
+  if (theta && (H % 2 != 0)) return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (rope != REL_ROPE_NONE && rope != REL_ROPE_INTERLEAVED && rope != REL_ROPE_HALF) return REL_E_PRESTEP;
+  if (pairing != REL_PAIRS_A && pairing != REL_PAIRS_B) return REL_E_PRESTEP;
+  if (rope != REL_ROPE_NONE && !(std::isfinite(rope_base) && rope_base > 1.0f)) return REL_E_PRESTEP;
+  if (theta)
+    for (int k = 0; k < H / 2; ++k)
+      if (!std::isfinite(theta[k])) return REL_E_PRESTEP;
+  if (!aligned16(P1) || !aligned16(P2) || !aligned16(I) || !aligned16(P1o) || !aligned16(P2o) ||
+      !aligned16(Io) || (reinterpret_cast<uintptr_t>(pos0) & 3u))
+    return REL_E_ALIGN;
+  const size_t tb = static_cast<size_t>(n) * elem_size(dt);
+  const size_t pb = static_cast<size_t>(B) * sizeof(int32_t);
+  // Each output may be its own input (in place) but may overlap nothing else.
+  const void* ins[3] = {P1, P2, I};
+  void* outs[3] = {P1o, P2o, Io};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (!(o == i && outs[o] == ins[i]) && overlaps(outs[o], tb, ins[i], tb)) return REL_E_ALIAS;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(outs[o], tb, outs[q], tb)) return REL_E_ALIAS;
+    if (pos0 && overlaps(outs[o], tb, pos0, pb)) return REL_E_ALIAS;
+  }
+  a = rel::PrestepArgs{P1, P2, I, pos0, P1o, P2o, Io, B, H, T, d_h, static_cast<int>(rope),
+                       pairing == REL_PAIRS_A ? 0 : 1, theta ? 1 : 0};
+  for (int k = 0; k < 64; ++k)
+    pp.inv_freq[k] = k < d_h / 2 ? std::pow(static_cast<double>(rope_base), -2.0 * k / d_h) : 0.0;
+  for (int k = 0; k < 128; ++k) {
+    const double t = (theta && k < H / 2) ? static_cast<double>(theta[k]) : 0.0;
+    pp.cos_theta[k] = static_cast<float>(std::cos(t));
+    pp.sin_theta[k] = static_cast<float>(std::sin(t));
+  }
+  return REL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +163,7 @@ const char* relation_status_str(rel_status s) {
     case REL_E_ALIAS: return "output overlaps an input or another output";
     case REL_E_WORKSPACE: return "workspace missing or too small";
     case REL_E_LAUNCH: return "kernel launch failed";
+    case REL_E_PRESTEP: return "invalid rotary mode, base, pairing or Givens angle";
   }
   return "unknown status";
 }
@@ -135,6 +180,64 @@ rel_status relation_fwd_lse(const void* P1, const void* P2, const void* V, const
                             rel_dtype dt, hipStream_t stream) {
   if (!P1 || !P2 || !V || !tau_s || !Y || !LSE) return REL_E_NULL;
   return fwd_impl(P1, P2, V, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
+}
+
+rel_status relation_prestep(const void* P1, const void* P2, const void* I, const int32_t* pos0,
+                            rel_rope rope, float rope_base, const float* theta, rel_pairing pairing,
+                            void* P1o, void* P2o, void* Io, int B, int H, int T, int d_h, rel_dtype dt,
+                            hipStream_t stream) {
+  rel::PrestepArgs a;
+  rel::PrestepParams pp;
+  const rel_status st = prestep_setup(a, pp, P1, P2, I, pos0, rope, rope_base, theta, pairing, P1o, P2o, Io,
+                                      B, H, T, d_h, dt);
+  if (st != REL_OK) return st;
+  return rel::launch_prestep(a, pp, dt == REL_BF16, stream) == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+size_t relation_fwd_model_workspace_bytes(int B, int H, int T, int d_h, rel_dtype dt) {
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h) || !dtype_ok(dt)) return 0;
+  return 3 * align256(static_cast<size_t>(n) * elem_size(dt));
+}
+
+rel_status relation_fwd_model(const void* P1, const void* P2, const void* I, const int32_t* pos0,
+                              rel_rope rope, float rope_base, const float* theta, rel_pairing pairing,
+                              const float* tau_s, float lambda, void* Y, float* LSE, int B, int H, int T,
+                              int d_h, rel_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!P1 || !P2 || !I || !tau_s || !Y) return REL_E_NULL;
+  const size_t need = relation_fwd_model_workspace_bytes(B, H, T, d_h, dt);
+  if (need == 0) {
+    int64_t n = 0;
+    if (!count(n, {B, H, T, d_h})) return REL_E_SHAPE;
+    return dtype_ok(dt) ? REL_E_HEADDIM : REL_E_DTYPE;
+  }
+  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  const size_t part = need / 3;
+  char* ws = static_cast<char*>(workspace);
+  rel::PrestepArgs a;
+  rel::PrestepParams pp;
+  rel_status st = prestep_setup(a, pp, P1, P2, I, pos0, rope, rope_base, theta, pairing, ws, ws + part,
+                                ws + 2 * part, B, H, T, d_h, dt);
+  if (st != REL_OK) return st;
+  // The forward's own checks (tau, lambda, Y and LSE against the workspace
+  // tensors and the raw inputs) run before anything is launched.
+  const size_t tb = static_cast<size_t>(B) * H * T * d_h * elem_size(dt);
+  if (!aligned16(Y)) return REL_E_ALIGN;
+  if (overlaps(Y, tb, P1, tb) || overlaps(Y, tb, P2, tb) || overlaps(Y, tb, I, tb) ||
+      overlaps(Y, tb, workspace, need) || (pos0 && overlaps(Y, tb, pos0, static_cast<size_t>(B) * 4)))
+    return REL_E_ALIAS;
+  if (LSE) {
+    const size_t lb = static_cast<size_t>(B) * H * T * sizeof(float);
+    if (overlaps(LSE, lb, P1, tb) || overlaps(LSE, lb, P2, tb) || overlaps(LSE, lb, I, tb) ||
+        overlaps(LSE, lb, workspace, need))
+      return REL_E_ALIAS;
+  }
+  HeadParams hp;
+  st = pack_heads(hp, tau_s, H, d_h, lambda);
+  if (st != REL_OK) return st;
+  if (LSE && !aligned4(LSE)) return REL_E_ALIGN;
+  if (rel::launch_prestep(a, pp, dt == REL_BF16, stream) != hipSuccess) return REL_E_LAUNCH;
+  return fwd_impl(ws, ws + part, ws + 2 * part, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
 }
 
 size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h) {

@@ -47,6 +47,12 @@ def lib() -> ctypes.CDLL:
         L.relation_bwd_workspace_bytes.restype = sz
         L.relation_bwd.argtypes = [vp, vp, vp, fp, f, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.relation_bwd.restype = i
+        L.relation_prestep.argtypes = [vp, vp, vp, vp, i, f, fp, i, vp, vp, vp, i, i, i, i, i, vp]
+        L.relation_prestep.restype = i
+        L.relation_fwd_model_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.relation_fwd_model_workspace_bytes.restype = sz
+        L.relation_fwd_model.argtypes = [vp, vp, vp, vp, i, f, fp, i, fp, f, vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.relation_fwd_model.restype = i
         L.relation_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.relation_decode_workspace_bytes.restype = sz
         L.relation_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp, sz, vp]
@@ -60,8 +66,12 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_workspace_bytes",
-           "relation_bwd", "relation_decode_workspace_bytes", "relation_decode",
+           "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
+           "relation_fwd_model", "relation_decode_workspace_bytes", "relation_decode",
            "relation_cache_append", "relation_status_str")
+
+ROPE = {"none": 0, "interleaved": 1, "half": 2}
+PAIRS = {"A": 0, "B": 1}
 
 
 def _ptr(t) -> int | None:
@@ -161,6 +171,54 @@ def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None
     del tau_keep
     _check("relation_bwd", st)
     return dP1, dP2, dV, dtau, dlam
+
+
+def _theta_arg(theta, H: int):
+    if theta is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(theta, dtype=np.float32).reshape(-1))
+    if arr.size != H // 2:
+        raise ValueError(f"theta needs H/2 = {H // 2} angles")
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def prestep(P1, P2, I, pos0=None, rope="interleaved", rope_base: float = 1e4, theta=None, pairing="A",
+            out=None, stream=None):
+    """RoPE on P1/P2 and Givens mixing of I ([B,H,T,d_h] device tensors); pos0:
+    device int32[B] or None; theta: H/2 angles or None. out=(P1o, P2o, Io) may
+    be the inputs themselves (in place)."""
+    _require_cuda(P1, P2, I)
+    B, H, T, D = P1.shape
+    if out is None:
+        out = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(I))
+    th_keep, th_p = _theta_arg(theta, H)
+    st = lib().relation_prestep(_ptr(P1), _ptr(P2), _ptr(I), _ptr(pos0), ROPE[rope], float(rope_base), th_p,
+                                PAIRS[pairing], _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), B, H, T, D,
+                                _dtype_code(P1), _stream(stream))
+    del th_keep
+    _check("relation_prestep", st)
+    return out
+
+
+def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", rope_base: float = 1e4,
+              theta=None, pairing="A", out=None, lse=None, workspace=None, stream=None):
+    """The operator on raw projections: pre-steps, then the forward. Returns
+    (Y, LSE or None, workspace holding the pre-stepped tensors)."""
+    _require_cuda(P1, P2, I)
+    B, H, T, D = P1.shape
+    if out is None:
+        out = torch.empty_like(I)
+    need = int(lib().relation_fwd_model_workspace_bytes(B, H, T, D, _dtype_code(P1)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    th_keep, th_p = _theta_arg(theta, H)
+    st = lib().relation_fwd_model(_ptr(P1), _ptr(P2), _ptr(I), _ptr(pos0), ROPE[rope], float(rope_base), th_p,
+                                  PAIRS[pairing], tau_p, float(lam), _ptr(out), _ptr(lse), B, H, T, D,
+                                  _dtype_code(P1), _ptr(workspace), workspace.numel(), _stream(stream))
+    del tau_keep, th_keep
+    _check("relation_fwd_model", st)
+    return out, lse, workspace
 
 
 def decode_workspace_bytes(B: int, H: int, L_cap: int, d_h: int) -> int:

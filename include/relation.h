@@ -1,7 +1,8 @@
 /*
  * relation.h - C ABI of librelation.so: the causal Self-Exchange Relation
- * forward (FlashRelation form), its backward, and its Relation Cache decode
- * step on AMD Instinct MI355X (gfx950).
+ * forward (FlashRelation form), its backward, the model-side pre-steps
+ * (RoPE, Givens head mixing) and the Relation Cache decode step on AMD
+ * Instinct MI355X (gfx950).
  *
  * Operator ("Ask Self, Ask Others: Relation Is All You Need", Eq. (1)-(3)),
  * per batch entry b and head h, for query row i (one-based) of T:
@@ -59,10 +60,24 @@ typedef enum {
   REL_E_ALIGN = 7,     /* a pointer is misaligned (see conventions)          */
   REL_E_ALIAS = 8,     /* an output range overlaps an input or output range  */
   REL_E_WORKSPACE = 9, /* workspace missing or smaller than required         */
-  REL_E_LAUNCH = 10    /* a kernel launch failed                             */
+  REL_E_LAUNCH = 10,   /* a kernel launch failed                             */
+  REL_E_PRESTEP = 11   /* invalid rotary mode / base, pairing or Givens angle */
 } rel_status;
 
 typedef enum { REL_F32 = 0, REL_BF16 = 1 } rel_dtype;
+
+/* Rotary pair convention of the pre-step: pair k turns by pos * base^(-2k/d_h). */
+typedef enum {
+  REL_ROPE_NONE = 0,         /* no rotation                              */
+  REL_ROPE_INTERLEAVED = 1,  /* pair k = (x_{2k}, x_{2k+1})              */
+  REL_ROPE_HALF = 2          /* pair k = (x_k, x_{k + d_h/2})            */
+} rel_rope;
+
+/* Givens head pairings (App. A.2.3; one-based heads, H even). */
+typedef enum {
+  REL_PAIRS_A = 0,           /* (1,2), (3,4), ..., (H-1,H)               */
+  REL_PAIRS_B = 1            /* (2,3), (4,5), ..., (H,1)                 */
+} rel_pairing;
 
 /*
  * relation_fwd - causal multi-head Relation forward without count
@@ -145,6 +160,61 @@ rel_status relation_bwd(const void* P1, const void* P2, const void* V,
                         void* dV, float* dtau, float* dlambda, int B, int H,
                         int T, int d_h, rel_dtype dt, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * relation_prestep - the model-side steps before the operator, in one pass
+ * over HBM:
+ *   - full-head rotary position encoding of P1 and P2 (the paper's models use
+ *     base 10^4, App. B.3): rotary pair k of the row at zero-based position
+ *     pos = pos0[b] + t turns by pos * rope_base^(-2k/d_h),
+ *       (x_a, x_b) -> (x_a cos - x_b sin, x_a sin + x_b cos);
+ *   - Givens mixing of the information heads (Eq. (4), App. A.2.2): for the
+ *     k-th pair (a, b) of `pairing`, with angle theta[k],
+ *       I~(a) = cos I(a) - sin I(b),   I~(b) = sin I(a) + cos I(b),
+ *     applied to all d_h channels of every row.
+ *
+ *   P1, P2, I     : in, device [B, H, T, d_h], dtype dt
+ *   pos0          : in, device int32[B] (position of row 0 per sequence; a
+ *                   decode token uses pos0 = its cache length), or NULL for 0
+ *   rope          : rotary convention; REL_ROPE_NONE copies P1 / P2
+ *   rope_base     : finite, > 1 (ignored for REL_ROPE_NONE)
+ *   theta         : HOST float[H/2], the pairing's angles in pair order (H
+ *                   must be even), or NULL for no mixing (I is copied)
+ *   P1o, P2o, Io  : out, device [B, H, T, d_h]; each may be exactly its own
+ *                   input (in place) and may overlap nothing else
+ * Numerics: fp32 arithmetic; the rotary angle is formed and range-reduced in
+ * fp64 before an fp32 sincos; bf16 outputs are rounded to nearest even.
+ */
+rel_status relation_prestep(const void* P1, const void* P2, const void* I,
+                            const int32_t* pos0, rel_rope rope,
+                            float rope_base, const float* theta,
+                            rel_pairing pairing, void* P1o, void* P2o,
+                            void* Io, int B, int H, int T, int d_h,
+                            rel_dtype dt, hipStream_t stream);
+
+/*
+ * relation_fwd_model_workspace_bytes - device workspace relation_fwd_model
+ * needs (the three pre-stepped tensors). 0 on invalid sizes or dtype.
+ */
+size_t relation_fwd_model_workspace_bytes(int B, int H, int T, int d_h,
+                                          rel_dtype dt);
+
+/*
+ * relation_fwd_model - the operator on raw projections, as the paper's model
+ * computes it: relation_prestep into the workspace, then relation_fwd_lse
+ * (LSE may be NULL) on the rotated P1 / P2 and the mixed information I~.
+ * Arguments as for those two calls; Y and LSE may not overlap the inputs or
+ * the workspace. After the call the workspace holds the pre-stepped tensors
+ * (rotated P1, rotated P2, mixed I, each 256-byte aligned, in that order),
+ * which a backward on the rotated coordinates can reuse.
+ */
+rel_status relation_fwd_model(const void* P1, const void* P2, const void* I,
+                              const int32_t* pos0, rel_rope rope,
+                              float rope_base, const float* theta,
+                              rel_pairing pairing, const float* tau_s,
+                              float lambda, void* Y, float* LSE, int B, int H,
+                              int T, int d_h, rel_dtype dt, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
 
 /*
  * relation_decode_workspace_bytes - bytes of device workspace relation_decode

@@ -12,7 +12,7 @@ from causal_self_exchange_amd import relation as R
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_TAU, E_LAMBDA, E_ALIGN, E_ALIAS, E_WS, E_LAUNCH = range(11)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_TAU, E_LAMBDA, E_ALIGN, E_ALIAS, E_WS, E_LAUNCH, E_PRESTEP = range(12)
 
 # Fake, never-dereferenced device addresses (16-byte aligned, far apart).
 A, B_, C, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = R.lib()
-    for code in range(11):
+    for code in range(12):
         assert lib.relation_status_str(code)
     assert lib.relation_status_str(99) == b"unknown status"
 
@@ -179,3 +179,29 @@ def bwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, dY=DY_, dP1=G1,
 ])
 def test_bwd_rejects_invalid_arguments(kw, code):
     assert bwd(**kw) == code
+
+
+def prestep(P1=A, P2=B_, I=C, pos0=None, rope=1, base=1e4, theta=(0.3,), pairing=0, P1o=G1, P2o=G2, Io=G3,
+            B=1, H=2, T=16, D=64, dt=R.REL_BF16):
+    keep, tp = _tau(theta) if theta is not None else (None, None)
+    return R.lib().relation_prestep(P1, P2, I, pos0, rope, base, tp, pairing, P1o, P2o, Io, B, H, T, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P1=None), E_NULL), (dict(Io=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=48), E_HEADDIM),
+    (dict(dt=5), E_DTYPE), (dict(H=3, theta=(0.1,)), E_SHAPE), (dict(rope=3), E_PRESTEP),
+    (dict(pairing=2), E_PRESTEP), (dict(base=1.0), E_PRESTEP), (dict(base=float("nan")), E_PRESTEP),
+    (dict(theta=(float("inf"),)), E_PRESTEP), (dict(P1o=G1 + 8), E_ALIGN), (dict(pos0=DT + 2), E_ALIGN),
+    (dict(P1o=B_), E_ALIAS), (dict(Io=G1 + 16), E_ALIAS), (dict(P2o=A + 64), E_ALIAS),
+    (dict(pos0=G3 + 32), E_ALIAS),
+])
+def test_prestep_rejects_invalid_arguments(kw, code):
+    assert prestep(**kw) == code
+
+
+def test_fwd_model_workspace_bytes():
+    lib = R.lib()
+    n = 1 * 32 * 8192 * 128
+    assert lib.relation_fwd_model_workspace_bytes(1, 32, 8192, 128, R.REL_BF16) == 3 * n * 2
+    assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 32, R.REL_F32) == 3 * 512
+    assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 48, R.REL_F32) == 0

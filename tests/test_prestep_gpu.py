@@ -1,0 +1,116 @@
+"""GPU parity of the model-side pre-steps (RoPE on P1/P2, Givens mixing of the
+information heads) and of the forward on raw projections, through the C ABI,
+against the fp64 CPU oracle on the same seeded inputs.
+
+Tolerances: a pre-step output is a rotation of two inputs computed in fp32
+(cos / sin of an fp64-reduced angle, one fma): its error is a few fp32 ulps
+of the row's largest input. fp32: per row ||out - ref||_inf <= 2e-6 * ||in||_inf.
+bf16: the fp32 value is rounded to nearest even (8 significant bits, unit
+roundoff 2^-8), so per element |out - ref| <= 2^-8 |ref| + 2e-6 ||in||_inf.
+The model forward meets the forward's own bars (bf16 max abs 2e-2, fp32
+per-row normwise 1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+from causal_self_exchange_amd import relation as R
+from causal_self_exchange_amd import workloads as W
+from oracle import prestep_oracle as PO
+from tests._helpers import assert_parity, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _inputs(B, H, T, D, dt, seed):
+    cfg = W.FwdConfig("p", B, H, T, D, dt, tau=("uniform", 0.5, 2.0))
+    inp = W.make_fwd_inputs(cfg, seed)
+    rng = np.random.default_rng(seed + 77)
+    theta = rng.uniform(-np.pi, np.pi, H // 2).astype(np.float32)
+    pos0 = rng.integers(0, 4000, B).astype(np.int32)
+    return inp, theta, pos0
+
+
+def _check_rows(got, ref, inp_rows_max, dt, what):
+    assert np.all(np.isfinite(got)), what
+    if dt == "f32":
+        err = np.max(np.abs(got - ref), axis=-1) / np.maximum(inp_rows_max, 1e-30)
+        assert float(np.max(err)) <= 2e-6, (what, float(np.max(err)))
+    else:
+        bound = 2.0 ** -8 * np.abs(ref) + 2e-6 * inp_rows_max[..., None]
+        bad = np.abs(got - ref) > bound
+        assert not bad.any(), (what, float(np.max(np.abs(got - ref) - bound)))
+
+
+CASES = [
+    (1, 2, 7, 32, "f32"), (2, 4, 65, 64, "bf16"), (1, 8, 300, 128, "bf16"), (2, 2, 129, 128, "f32"),
+    (3, 6, 33, 64, "f32"), (1, 8, 1, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("pairing", ["A", "B"])
+@pytest.mark.parametrize("mode", ["interleaved", "half", "none"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_prestep_matches_oracle(case, mode, pairing):
+    B, H, T, D, dt = case
+    inp, theta, pos0 = _inputs(B, H, T, D, dt, 3 + T)
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    p0 = torch.from_numpy(pos0).to(DEV)
+    o1, o2, o3 = R.prestep(P1, P2, I, p0, mode, 1e4, theta, pairing)
+    torch.cuda.synchronize()
+    r1, r2, r3 = PO.prestep(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), pos0, 1e4, mode,
+                            theta.astype(np.float64), pairing)
+    for got, ref, src, name in ((o1, r1, inp["P1"], "P1"), (o2, r2, inp["P2"], "P2")):
+        _check_rows(f64(got), ref, np.max(np.abs(f64(src)), axis=-1), dt, f"{case} {mode} {name}")
+    # I rows mix two heads: bound by the larger of the pair's rows (the max over heads).
+    imax = np.max(np.abs(f64(inp["V"])), axis=(1, 3))[:, None, :]
+    _check_rows(f64(o3), r3, np.broadcast_to(imax, r3.shape[:3]), dt, f"{case} {pairing} I")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prestep_in_place_equals_out_of_place(dt):
+    inp, theta, pos0 = _inputs(2, 4, 100, 64, dt, 5)
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    p0 = torch.from_numpy(pos0).to(DEV)
+    want = R.prestep(P1, P2, I, p0, "half", 1e4, theta, "B")
+    a, b, c = P1.clone(), P2.clone(), I.clone()
+    R.prestep(a, b, c, p0, "half", 1e4, theta, "B", out=(a, b, c))
+    torch.cuda.synchronize()
+    for x, y in zip((a, b, c), want):
+        assert torch.equal(x, y)
+
+
+def test_prestep_without_angles_copies_information_and_allows_odd_heads():
+    inp, _, _ = _inputs(1, 3, 50, 32, "bf16", 6)
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    _, _, o3 = R.prestep(P1, P2, I, None, "interleaved", 1e4, None, "A")
+    torch.cuda.synchronize()
+    assert torch.equal(o3, I)
+
+
+@pytest.mark.parametrize("mode,pairing", [("interleaved", "A"), ("half", "B")])
+@pytest.mark.parametrize("case", [(2, 4, 300, 64, "bf16"), (1, 8, 513, 128, "bf16"), (1, 2, 128, 32, "f32")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_model_forward_matches_oracle(case, mode, pairing):
+    B, H, T, D, dt = case
+    inp, theta, pos0 = _inputs(B, H, T, D, dt, 8 + T)
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    p0 = torch.from_numpy(pos0).to(DEV)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    Y, L, ws = R.fwd_model(P1, P2, I, inp["tau"], 0.5, p0, mode, 1e4, theta, pairing, lse=lse)
+    torch.cuda.synchronize()
+    ref = PO.relation_fwd_model(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), inp["tau"].astype(np.float64),
+                                0.5, pos0, 1e4, mode, theta.astype(np.float64), pairing)
+    assert_parity(f64(Y), ref, W.torch_dtype(dt), f"{case} {mode}")
+    # The workspace holds the pre-stepped tensors the forward consumed.
+    n = B * H * T * D
+    es = 2 if dt == "bf16" else 4
+    part = ((n * es + 255) // 256) * 256
+    tdt = W.torch_dtype(dt)
+    pre = [ws[k * part: k * part + n * es].view(tdt).view(B, H, T, D) for k in range(3)]
+    want = R.prestep(P1, P2, I, p0, mode, 1e4, theta, pairing)
+    torch.cuda.synchronize()
+    for x, y in zip(pre, want):
+        assert torch.equal(x, y)
