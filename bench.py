@@ -11,7 +11,8 @@ reports steady-state throughput with warm-up excluded.
 Prints ONE JSON line. Also reported (not the headline): the backward
 (relation_bwd) on the same workload, the model-side pre-steps (RoPE + Givens,
 relation_prestep) and the forward on raw projections (relation_fwd_model) on
-its shape, one Relation Cache decode step (B=64,
+its shape, the Linear Relation forward on its shape, one Relation Cache
+decode step (B=64,
 H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of algorithmic cache
 traffic, and the CPU oracle timed on a bounded sample.
 """
@@ -177,6 +178,38 @@ def bench_prestep(torch, R, W, steps, warmup):
             "fwd_model_TFLOP/s": round(cfg.flops / (mms * 1e-3) / 1e12, 2)}
 
 
+def bench_linear(torch, R, W, steps, warmup):
+    """relation_linear_fwd (chunk-parallel Linear Relation) on the T = 8192
+    workload's shape (B=1, H=32, d_h=128, bf16) with the seeded retention of
+    workloads.make_linear_inputs. Work per chunk of L = 64 tokens and head:
+    the chunk state 2 L d^2, the read from the entering state 2 L d^2, the
+    intra-chunk coefficients and their application 2 L^2 d (half of it
+    masked), the scan 2 d^2: counted as (4 d^2 + 2 L d) FLOP per token."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_linear_inputs(cfg, 42)
+    P1, P2, I = (inp[k].cuda() for k in ("P1", "P2", "V"))
+    A = inp["alpha"].cuda()
+    Y = torch.empty_like(I)
+    ws = torch.empty(R.lib().relation_linear_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h), dtype=torch.uint8,
+                     device="cuda")
+
+    def fn():
+        R.linear_fwd(P1, P2, I, A, inp["tau"], out=Y, workspace=ws)
+
+    _, total, _ = time_launches(fn, steps, warmup, torch)
+    ms = total / steps
+    d, L = cfg.d_h, 64
+    ntok = cfg.B * cfg.H * cfg.T
+    flops = float(ntok) * (4 * d * d + 2 * L * d)
+    io_bytes = float(ntok) * d * (3 * 2 + 4 + 2)          # P1, P2, I bf16 + alpha fp32 in, Y bf16 out
+    state_bytes = float(cfg.B * cfg.H * ((cfg.T + L - 1) // L)) * d * d * 4 * 4   # chunk states: write, scan r/w, read
+    return {"workload": "linear relation: B=1 H=32 T=8192 d_h=128 bf16, seeded retention, 64-token chunks",
+            "us_per_call": round(ms * 1e3, 2), "tokens/s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+            "TFLOP/s_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
+            "GB/s_io_plus_states": round((io_bytes + state_bytes) / (ms * 1e-3) / 1e9, 1),
+            "flops_counted": flops, "io_bytes": io_bytes, "state_bytes": state_bytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +219,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prestep", action="store_true")
+    ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
                          "5 times: the reference kernel for scaling HBM byte counters")
@@ -249,6 +283,8 @@ def main():
         out["backward"] = bench_backward(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_prestep:
         out["prestep"] = bench_prestep(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_linear:
+        out["linear"] = bench_linear(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, R, W, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu_baseline:

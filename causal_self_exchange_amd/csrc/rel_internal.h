@@ -91,6 +91,22 @@ struct PrestepParams {
   float sin_theta[128];
 };
 
+// Linear Relation forward (chunk-parallel recurrence).
+constexpr int kLinChunk = 64;          // tokens per chunk
+struct LinArgs {
+  const void* P1;
+  const void* P2;
+  const void* I;
+  const float* alpha;   // [B][H][T][d_h] channel-wise retention
+  void* Y;
+  float* final;         // optional [B][H][d_h][d_h] final state C_T
+  float* state;         // workspace: [B*H][ceil(T/64)][d_h][d_h] chunk states
+  float* decay;         // workspace: [B*H][ceil(T/64)][d_h] chunk decays
+  int B, H, T, d_h;
+};
+inline int64_t lin_state_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D * D; }
+inline int64_t lin_decay_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D; }
+
 // Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
 // states per (b, h), one per partial work-group.
 constexpr int kDecodeChunk = 256;
@@ -107,6 +123,7 @@ hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStrea
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(int d_h, int T);
 hipError_t launch_prestep(const PrestepArgs& a, const PrestepParams& pp, bool bf16, hipStream_t s);
+hipError_t launch_linear(const LinArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
                                int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s);

@@ -240,6 +240,51 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I, con
   return fwd_impl(ws, ws + part, ws + 2 * part, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
 }
 
+size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h) {
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h)) return 0;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  return align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float)) +
+         align256(static_cast<size_t>(rel::lin_decay_floats(BH, T, d_h)) * sizeof(float));
+}
+
+rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I, const float* alpha,
+                               const float* tau_s, void* Y, float* state_out, int B, int H, int T, int d_h,
+                               rel_dtype dt, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!P1 || !P2 || !I || !alpha || !tau_s || !Y) return REL_E_NULL;
+  int64_t n = 0;
+  if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
+  if (!dtype_ok(dt)) return REL_E_DTYPE;
+  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  HeadParams hp;
+  const rel_status st = pack_heads(hp, tau_s, H, d_h, 0.0f);
+  if (st != REL_OK) return st;
+  const size_t need = relation_linear_workspace_bytes(B, H, T, d_h);
+  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  if (!aligned16(P1) || !aligned16(P2) || !aligned16(I) || !aligned16(Y) || !aligned16(alpha) ||
+      !aligned16(workspace) || !aligned16(state_out))
+    return REL_E_ALIGN;
+  const size_t tb = static_cast<size_t>(n) * elem_size(dt);
+  const size_t ab = static_cast<size_t>(n) * sizeof(float);
+  const size_t sb = static_cast<size_t>(B) * H * d_h * d_h * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{P1, tb}, {P2, tb}, {I, tb}, {alpha, ab}};
+  const Range outs[] = {{Y, tb}, {state_out, state_out ? sb : 0}, {workspace, need}};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (o.n && overlaps(o.p, o.n, i.p, i.n)) return REL_E_ALIAS;
+  for (size_t x = 0; x < 3; ++x)
+    for (size_t y = x + 1; y < 3; ++y)
+      if (outs[x].n && outs[y].n && overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return REL_E_ALIAS;
+
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  char* ws = static_cast<char*>(workspace);
+  float* state = reinterpret_cast<float*>(ws);
+  float* decay = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float)));
+  rel::LinArgs a{P1, P2, I, alpha, Y, state_out, state, decay, B, H, T, d_h};
+  return rel::launch_linear(a, hp, dt == REL_BF16, stream) == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
 size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h) {
   int64_t n = 0;
   if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h)) return 0;

@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.relation_fwd_model_workspace_bytes.restype = sz
         L.relation_fwd_model.argtypes = [vp, vp, vp, vp, i, f, fp, i, fp, f, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.relation_fwd_model.restype = i
+        L.relation_linear_workspace_bytes.argtypes = [i, i, i, i]
+        L.relation_linear_workspace_bytes.restype = sz
+        L.relation_linear_fwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        L.relation_linear_fwd.restype = i
         L.relation_decode_workspace_bytes.argtypes = [i, i, i, i]
         L.relation_decode_workspace_bytes.restype = sz
         L.relation_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp, sz, vp]
@@ -67,7 +71,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_workspace_bytes",
            "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
-           "relation_fwd_model", "relation_decode_workspace_bytes", "relation_decode",
+           "relation_fwd_model", "relation_linear_workspace_bytes", "relation_linear_fwd",
+           "relation_decode_workspace_bytes", "relation_decode",
            "relation_cache_append", "relation_status_str")
 
 ROPE = {"none": 0, "interleaved": 1, "half": 2}
@@ -219,6 +224,27 @@ def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", r
     del tau_keep, th_keep
     _check("relation_fwd_model", st)
     return out, lse, workspace
+
+
+def linear_fwd(P1, P2, I, alpha, tau, out=None, state=None, workspace=None, stream=None):
+    """Linear Relation forward; alpha fp32 [B,H,T,d_h]; state: optional fp32
+    [B,H,d_h,d_h] output for C_T. Returns (Y, state)."""
+    _require_cuda(P1, P2, I, alpha)
+    B, H, T, D = P1.shape
+    if alpha.dtype != torch.float32 or alpha.shape != P1.shape:
+        raise ValueError("alpha must be float32 with the shape of P1")
+    if out is None:
+        out = torch.empty_like(I)
+    need = int(lib().relation_linear_workspace_bytes(B, H, T, D))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_linear_fwd(_ptr(P1), _ptr(P2), _ptr(I), _ptr(alpha), tau_p, _ptr(out), _ptr(state),
+                                   B, H, T, D, _dtype_code(P1), _ptr(workspace), workspace.numel(),
+                                   _stream(stream))
+    del tau_keep
+    _check("relation_linear_fwd", st)
+    return out, state
 
 
 def decode_workspace_bytes(B: int, H: int, L_cap: int, d_h: int) -> int:

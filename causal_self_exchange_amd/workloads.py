@@ -17,6 +17,8 @@ Recipe (all draws float32 from numpy's PCG64 ``default_rng(seed)``):
            to the storage dtype with round-to-nearest-even.
   backward: the forward's draws, then dY ~ N(0, 1) [B, H, T, d_h] from
            ``default_rng(seed + 1000003)``, rounded to the storage dtype.
+  linear : the forward's draws, then the retention alpha (see
+           make_linear_inputs) from ``default_rng(seed + 2000003)``.
   decode : cache lengths L_b ~ U{lo..hi}, then for each sequence b in order
            its cached P2 rows [H, L_b, d_h] and cached V rows; then the new
            token's p1, p2, v [B, H, d_h]. Cache rows past L_b hold NaN.
@@ -109,6 +111,24 @@ def make_bwd_inputs(cfg: FwdConfig, seed: int):
     rng = np.random.default_rng(seed + 1000003)
     dY = rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.d_h), dtype=np.float32)
     inp["dY"] = _store(dY, cfg.dtype)
+    return inp
+
+
+def make_linear_inputs(cfg: FwdConfig, seed: int):
+    """make_fwd_inputs plus a retention alpha [B,H,T,d_h] (fp32) drawn like the
+    paper's parameterisation with random weights: per (h, channel) a rate
+    a ~ U(1, 16) and a bias beta = log(e^dt - 1) with dt log-uniform in
+    [1e-3, 1e-1]; per token z ~ 0.5 N(0, 1); alpha = exp(-a softplus(z + beta)).
+    Drawn from default_rng(seed + 2000003), so the other inputs equal
+    make_fwd_inputs(cfg, seed)."""
+    inp = make_fwd_inputs(cfg, seed)
+    rng = np.random.default_rng(seed + 2000003)
+    a = rng.uniform(1.0, 16.0, (cfg.H, cfg.d_h))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (cfg.H, cfg.d_h)))
+    beta = np.log(np.expm1(dt))
+    z = 0.5 * rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.d_h))
+    alpha = np.exp(-a[None, :, None, :] * np.logaddexp(0.0, z + beta[None, :, None, :]))
+    inp["alpha"] = torch.from_numpy(alpha.astype(np.float32))
     return inp
 
 

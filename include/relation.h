@@ -1,8 +1,8 @@
 /*
  * relation.h - C ABI of librelation.so: the causal Self-Exchange Relation
  * forward (FlashRelation form), its backward, the model-side pre-steps
- * (RoPE, Givens head mixing) and the Relation Cache decode step on AMD
- * Instinct MI355X (gfx950).
+ * (RoPE, Givens head mixing), the Linear Relation forward and the Relation
+ * Cache decode step on AMD Instinct MI355X (gfx950).
  *
  * Operator ("Ask Self, Ask Others: Relation Is All You Need", Eq. (1)-(3)),
  * per batch entry b and head h, for query row i (one-based) of T:
@@ -215,6 +215,40 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I,
                               float lambda, void* Y, float* LSE, int B, int H,
                               int T, int d_h, rel_dtype dt, void* workspace,
                               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * relation_linear_workspace_bytes - device workspace relation_linear_fwd
+ * needs (one d_h x d_h fp32 state and d_h decays per 64-token chunk and
+ * head). 0 on invalid sizes.
+ */
+size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h);
+
+/*
+ * relation_linear_fwd - the Linear Relation forward (Sec. 5.2, Eq. (15)-(17),
+ * App. A.4): per head, with C_0 = 0 (d_h x d_h),
+ *   S_t = sigmoid(p1_t . p2_t / (tau_h sqrt(d_h))),
+ *   q_t = p1_t / |p1_t|,  k_t = p2_t / |p2_t|   (0 for a zero row),
+ *   C-_t = Diag(alpha_t) C_{t-1},  Y_t = I_t + S_t (C-_t)^T q_t,
+ *   C_t = C-_t + S_t k_t I_t^T        (read before write).
+ * Evaluated in 64-token chunks: per-chunk state contributions, a scan over
+ * chunks, then each chunk's outputs from its entering state.
+ *
+ *   P1, P2, I : in, device [B, H, T, d_h], dtype dt (P1 / P2 after RoPE, I the
+ *               mixed information state)
+ *   alpha     : in, device fp32 [B, H, T, d_h], the channel-wise retention in
+ *               (0, 1]; values outside are clamped to [1e-30, 1] (NaN -> 1e-30)
+ *   tau_s     : host float[H]
+ *   Y         : out, device [B, H, T, d_h], dtype dt
+ *   state_out : out, device fp32 [B, H, d_h, d_h] = C_T (rows: relation
+ *               coordinate, columns: information channel), or NULL
+ *   workspace : device scratch of >= relation_linear_workspace_bytes
+ * Numerics: fp32 arithmetic throughout; bf16 Y rounded to nearest even.
+ */
+rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I,
+                               const float* alpha, const float* tau_s,
+                               void* Y, float* state_out, int B, int H, int T,
+                               int d_h, rel_dtype dt, void* workspace,
+                               size_t ws_bytes, hipStream_t stream);
 
 /*
  * relation_decode_workspace_bytes - bytes of device workspace relation_decode

@@ -205,3 +205,28 @@ def test_fwd_model_workspace_bytes():
     assert lib.relation_fwd_model_workspace_bytes(1, 32, 8192, 128, R.REL_BF16) == 3 * n * 2
     assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 32, R.REL_F32) == 3 * 512
     assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 48, R.REL_F32) == 0
+
+
+def linear(P1=A, P2=B_, I=C, alpha=DY_, tau=(1.0, 1.0), Yp=Y, state=None, B=1, H=2, T=100, D=64,
+           dt=R.REL_BF16, ws=WS, ws_bytes=None):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    if ws_bytes is None:
+        ws_bytes = R.lib().relation_linear_workspace_bytes(B, H, T, D) if T > 0 and B > 0 else 0
+    return R.lib().relation_linear_fwd(P1, P2, I, alpha, tp, Yp, state, B, H, T, D, dt, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=None), E_NULL), (dict(Yp=None), E_NULL), (dict(tau=None), E_NULL), (dict(T=0), E_SHAPE),
+    (dict(D=48), E_HEADDIM), (dict(dt=9), E_DTYPE), (dict(tau=(1.0, -1.0)), E_TAU), (dict(ws=None), E_WS),
+    (dict(ws_bytes=100), E_WS), (dict(alpha=DY_ + 4), E_ALIGN), (dict(state=G1 + 8), E_ALIGN),
+    (dict(Yp=A), E_ALIAS), (dict(state=DY_ + 64), E_ALIAS), (dict(ws=C + 16), E_ALIAS), (dict(state=WS), E_ALIAS),
+])
+def test_linear_rejects_invalid_arguments(kw, code):
+    assert linear(**kw) == code
+
+
+def test_linear_workspace_bytes():
+    lib = R.lib()
+    assert lib.relation_linear_workspace_bytes(1, 32, 8192, 128) == 32 * 128 * 128 * 128 * 4 + 32 * 128 * 128 * 4
+    assert lib.relation_linear_workspace_bytes(1, 1, 1, 32) == 32 * 32 * 4 + 256
+    assert lib.relation_linear_workspace_bytes(1, 1, 10, 48) == 0
