@@ -23,25 +23,66 @@ namespace {
 
 constexpr int kL = kLinChunk;          // tokens per chunk
 constexpr int kThreads = 256;
+static_assert(kL == 64, "the output kernel's sub-block pairs assume 4 blocks of 16 rows");
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename Tin>
-__device__ __forceinline__ float ld(const Tin* p, size_t i) { return to_f32(p[i]); }
+__device__ __forceinline__ float ld_val(const Tin* p, size_t i) { return to_f32(p[i]); }
 
-// Row statistics of one chunk: S_t (into s[]), the row norms' reciprocals of
-// p1 and p2 (into n1[], n2[]), for rows t < rows; one wave per row at a time.
-template <typename Tin, int D>
-__device__ __forceinline__ void chunk_rows(const Tin* P1, const Tin* P2, int rows, float inv_scale, float* s,
-                                           float* n1, float* n2) {
+// Copy of a chunk's rows (rows >= `rows` give 0) into an fp32 LDS array,
+// row-major [t][r] (ld = row stride) or channel-major [r][t]. Every thread
+// issues all of its 16-byte loads before it writes any of them, so one
+// memory latency covers the chunk.
+template <typename Tin, int D, bool kChannelMajor>
+__device__ __forceinline__ void stage_rows(const Tin* src, int rows, float* dst, int ld) {
+  constexpr int kVec = 16 / (int)sizeof(Tin);          // elements per 16-byte load
+  constexpr int kN = kL * D / (kVec * kThreads);        // loads per thread
+  static_assert(kN >= 1 && kL * D % (kVec * kThreads) == 0, "whole loads per thread");
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v v[kN];
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int e = (threadIdx.x + i * kThreads) * kVec;
+    v[i] = (e / D) < rows ? *reinterpret_cast<const u32x4v*>(src + e) : u32x4v{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int e = (threadIdx.x + i * kThreads) * kVec;
+    const int t = e / D, r0 = e % D;
+    float x[kVec];
+    if constexpr (sizeof(Tin) == 2) {
+      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+      const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) x[u] = (float)b[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) x[u] = __uint_as_float(v[i][u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u];
+      else dst[t * ld + r0 + u] = x[u];
+    }
+  }
+}
+
+// Row statistics from LDS copies of P1 and P2 (element (t, r) at
+// p[t * rs + r * cs]): S_t into s[], reciprocal row norms into n1[], n2[];
+// one wave per row at a time.
+template <int D>
+__device__ __forceinline__ void row_stats(const float* p1, const float* p2, int rs, int cs, int rows, float inv_scale,
+                                          float* s, float* n1, float* n2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t = wave; t < kL; t += kThreads / 64) {
     float d12 = 0.0f, d11 = 0.0f, d22 = 0.0f;
-    if (t < rows) {
-      for (int r = lane; r < D; r += 64) {
-        const float a = ld(P1, (size_t)t * D + r), b = ld(P2, (size_t)t * D + r);
-        d12 = fmaf(a, b, d12);
-        d11 = fmaf(a, a, d11);
-        d22 = fmaf(b, b, d22);
-      }
+    for (int r = lane; r < D; r += 64) {
+      const float a = p1[t * rs + r * cs], b = p2[t * rs + r * cs];
+      d12 = fmaf(a, b, d12);
+      d11 = fmaf(a, a, d11);
+      d22 = fmaf(b, b, d22);
     }
 #pragma unroll
     for (int w = 32; w >= 1; w >>= 1) {
@@ -58,28 +99,40 @@ __device__ __forceinline__ void chunk_rows(const Tin* P1, const Tin* P2, int row
   }
 }
 
-// Inclusive per-channel prefix of log alpha over the chunk's rows into bt[t][r]
-// (rows past the chunk's end repeat the last value). alpha is clamped to
-// [1e-30, 1] (NaN to 1e-30): log alpha stays finite, so differences of
-// prefixes never form inf - inf, and a retention below 1e-30 already wipes
-// the state within one step to fp32 precision.
-__device__ __forceinline__ void chunk_decay(const float* A, int rows, int D, float* bt) {
+// In-place inclusive per-channel prefix of log alpha over the chunk (element
+// (t, r) at b[t * rs + r * cs], holding alpha on entry; rows >= `rows` repeat
+// the last value). alpha is clamped to [1e-30, 1] (NaN to 1e-30): log alpha
+// stays finite, so differences of prefixes never form inf - inf, and a
+// retention below 1e-30 already wipes the state within one step to fp32
+// precision. A thread reads its whole channel before the first logarithm.
+template <int D>
+__device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows) {
   for (int r = threadIdx.x; r < D; r += kThreads) {
+    float x[kL];
+#pragma unroll
+    for (int t = 0; t < kL; ++t) x[t] = b[t * rs + r * cs];
     float acc = 0.0f;
+#pragma unroll
     for (int t = 0; t < kL; ++t) {
-      if (t < rows) acc += logf(fminf(fmaxf(A[(size_t)t * D + r], 1e-30f), 1.0f));
-      bt[t * D + r] = acc;
+      if (t < rows) acc += logf(fminf(fmaxf(x[t], 1e-30f), 1.0f));
+      x[t] = acc;
     }
+#pragma unroll
+    for (int t = 0; t < kL; ++t) b[t * rs + r * cs] = x[t];
   }
 }
 
 // Phase 1: per (b*H + h, chunk): dC = sum_j S_j (k_j o e^{b_last - b_j}) I_j^T
-// and g = e^{b_last}, into the state slot of the chunk.
+// and g = e^{b_last}, into the state slot of the chunk. dC = Kt^T I is a
+// d_h x d_h x 64 product on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 out): a
+// wave owns column block n and all row blocks (independent accumulators that
+// share the I operand, which comes straight from global memory into
+// registers). LDS holds Kt and the decay prefix only (P1 passes through the
+// prefix buffer first), 64 KB at d_h = 128, so two work-groups fit per CU.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
-  __shared__ float kt[kL][D];     // S_j k_j e^{b_last - b_j}
-  __shared__ float it[kL][D];     // I_j
-  __shared__ float bt[kL * D];
+  __shared__ float kt[kL][D];     // p2_j, then S_j k_j e^{b_last - b_j}
+  __shared__ float bt[kL][D];     // p1_j, then alpha_j, then b_j
   __shared__ float s[kL], n1[kL], n2[kL];
   const int nc = (a.T + kL - 1) / kL;
   const int c = blockIdx.x % nc;
@@ -88,36 +141,59 @@ __global__ __launch_bounds__(kThreads) void lin_chunk_kernel(LinArgs a, HeadPara
   const int t0 = c * kL;
   const int rows = min(kL, a.T - t0);
   const size_t base = ((size_t)bh * a.T + t0) * D;
-  const Tin* P1 = static_cast<const Tin*>(a.P1) + base;
-  const Tin* P2 = static_cast<const Tin*>(a.P2) + base;
   const Tin* I = static_cast<const Tin*>(a.I) + base;
-  const float* A = a.alpha + base;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+  constexpr int kT = D / 32;
+  constexpr int kNPerWave = (kT + 3) / 4;            // column blocks per wave (ceil)
 
-  chunk_rows<Tin, D>(P1, P2, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
-  chunk_decay(A, rows, D, bt);
+  // I operands (B[j][col] = I_j[col], j = 2 ks + lh) of this wave's column
+  // blocks: issued first, consumed last.
+  float bf[kNPerWave][kL / 2];
+#pragma unroll
+  for (int q = 0; q < kNPerWave; ++q) {
+    const int n = wave + 4 * q;
+#pragma unroll
+    for (int ks = 0; ks < kL / 2; ++ks) {
+      const int j = 2 * ks + lh;
+      bf[q][ks] = (n < kT && j < rows) ? ld_val(I, (size_t)j * D + 32 * n + l32) : 0.0f;
+    }
+  }
+  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.P1) + base, rows, &bt[0][0], D);
+  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.P2) + base, rows, &kt[0][0], D);
+  __syncthreads();
+  row_stats<D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
+  __syncthreads();
+  stage_rows<float, D, false>(a.alpha + base, rows, &bt[0][0], D);
+  __syncthreads();
+  decay_prefix<D>(&bt[0][0], D, 1, rows);
   __syncthreads();
   for (int e = threadIdx.x; e < kL * D; e += kThreads) {
     const int t = e / D, r = e % D;
-    const bool v = t < rows;
-    const float blast = bt[(kL - 1) * D + r];
-    kt[t][r] = v ? s[t] * ld(P2, (size_t)t * D + r) * n2[t] * __expf(blast - bt[t * D + r]) : 0.0f;
-    it[t][r] = v ? ld(I, (size_t)t * D + r) : 0.0f;
+    kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
   }
   __syncthreads();
-  // dC[r][col]: each thread a block of rows r and 4 consecutive columns.
   float* dC = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
-  constexpr int kCols = 4;
-  for (int o = threadIdx.x; o < D * D / kCols; o += kThreads) {
-    const int r = o / (D / kCols), c4 = (o % (D / kCols)) * kCols;
-    float acc[kCols] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < kL; ++j) {
-      const float kv = kt[j][r];
 #pragma unroll
-      for (int u = 0; u < kCols; ++u) acc[u] = fmaf(kv, it[j][c4 + u], acc[u]);
+  for (int q = 0; q < kNPerWave; ++q) {
+    const int n = wave + 4 * q;
+    if (n >= kT) break;
+    f32x16 acc[kT];
+#pragma unroll
+    for (int m = 0; m < kT; ++m) acc[m] = f32x16{};
+#pragma unroll 4
+    for (int ks = 0; ks < kL / 2; ++ks) {
+      const int j = 2 * ks + lh;
+#pragma unroll
+      for (int m = 0; m < kT; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[j][32 * m + l32], bf[q][ks], acc[m], 0, 0, 0);
     }
-    *reinterpret_cast<float4*>(dC + (size_t)r * D + c4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+    for (int m = 0; m < kT; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dC[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[m][r];
   }
-  if (threadIdx.x < D) a.decay[((size_t)bh * nc + c) * D + threadIdx.x] = __expf(bt[(kL - 1) * D + threadIdx.x]);
+  if (threadIdx.x < D) a.decay[((size_t)bh * nc + c) * D + threadIdx.x] = __expf(bt[kL - 1][threadIdx.x]);
 }
 
 // Phase 2: per state element (b*H + h, r, col): Cin_0 = 0,
@@ -142,14 +218,25 @@ __global__ __launch_bounds__(kThreads) void lin_scan_kernel(LinArgs a) {
   if (a.final) a.final[(size_t)bh * D * D + e] = C;
 }
 
-// Phase 3: per (b*H + h, chunk): Y = I + inter + intra.
+// Phase 3: per (b*H + h, chunk): Y = I + at I + Qt Cin, with
+//   at[t][j] = S_t S_j sum_r q_{t,r} k_{j,r} e^{b_{t,r} - b_{j,r}}  (j < t),
+//   Qt[t][r] = S_t q_{t,r} e^{b_{t,r}}.
+// at is built per 16-row sub-block pair: off the diagonal (tb > jb) the decay
+// factors through the reference row R = 16 jb + 15 (j <= R < t), as
+// e^{b_t - b_R} e^{b_R - b_j} with both exponents <= 0, and the sum over r runs
+// on v_mfma_f32_16x16x4_f32; the four diagonal blocks take the exact
+// per-element exponentials. The output is one v_mfma_f32_32x32x2_f32
+// accumulation over j (at I) and r (Qt Cin). LDS arrays are stored
+// channel-major ([r][t], rows padded to 65 floats) so that every operand read
+// and transposing write is conflict-free.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kThreads) void lin_out_kernel(LinArgs a, HeadParams hp) {
-  __shared__ float q[kL][D];      // q_t, later q_t o e^{b_t}
-  __shared__ float k[kL][D];      // S_j k_j
-  __shared__ float bt[kL * D];    // b_t (later reused to stage rows of Cin)
+  constexpr int kP = kL + 1;      // padded row length of the channel-major arrays
+  __shared__ float qT[D][kP];     // S_t q_{t,r}
+  __shared__ float kT[D][kP];     // S_j k_{j,r}
+  __shared__ float bT[D][kP];     // b_{t,r}
   __shared__ float it[kL][D];     // I_j
-  __shared__ float at[kL][kL + 1];// intra coefficients S_t S_j (q_t . k_j decayed)
+  __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t]
   __shared__ float s[kL], n1[kL], n2[kL];
   const int nc = (a.T + kL - 1) / kL;
   const int c = blockIdx.x % nc;
@@ -158,94 +245,93 @@ __global__ __launch_bounds__(kThreads) void lin_out_kernel(LinArgs a, HeadParams
   const int t0 = c * kL;
   const int rows = min(kL, a.T - t0);
   const size_t base = ((size_t)bh * a.T + t0) * D;
-  const Tin* P1 = static_cast<const Tin*>(a.P1) + base;
-  const Tin* P2 = static_cast<const Tin*>(a.P2) + base;
-  const Tin* I = static_cast<const Tin*>(a.I) + base;
-  const float* A = a.alpha + base;
   Tin* Y = static_cast<Tin*>(a.Y) + base;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-  chunk_rows<Tin, D>(P1, P2, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
-  chunk_decay(A, rows, D, bt);
+  stage_rows<Tin, D, true>(static_cast<const Tin*>(a.P1) + base, rows, &qT[0][0], kP);
+  stage_rows<Tin, D, true>(static_cast<const Tin*>(a.P2) + base, rows, &kT[0][0], kP);
+  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.I) + base, rows, &it[0][0], D);
+  stage_rows<float, D, true>(a.alpha + base, rows, &bT[0][0], kP);
+  __syncthreads();
+  row_stats<D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
+  decay_prefix<D>(&bT[0][0], 1, kP, rows);
   __syncthreads();
   for (int e = threadIdx.x; e < kL * D; e += kThreads) {
-    const int t = e / D, r = e % D;
-    const bool v = t < rows;
-    q[t][r] = v ? ld(P1, (size_t)t * D + r) * n1[t] : 0.0f;
-    k[t][r] = v ? s[t] * ld(P2, (size_t)t * D + r) * n2[t] : 0.0f;
-    it[t][r] = v ? ld(I, (size_t)t * D + r) : 0.0f;
+    const int r = e / kL, t = e % kL;
+    qT[r][t] *= s[t] * n1[t];
+    kT[r][t] *= s[t] * n2[t];
   }
   __syncthreads();
-  // Intra-chunk coefficients for j < t (0 elsewhere).
-  for (int e = threadIdx.x; e < kL * kL; e += kThreads) {
-    const int t = e / kL, j = e % kL;
+
+  // Off-diagonal sub-block pairs (tb, jb), tb > jb: 6 pairs.
+  {
+    constexpr int kPairT[6] = {1, 2, 3, 2, 3, 3};
+    constexpr int kPairJ[6] = {0, 0, 0, 1, 1, 2};
+    const int l16 = lane & 15, lq = lane >> 4;
+    for (int p = wave; p < 6; p += kThreads / 64) {
+      const int tb = kPairT[p], jb = kPairJ[p];
+      const int t = 16 * tb + l16, j = 16 * jb + l16, R = 16 * jb + 15;
+      f32x4 acc = {};
+#pragma unroll 4
+      for (int ks = 0; ks < D / 4; ++ks) {
+        const int r = 4 * ks + lq;
+        const float ref = bT[r][R];
+        const float av = qT[r][t] * __expf(bT[r][t] - ref);
+        const float bv = kT[r][j] * __expf(ref - bT[r][j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+      }
+      // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atT[16 * jb + l16][16 * tb + 4 * lq + i] = acc[i];
+    }
+  }
+  // Diagonal blocks (exact) and the zero blocks above the diagonal.
+  for (int e = threadIdx.x; e < 4 * 256; e += kThreads) {
+    const int blk = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
+    const int t = 16 * blk + tl, j = 16 * blk + jl;
     float acc = 0.0f;
-    if (j < t && t < rows) {
-      for (int r = 0; r < D; ++r) acc = fmaf(q[t][r] * k[j][r], __expf(bt[t * D + r] - bt[j * D + r]), acc);
-      acc *= s[t];
+    if (jl < tl) {
+      for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
     }
-    at[t][j] = acc;
+    atT[j][t] = acc;
+  }
+  for (int e = threadIdx.x; e < 6 * 256; e += kThreads) {
+    constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
+    constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
+    const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
+    atT[16 * kUpJ[p] + jl][16 * kUpT[p] + tl] = 0.0f;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < kL * D; e += kThreads) {
-    const int t = e / D, r = e % D;
-    q[t][r] *= __expf(bt[t * D + r]);
-  }
-  // Outputs: thread handles 4 consecutive columns of 2 rows per pass.
-  constexpr int kCols = 4;
-  constexpr int kRowsPer = 2;
+
+  // Y tiles (m, n): rows 32 m .., columns 32 n ..; a wave takes column block
+  // n for both row blocks, with its column of Cin preloaded into registers.
+  const int l32 = lane & 31, lh = lane >> 5;
+  constexpr int kTN = D / 32;
   const float* cin = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
-  float* stage = bt;              // rows r0 .. r0 + kStage - 1 of Cin
-  constexpr int kStage = D < kL ? D : kL;   // rows of Cin staged at a time (D % kStage == 0)
-  static_assert(kStage * D <= kL * D && D % kStage == 0, "staging fits");
-  for (int base_o = 0; base_o < kL * D / (kCols * kRowsPer); base_o += kThreads) {
-    const int o = base_o + threadIdx.x;
-    const bool act = o < kL * D / (kCols * kRowsPer);
-    const int tp = act ? o / (D / kCols) : 0;            // row pair
-    const int c4 = act ? (o % (D / kCols)) * kCols : 0;
-    float acc[kRowsPer][kCols];
+  for (int n = wave; n < kTN; n += kThreads / 64) {
+    const int col = 32 * n + l32;
+    float cf[D / 2];
 #pragma unroll
-    for (int x = 0; x < kRowsPer; ++x)
+    for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + col];
 #pragma unroll
-      for (int u = 0; u < kCols; ++u) acc[x][u] = 0.0f;
-    // Intra: sum_j at[t][j] I_j.
-    for (int j = 0; j < kL; ++j) {
-#pragma unroll
-      for (int x = 0; x < kRowsPer; ++x) {
-        const float w = at[kRowsPer * tp + x][j];
-#pragma unroll
-        for (int u = 0; u < kCols; ++u) acc[x][u] = fmaf(w, it[j][c4 + u], acc[x][u]);
+    for (int m = 0; m < 2; ++m) {
+      const int t = 32 * m + l32;
+      f32x16 acc = {};
+#pragma unroll 8
+      for (int ks = 0; ks < kL / 2; ++ks) {
+        const int j = 2 * ks + lh;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(atT[j][t], it[j][col], acc, 0, 0, 0);
       }
-    }
-    // Inter: S_t sum_r (q_t o e^{b_t})_r Cin[r][col], Cin staged kL rows at a time.
-    float inter[kRowsPer][kCols];
 #pragma unroll
-    for (int x = 0; x < kRowsPer; ++x)
-#pragma unroll
-      for (int u = 0; u < kCols; ++u) inter[x][u] = 0.0f;
-    for (int r0 = 0; r0 < D; r0 += kStage) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < kStage * D; e += kThreads) stage[e] = cin[(size_t)r0 * D + e];
-      __syncthreads();
-      if (act) {
-        for (int rr = 0; rr < kStage; ++rr) {
-#pragma unroll
-          for (int x = 0; x < kRowsPer; ++x) {
-            const float w = q[kRowsPer * tp + x][r0 + rr];
-#pragma unroll
-            for (int u = 0; u < kCols; ++u) inter[x][u] = fmaf(w, stage[rr * D + c4 + u], inter[x][u]);
-          }
-        }
+      for (int ks = 0; ks < D / 2; ++ks) {
+        const int r = 2 * ks + lh;
+        const float qv = qT[r][t] * __expf(bT[r][t]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, cf[ks], acc, 0, 0, 0);
       }
-    }
-    if (act) {
 #pragma unroll
-      for (int x = 0; x < kRowsPer; ++x) {
-        const int t = kRowsPer * tp + x;
-        if (t < rows) {
-#pragma unroll
-          for (int u = 0; u < kCols; ++u)
-            Y[(size_t)t * D + c4 + u] = from_f32<Tin>(it[t][c4 + u] + fmaf(s[t], inter[x][u], acc[x][u]));
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int tr = 32 * m + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
       }
     }
   }
