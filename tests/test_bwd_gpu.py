@@ -6,7 +6,7 @@ Tolerances (the pages fix none for gradients; these follow the forward's bar):
   tensors, per row i of each gradient g:
       ||g_i - g*_i||_inf <= tol * max(1, ||g*_i||_inf)
     tol = 2e-2 for bf16 (the forward's absolute bar, relative once a row's
-    gradient exceeds 1 -- the bf16 output rounding alone is 2^-9 relative),
+    gradient exceeds 1 -- the bf16 output rounding alone is up to 2^-8 relative),
     tol = 1e-5 for fp32.
   scalars: each row's share of dtau / dlambda is formed from F_ii, dY_i . V_i
     and D_i = dY_i . Y_i, so the bar is tol times the sum over rows of
