@@ -179,8 +179,13 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[D / 32], float alpha) {
   }
 }
 
-template <int D>
+// D: head size of the LDS tile layout and the MFMA schedule (64 or 128); DR:
+// the rows' real head size in memory (48 runs on the 64 layout and 80 on the
+// 128 layout, the chunks past DR held at zero, so evidence and transport are
+// exact and the padded output rows are not stored).
+template <int D, int DR = D>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadParams hp) {
+  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   char* const kbase = smem;                          // P2 ring: tile t in slot t % 3
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // One query tile (256 rows) of one head, start to finish.
   auto run_tile = [&](int qt, int bh) __attribute__((always_inline)) {
   const int h = bh % a.H;
-  const size_t head = (size_t)bh * (size_t)T * D;
-  const long long head_bytes = (long long)T * D * 2;
+  const size_t head = (size_t)bh * (size_t)T * DR;
+  const long long head_bytes = (long long)T * DR * 2;
   const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
   const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
   const __bf16* V = static_cast<const __bf16*>(a.V) + head;
@@ -213,13 +218,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 
   // P1 rows as the evidence MFMA's B operand: lane holds p1[qrow][16 ds + 8 hf + 0..7];
   // the same chunks of p2[qrow] give the Self evidence p1_i . p2_i.
-  const int qoff = qrow * (D * 2) + hf * 16;
+  const int qoff = qrow * (DR * 2) + hf * 16;
   // (The dot product waits until the prologue's tile loads are issued too.)
   bf16x8 qf[C::kDs], kv[C::kDs];
 #pragma unroll
   for (int ds = 0; ds < C::kDs; ++ds) {
-    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
-    kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
+    // k-steps past DR / 16 cover padded columns: out-of-range offsets read 0.
+    const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;
+    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, o, 0, 0));
+    kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
   }
   const float inv_tau = hp.inv_tau[h];
 
@@ -241,11 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 #pragma unroll
   for (int u = 0; u < C::kDmaPerWave; ++u) {
     const int k = wave + kWaves * u;
-    dma_koff[u] = C::row_src(k, lane);
-    dma_voff[u] = C::tr_src(k, lane);
+    dma_koff[u] = C::template row_src_real<DR>(k, lane);
+    dma_voff[u] = C::template tr_src_real<DR>(k, lane);
   }
   auto dma_k = [&](int t) {
-    const auto rs = rsrc_words(P2 + (size_t)t * kBN * D, t < ntiles ? hb - t * kBN * D * 2 : 0);
+    const auto rs = rsrc_words(P2 + (size_t)t * kBN * DR, t < ntiles ? hb - t * kBN * DR * 2 : 0);
     char* slot = kbase + (t % kKSlots) * C::kKBytes;
 #pragma unroll
     for (int u = 0; u < C::kDmaPerWave; ++u) dma16(rs, slot + (wave + kWaves * u) * C::kKBlock, dma_koff[u]);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // V tiles past nvt go to the sink block, so the ring keeps the last real ones.
   char* const vsink = vbase + kVSlots * C::kVBytes;
   auto dma_v = [&](int t) {
-    const auto rs = rsrc_words(V + (size_t)t * kBN * D, t < nvt ? hb - t * kBN * D * 2 : 0);
+    const auto rs = rsrc_words(V + (size_t)t * kBN * DR, t < nvt ? hb - t * kBN * DR * 2 : 0);
     char* slot = vbase + (t & (kVSlots - 1)) * C::kVBytes;
 #pragma unroll
     for (int u = 0; u < C::kDmaPerWave; ++u)
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const float S = sigmoid_f32(dself * hp.scale * inv_tau);
   const RowCombine c(S, m2 * kLn2, lsum, hp.lambda * logf((float)(qrow + 1)));
   if (a.lse != nullptr && hf == 0 && qrow < T) a.lse[(size_t)bh * T + qrow] = c.lse;
-  const int roff = qrow * (D * 2) + hf * 8;
+  const int roff = qrow * (DR * 2) + hf * 8;
   // V_i of this lane's row from the V ring (tile qrow / 64 is among the last
   // four loaded): columns 32 db + 8 g4 + 4 hf .. +3, i.e. half hf of chunk
   // 4 db + g4 of row qrow % 64 in the block layout.
@@ -557,6 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
+      if (32 * db + 8 * g4 >= DR) continue;      // padded columns
       bf16x4 yy;
 #pragma unroll
       for (int e = 0; e < 4; ++e) yy[e] = (__bf16)(c.w_self * (float)vv[db][g4][e] + c.w_hist * o[db][4 * g4 + e]);
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   }
 }
 
-template <int D>
+template <int D, int DR = D>
 hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kBM - 1) / kBM;
   const long long nwork = (long long)((nq + 1) / 2) * a.B * a.H;
@@ -600,7 +608,7 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
     cus[dev].store(n_cu, std::memory_order_relaxed);
   }
   const long long grid = nwork < n_cu ? nwork : n_cu;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, DR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 
@@ -609,12 +617,14 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
 bool fwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including
   // the rows past T of the last query tile.
-  return (d_h == 64 || d_h == 128) && ((long long)T + kBM) * d_h * 2 < 0x7fffffffLL;
+  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kBM) * d_h * 2 < 0x7fffffffLL;
 }
 
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   switch (a.d_h) {
+    case 48: return launch_typed<64, 48>(a, hp, s);
     case 64: return launch_typed<64>(a, hp, s);
+    case 80: return launch_typed<128, 80>(a, hp, s);
     case 128: return launch_typed<128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }

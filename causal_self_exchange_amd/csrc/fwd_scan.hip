@@ -102,7 +102,9 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
 hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s) {
   switch (a.d_h) {
     case 32: return bf16 ? launch_typed<__bf16, 32>(a, hp, s) : launch_typed<float, 32>(a, hp, s);
+    case 48: return bf16 ? launch_typed<__bf16, 48>(a, hp, s) : launch_typed<float, 48>(a, hp, s);
     case 64: return bf16 ? launch_typed<__bf16, 64>(a, hp, s) : launch_typed<float, 64>(a, hp, s);
+    case 80: return bf16 ? launch_typed<__bf16, 80>(a, hp, s) : launch_typed<float, 80>(a, hp, s);
     case 128: return bf16 ? launch_typed<__bf16, 128>(a, hp, s) : launch_typed<float, 128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }

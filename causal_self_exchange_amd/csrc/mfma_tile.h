@@ -31,6 +31,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileRows = 64;               // rows per LDS tile
 constexpr int kBufFlags = 0x00020000;       // raw buffer descriptor word 3 (gfx9)
+constexpr int kOutOfRange = 0x7ffffff0;     // buffer offset past every head's range (reads 0)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -70,6 +71,22 @@ struct TileLayout {
   __device__ static int tr_src(int k, int lane) {
     const int rr = lane >> 3;
     return (8 * (k % 8) + rr) * (D * 2) + 16 * (8 * (k / 8) + ((lane & 7) ^ (4 * ((rr >> 1) & 1))));
+  }
+  // The same for rows of DR <= D elements in memory (DR a multiple of 16):
+  // chunks past the row's end get an offset past any buffer's range, so the
+  // direct load writes zeros there.
+  template <int DR>
+  __device__ static int row_src_real(int k, int lane) {
+    if constexpr (DR == D) return row_src(k, lane);
+    const int cc = 8 * (k / 8) + (lane >> 3);
+    return cc < DR / 8 ? (8 * (k % 8) + (lane & 7)) * (DR * 2) + 16 * cc : kOutOfRange;
+  }
+  template <int DR>
+  __device__ static int tr_src_real(int k, int lane) {
+    if constexpr (DR == D) return tr_src(k, lane);
+    const int rr = lane >> 3;
+    const int cc = 8 * (k / 8) + ((lane & 7) ^ (4 * ((rr >> 1) & 1)));
+    return cc < DR / 8 ? (8 * (k % 8) + rr) * (DR * 2) + 16 * cc : kOutOfRange;
   }
   // Lane read base of the row layout: operand rows (lane % 32, chunk lane / 32).
   __device__ static int row_base(int lane) {

@@ -188,7 +188,9 @@ hipError_t launch_typed(const PrestepArgs& a, const PrestepParams& pp, hipStream
 hipError_t launch_prestep(const PrestepArgs& a, const PrestepParams& pp, bool bf16, hipStream_t s) {
   switch (a.d_h) {
     case 32: return bf16 ? launch_typed<__bf16, 32>(a, pp, s) : launch_typed<float, 32>(a, pp, s);
+    case 48: return bf16 ? launch_typed<__bf16, 48>(a, pp, s) : launch_typed<float, 48>(a, pp, s);
     case 64: return bf16 ? launch_typed<__bf16, 64>(a, pp, s) : launch_typed<float, 64>(a, pp, s);
+    case 80: return bf16 ? launch_typed<__bf16, 80>(a, pp, s) : launch_typed<float, 80>(a, pp, s);
     case 128: return bf16 ? launch_typed<__bf16, 128>(a, pp, s) : launch_typed<float, 128>(a, pp, s);
     default: return hipErrorInvalidValue;
   }

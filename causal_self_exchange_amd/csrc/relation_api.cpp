@@ -27,6 +27,9 @@ size_t elem_size(rel_dtype dt) { return dt == REL_BF16 ? 2 : 4; }
 bool dtype_ok(rel_dtype dt) { return dt == REL_F32 || dt == REL_BF16; }
 
 bool head_dim_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128; }
+// The forward, its training variant and the pre-steps also take the paper's
+// non-power-of-two head sizes.
+bool fwd_head_dim_ok(int d_h) { return head_dim_ok(d_h) || d_h == 48 || d_h == 80; }
 
 // Product of positive ints; false if any is < 1 or the product exceeds 2^40
 // elements (4 TiB of fp32, far beyond one GPU's memory).
@@ -70,7 +73,7 @@ rel_status fwd_impl(const void* P1, const void* P2, const void* V, const float* 
   int64_t n = 0;
   if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
-  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!fwd_head_dim_ok(d_h)) return REL_E_HEADDIM;
   HeadParams hp;
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
@@ -112,7 +115,7 @@ rel_status prestep_setup(rel::PrestepArgs& a, rel::PrestepParams& pp, const void
   if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
   if (theta && (H % 2 != 0)) return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
-  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!fwd_head_dim_ok(d_h)) return REL_E_HEADDIM;
   if (rope != REL_ROPE_NONE && rope != REL_ROPE_INTERLEAVED && rope != REL_ROPE_HALF) return REL_E_PRESTEP;
   if (pairing != REL_PAIRS_A && pairing != REL_PAIRS_B) return REL_E_PRESTEP;
   if (rope != REL_ROPE_NONE && !(std::isfinite(rope_base) && rope_base > 1.0f)) return REL_E_PRESTEP;
@@ -196,7 +199,7 @@ rel_status relation_prestep(const void* P1, const void* P2, const void* I, const
 
 size_t relation_fwd_model_workspace_bytes(int B, int H, int T, int d_h, rel_dtype dt) {
   int64_t n = 0;
-  if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h) || !dtype_ok(dt)) return 0;
+  if (!count(n, {B, H, T, d_h}) || !fwd_head_dim_ok(d_h) || !dtype_ok(dt)) return 0;
   return 3 * align256(static_cast<size_t>(n) * elem_size(dt));
 }
 

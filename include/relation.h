@@ -34,7 +34,10 @@
  *   - Tensor pointers must be 16-byte aligned, float arrays (LSE, dtau,
  *     dlambda) 4-byte aligned; an output range may not overlap any input
  *     range or another output range.
- *   - Supported: d_h in {32, 64, 128}; 1 <= H <= REL_MAX_HEADS; B <= 65535.
+ *   - Supported: d_h in {32, 64, 128} for every entry point, and also 48 and
+ *     80 (the paper's model geometries) for relation_fwd, relation_fwd_ex,
+ *     relation_fwd_lse, relation_prestep and relation_fwd_model;
+ *     1 <= H <= REL_MAX_HEADS; B <= 65535.
  */
 #ifndef RELATION_H
 #define RELATION_H

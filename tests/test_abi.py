@@ -53,7 +53,7 @@ def fwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, B=1, H=2, T=16, D=64, d
     (dict(T=0), E_SHAPE), (dict(B=0), E_SHAPE), (dict(H=0, tau=(1.0,)), E_SHAPE), (dict(D=-64), E_SHAPE),
     (dict(B=70000), E_SHAPE), (dict(H=257, tau=[1.0] * 257), E_SHAPE),
     (dict(T=2**31 - 1, B=65535, H=256, tau=[1.0] * 256, D=128), E_SHAPE),
-    (dict(dt=7), E_DTYPE), (dict(D=48), E_HEADDIM), (dict(D=256), E_HEADDIM),
+    (dict(dt=7), E_DTYPE), (dict(D=96), E_HEADDIM), (dict(D=256), E_HEADDIM), (dict(D=40), E_HEADDIM),
     (dict(tau=(1.0, 0.0)), E_TAU), (dict(tau=(-1.0, 1.0)), E_TAU),
     (dict(tau=(1.0, float("nan"))), E_TAU), (dict(tau=(float("inf"), 1.0)), E_TAU),
     (dict(lam=float("nan")), E_LAMBDA), (dict(lam=float("inf")), E_LAMBDA),
@@ -133,7 +133,7 @@ def fwd_lse(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, B=1, H=2, T
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(L=None), E_NULL), (dict(P1=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=48), E_HEADDIM),
+    (dict(L=None), E_NULL), (dict(P1=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=96), E_HEADDIM),
     (dict(tau=(1.0, 0.0)), E_TAU), (dict(L=LSE_ + 2), E_ALIGN), (dict(L=A + 64), E_ALIAS),
     (dict(L=Y + 4), E_ALIAS), (dict(L=Y - 4), E_ALIAS),
 ])
@@ -188,7 +188,7 @@ def prestep(P1=A, P2=B_, I=C, pos0=None, rope=1, base=1e4, theta=(0.3,), pairing
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(P1=None), E_NULL), (dict(Io=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=48), E_HEADDIM),
+    (dict(P1=None), E_NULL), (dict(Io=None), E_NULL), (dict(T=0), E_SHAPE), (dict(D=96), E_HEADDIM),
     (dict(dt=5), E_DTYPE), (dict(H=3, theta=(0.1,)), E_SHAPE), (dict(rope=3), E_PRESTEP),
     (dict(pairing=2), E_PRESTEP), (dict(base=1.0), E_PRESTEP), (dict(base=float("nan")), E_PRESTEP),
     (dict(theta=(float("inf"),)), E_PRESTEP), (dict(P1o=G1 + 8), E_ALIGN), (dict(pos0=DT + 2), E_ALIGN),
@@ -204,7 +204,10 @@ def test_fwd_model_workspace_bytes():
     n = 1 * 32 * 8192 * 128
     assert lib.relation_fwd_model_workspace_bytes(1, 32, 8192, 128, R.REL_BF16) == 3 * n * 2
     assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 32, R.REL_F32) == 3 * 512
-    assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 48, R.REL_F32) == 0
+    assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 96, R.REL_F32) == 0
+    # the paper's head sizes 48 and 80 are accepted by the forward family
+    assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 48, R.REL_F32) == 3 * 768
+    assert lib.relation_fwd_model_workspace_bytes(2, 8, 1024, 80, R.REL_BF16) == 3 * 2 * 8 * 1024 * 80 * 2
 
 
 def linear(P1=A, P2=B_, I=C, alpha=DY_, tau=(1.0, 1.0), Yp=Y, state=None, B=1, H=2, T=100, D=64,

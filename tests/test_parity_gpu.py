@@ -310,3 +310,46 @@ def test_autoregressive_decode_matches_forward(dt):
     R.cache_append(cP2, cV, lens, p2, v)          # full cache: unchanged
     torch.cuda.synchronize()
     assert lens.cpu().tolist() == [T] * B
+
+
+# ------------------------------------------ the paper's head sizes 48, 80 ----
+
+PAPER_SHAPES = [
+    (2, 8, 300, 48, "bf16"), (1, 8, 513, 80, "bf16"), (1, 2, 129, 48, "f32"), (1, 2, 100, 80, "f32"),
+    (1, 1, 1, 48, "bf16"), (1, 3, 257, 80, "bf16"),
+]
+
+
+@pytest.mark.parametrize("kernel", [None, "scan"])
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+@pytest.mark.parametrize("shape", PAPER_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_paper_head_sizes(shape, lam, kernel):
+    """d_h = 48 and 80 ([paper] Table 6 geometries): bf16 runs the MFMA kernel
+    on the 64 / 128 tile layouts with zero-filled padding chunks; the
+    row-scan kernel is checked too. LSE from the training forward as well."""
+    B, H, T, D, dt = shape
+    cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0), lam=lam)
+    inp = W.make_fwd_inputs(cfg, 31 + T)
+    P1, P2, V = _dev(inp)
+    with _kernel_env(kernel):
+        Y, L = R.fwd_lse(P1, P2, V, inp["tau"], lam)
+    torch.cuda.synchronize()
+    assert_parity(f64(Y), _oracle_full(inp, lam), W.torch_dtype(dt), f"{shape} {kernel}")
+    want = np.stack([np.stack([O.row_lse(f64(inp["P1"])[b, h], f64(inp["P2"])[b, h], float(inp["tau"][h]), lam)
+                               for h in range(H)]) for b in range(B)])
+    assert float(np.max(np.abs(f64(L) - want))) <= 1e-4
+
+
+def test_paper_head_size_guard_columns_untouched():
+    """Padded columns are never stored: a Y buffer with guard rows after the
+    last head keeps its sentinel values."""
+    cfg = W.FwdConfig("t", 1, 2, 200, 80, "bf16")
+    inp = W.make_fwd_inputs(cfg, 2)
+    P1, P2, V = _dev(inp)
+    n = P1.numel()
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    Y = buf[:n].view(P1.shape)
+    R.fwd(P1, P2, V, inp["tau"], 0.0, out=Y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[n:] == 7.0)
+    assert_parity(f64(Y), _oracle_full(inp), torch.bfloat16, "guard")
