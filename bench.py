@@ -11,7 +11,8 @@ reports steady-state throughput with warm-up excluded.
 Prints ONE JSON line. Also reported (not the headline): the backward
 (relation_bwd) on the same workload, the model-side pre-steps (RoPE + Givens,
 relation_prestep) and the forward on raw projections (relation_fwd_model) on
-its shape, the Linear Relation forward on its shape, one Relation Cache
+its shape, the Linear Relation forward on its shape, the paper-geometry
+comparison with PyTorch FlashAttention on this GPU, one Relation Cache
 decode step (B=64,
 H=32, d_h=128, cache lengths U{1024..4096}) in GB/s of algorithmic cache
 traffic, and the CPU oracle timed on a bounded sample.
@@ -210,6 +211,89 @@ def bench_linear(torch, R, W, steps, warmup):
             "flops_counted": flops, "io_bytes": io_bytes, "state_bytes": state_bytes}
 
 
+PAPER_GEOMETRY = (   # ([paper] Table 6 / Table 4(b)): d_h, T; H = 8, 131,072 tokens per step
+    ("10M", 48, 1024), ("30M", 64, 2048), ("100M", 80, 4096))
+
+
+def _flash_sdpa(torch):
+    """A context forcing PyTorch's flash (else memory-efficient) SDPA kernel;
+    never the math path (it issues batched bf16 products). None if neither
+    backend is available."""
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+    except ImportError:
+        return None, None
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            q = torch.randn(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+            with sdpa_kernel([be]):
+                torch.nn.functional.scaled_dot_product_attention(q, q, q, is_causal=True)
+            torch.cuda.synchronize()
+            return name, be
+        except RuntimeError:
+            continue
+    return None, None
+
+
+def bench_paper_geometry(torch, R, W, steps, warmup):
+    """The operator-level counterpart of the paper's Table 4(b): FlashRelation
+    (relation_fwd_ex, lambda = 0.5 as in the paper's models) against PyTorch
+    FlashAttention (scaled_dot_product_attention, causal, flash backend
+    forced) on the same MI355X, H = 8 and 131,072 tokens per step at the three
+    model geometries (d_h, T) = (48, 1024), (64, 2048), (80, 4096). Forward
+    for all three; forward + backward where relation_bwd has MFMA kernels
+    (d_h = 64). Tokens/s and the FR / FA ratio."""
+    from torch.nn.attention import sdpa_kernel
+    be_name, be = _flash_sdpa(torch)
+    out = {"attention_backend": be_name, "rows": []}
+    for scale, d, T in PAPER_GEOMETRY:
+        B, H = 131072 // T, 8
+        cfg = W.FwdConfig("paper", B, H, T, d, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+        inp = W.make_bwd_inputs(cfg, 42)
+        P1, P2, V, dY = (inp[k].cuda() for k in ("P1", "P2", "V", "dY"))
+        Y = torch.empty_like(V)
+        _, fr_ms, _ = time_launches(lambda: R.fwd(P1, P2, V, inp["tau"], 0.5, out=Y), steps, warmup, torch)
+        fr_ms /= steps
+        row = {"scale": scale, "B": B, "H": H, "T": T, "d_h": d, "tokens": B * T,
+               "FR_fwd_ms": round(fr_ms, 4), "FR_fwd_tok/s": round(B * T / (fr_ms * 1e-3), 0)}
+        if be is not None:
+            with sdpa_kernel([be]):
+                _, fa_ms, _ = time_launches(
+                    lambda: torch.nn.functional.scaled_dot_product_attention(P1, P2, V, is_causal=True),
+                    steps, warmup, torch)
+            fa_ms /= steps
+            row.update({"FA_fwd_ms": round(fa_ms, 4), "FA_fwd_tok/s": round(B * T / (fa_ms * 1e-3), 0),
+                        "FR_over_FA_fwd": round(fa_ms / fr_ms, 3)})
+        if d == 64:
+            Yl, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
+            grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
+                     torch.empty(H, device="cuda"), torch.empty(1, device="cuda"))
+            ws = torch.empty(R.bwd_workspace_bytes(B, H, T, d), dtype=torch.uint8, device="cuda")
+
+            def fr_train():
+                R.fwd_lse(P1, P2, V, inp["tau"], 0.5, out=Yl, lse=L)
+                R.bwd(P1, P2, V, inp["tau"], 0.5, Yl, L, dY, grads=grads, workspace=ws)
+
+            _, frt, _ = time_launches(fr_train, steps, warmup, torch)
+            frt /= steps
+            row.update({"FR_fwd_bwd_ms": round(frt, 4), "FR_fwd_bwd_tok/s": round(B * T / (frt * 1e-3), 0)})
+            if be is not None:
+                q, k, v = (x.detach().clone().requires_grad_(True) for x in (P1, P2, V))
+
+                def fa_train():
+                    with sdpa_kernel([be]):
+                        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                    o.backward(dY)
+
+                _, fat, _ = time_launches(fa_train, steps, warmup, torch)
+                fat /= steps
+                row.update({"FA_fwd_bwd_ms": round(fat, 4), "FA_fwd_bwd_tok/s": round(B * T / (fat * 1e-3), 0),
+                            "FR_over_FA_fwd_bwd": round(fat / frt, 3)})
+        out["rows"].append(row)
+        del P1, P2, V, dY, Y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +304,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prestep", action="store_true")
     ap.add_argument("--no-linear", action="store_true")
+    ap.add_argument("--no-paper", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
                          "5 times: the reference kernel for scaling HBM byte counters")
@@ -285,6 +370,8 @@ def main():
         out["prestep"] = bench_prestep(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
     if not args.no_linear:
         out["linear"] = bench_linear(torch, R, W, max(10, args.steps // 4), max(10, args.warmup // 4))
+    if not args.no_paper:
+        out["paper_geometry"] = bench_paper_geometry(torch, R, W, max(10, args.steps // 10), max(5, args.warmup // 10))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, R, W, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu_baseline:
