@@ -2,9 +2,10 @@
 
 kernel_stats(csv): per-kernel call count and average / min / max duration from
 a `rocprofv3 --kernel-trace --stats --output-format csv` kernel_stats file.
-trace_avg(csv, kernel_substr, last_n): mean duration (us) of the last `last_n`
-dispatches of one kernel from a `--kernel-trace` kernel_trace file (the timed
-launches of a run that first warms up).
+trace_avg(csv, kernel_substr, last_n, within_first): mean duration (us) of the
+last `last_n` dispatches of one kernel from a `--kernel-trace` kernel_trace
+file (the timed launches of a run that first warms up), optionally within its
+first `within_first` dispatches.
 counter_avg(csv, kernel_substr, counter): a counter's mean over dispatches of
 one kernel from a `--pmc` counter_collection file.
 traffic(...): HBM bytes per launch of a kernel from FETCH_SIZE / WRITE_SIZE
@@ -28,13 +29,19 @@ def kernel_stats(path: str) -> list[dict]:
     return out
 
 
-def trace_avg(path: str, kernel_substr: str, last_n: int) -> dict:
+def trace_avg(path: str, kernel_substr: str, last_n: int, within_first: int | None = None) -> dict:
+    """Mean duration of the last `last_n` dispatches (in dispatch order) of the
+    kernels whose name contains `kernel_substr`, counting only the first
+    `within_first` such dispatches when given (a run that launches the kernel
+    again after its timed region)."""
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
             if kernel_substr in r["Kernel_Name"]:
                 rows.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     rows.sort()
+    if within_first is not None:
+        rows = rows[:within_first]
     durs = [d for _, d in rows[-last_n:]]
     if not durs:
         raise ValueError(f"no dispatches of {kernel_substr} in {path}")
