@@ -53,7 +53,7 @@ import numpy as np
 __all__ = [
     "sigmoid", "silu", "silu_grad", "evidence", "relation_matrix", "flow", "relation_head",
     "relation_fwd", "relation_rows", "relation_decode", "row_lse", "relation_head_bwd",
-    "relation_bwd", "factorized_head", "flash_scan_head",
+    "relation_bwd", "relation_head_bwd_sampled", "factorized_head", "flash_scan_head",
 ]
 
 
@@ -229,6 +229,63 @@ def relation_bwd(P1, P2, V, tau, lam, dY):
             dtau[h] += g[3]
             dlam += g[4]
     return dP1, dP2, dV, dtau, dlam
+
+
+def relation_head_bwd_sampled(p1, p2, v, tau, lam, dy, rows, cols, block=256):
+    """Selected gradient entries of one head without the T x T matrices, for
+    sizes where ``relation_head_bwd`` does not fit: dP1 at query rows `rows`,
+    dV and dP2 at key rows `cols`, and the head's dtau. The same chain rule
+    as ``relation_head_bwd``, evaluated row by row (dP1_i needs row i of R, F,
+    dF) and column by column (dV_j, dP2_j need column j), after one
+    block-by-block pass of the forward for every row's LSE_i, Y_i and D_i."""
+    p1, p2, v, dy = (np.asarray(x, dtype=np.float64) for x in (p1, p2, v, dy))
+    T, d_h = p1.shape
+    tau = float(tau)
+    c = 1.0 / math.sqrt(d_h)
+    log_i = np.log(np.arange(1, T + 1, dtype=np.float64))
+    diag_u = np.sum(p1 * p2, axis=1) * c
+    S = sigmoid(diag_u / tau)
+    lse = np.empty(T)
+    Y = np.empty((T, d_h))
+    for r0 in range(0, T, block):                     # forward, `block` query rows at a time
+        r1 = min(T, r0 + block)
+        U = (p1[r0:r1] @ p2.T) * c
+        R = silu(U) - lam * log_i[r0:r1, None]
+        i = np.arange(r0, r1)[:, None]
+        j = np.arange(T)[None, :]
+        R = np.where(j < i, R, -np.inf)
+        R[np.arange(r1 - r0), np.arange(r0, r1)] = S[r0:r1]
+        mx = np.max(R, axis=1, keepdims=True)
+        W = np.exp(R - mx)
+        lse[r0:r1] = mx[:, 0] + np.log(np.sum(W, axis=1))
+        Y[r0:r1] = (W / np.sum(W, axis=1, keepdims=True)) @ v
+    D = np.sum(dy * Y, axis=1)
+    dP1 = np.empty((len(rows), d_h))
+    for n, i in enumerate(rows):                      # row i: F_i., dF_i. over keys j <= i
+        u = (p2[: i + 1] @ p1[i]) * c
+        R = silu(u) - lam * log_i[i]
+        R[i] = S[i]
+        F = np.exp(R - lse[i])
+        dR = F * (v[: i + 1] @ dy[i] - D[i])
+        dU = dR * silu_grad(u)
+        dU[i] = dR[i] * S[i] * (1.0 - S[i]) / tau
+        dP1[n] = (dU @ p2[: i + 1]) * c
+    dV = np.empty((len(cols), d_h))
+    dP2 = np.empty((len(cols), d_h))
+    for n, j in enumerate(cols):                      # column j: F_.j, dF_.j over queries i >= j
+        u = (p1[j:] @ p2[j]) * c
+        R = silu(u) - lam * log_i[j:]
+        R[0] = S[j]
+        F = np.exp(R - lse[j:])
+        dR = F * (dy[j:] @ v[j] - D[j:])
+        dU = dR * silu_grad(u)
+        dU[0] = dR[0] * S[j] * (1.0 - S[j]) / tau
+        dV[n] = F @ dy[j:]
+        dP2[n] = (dU @ p1[j:]) * c
+    F_self = np.exp(S - lse)
+    dR_self = F_self * (np.sum(dy * v, axis=1) - D)
+    dtau = float(np.sum(dR_self * S * (1.0 - S) * (-diag_u / tau ** 2)))
+    return dict(dP1=dP1, dV=dV, dP2=dP2, dtau=dtau, lse=lse, Y=Y, F_self=F_self, S=S, U_self=diag_u)
 
 
 # ---------------------------------------------------------------------------

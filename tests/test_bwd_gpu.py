@@ -207,3 +207,36 @@ def test_bwd_gradients_of_the_future_do_not_reach_the_past():
     inp["dY"][:, :, :150] = 0
     _, _, (dP1, *_rest) = _gpu_train(inp, 0.0)
     assert float(dP1[:, :, :150].abs().max()) == 0.0
+
+
+def _sample(T, rng, n=24):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 255, 256, 257, 4095, 4096, T - 65, T - 64, T - 2, T - 1]
+    s = set(r for r in fixed if 0 <= r < T)
+    s.update(int(x) for x in rng.integers(0, T, n))
+    return sorted(s)
+
+
+@pytest.mark.parametrize("h", [0, 13, 31])
+def test_bwd_long_config_sampled(h):
+    """The T = 8192 workload (B=1 H=32 d_h=128 bf16, the bench's backward call)
+    on sampled rows of dP1 and sampled key rows of dV / dP2 of one head, plus
+    the head's dtau and every row's LSE, each computed by the oracle from the
+    definition row by row / column by column."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_bwd_inputs(cfg, 42)
+    Y, L, g = _gpu_train(inp, 0.0)
+    rng = np.random.default_rng(100 + h)
+    rows, cols = _sample(cfg.T, rng), _sample(cfg.T, rng)
+    p1, p2, v, dy = (f64(inp[k])[0, h] for k in ("P1", "P2", "V", "dY"))
+    tau = float(inp["tau"][h])
+    ref = O.relation_head_bwd_sampled(p1, p2, v, tau, 0.0, dy, rows, cols)
+    assert float(np.max(np.abs(f64(L)[0, h] - ref["lse"]))) <= LSE_ATOL
+    errs = {"dP1": row_err(f64(g[0])[0, h, rows], ref["dP1"]),
+            "dP2": row_err(f64(g[1])[0, h, cols], ref["dP2"]),
+            "dV": row_err(f64(g[2])[0, h, cols], ref["dV"])}
+    print(f"\nlong h={h}: " + " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+    size = ref["F_self"] * np.sum(np.abs(dy) * (np.abs(v) + np.abs(ref["Y"])), axis=1)
+    scale = float(np.sum(size * ref["S"] * (1 - ref["S"]) * np.abs(ref["U_self"]) / tau ** 2))
+    assert abs(float(f64(g[3])[h]) - ref["dtau"]) <= TOL["bf16"] * scale + 1e-6

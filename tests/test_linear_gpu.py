@@ -96,3 +96,16 @@ def test_linear_deterministic():
     a = _run(inp)
     b = _run(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("h", [0, 31])
+def test_linear_long_shape_full_heads(h):
+    """The bench's Linear Relation call (B=1 H=32 T=8192 d_h=128 bf16, seeded
+    retention), every output row and the final state of one head against the
+    oracle's recurrence."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_linear_inputs(cfg, 42)
+    Y, st = _run(inp)
+    sub = {k: inp[k][:, h:h + 1] for k in ("P1", "P2", "V", "alpha")}
+    sub["tau"] = inp["tau"][h:h + 1]
+    _check(sub, Y[:, h:h + 1], st[:, h:h + 1], "bf16", f"long h={h}")

@@ -187,3 +187,22 @@ def test_row_terms_sum_to_the_scalars_and_rows_of_dR_sum_to_zero(lam):
     np.testing.assert_allclose(terms["lam_terms"], log_i * terms["dR_self"], rtol=1e-9, atol=1e-13)
     # and the Self weight is e^{S_i - LSE_i}
     np.testing.assert_allclose(terms["F_self"], np.exp(terms["S"] - O.row_lse(p1, p2, 0.7, lam)), rtol=1e-12)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+def test_sampled_gradients_equal_the_materialised_ones(lam):
+    """The row / column route for large T agrees with the materialised
+    backward (itself pinned above) on every row and column, with a block size
+    that does not divide T."""
+    rng = np.random.default_rng(14)
+    T, d = 37, 5
+    p1, p2, v, dy = _head(rng, T, d, scale=1.2)
+    full = O.relation_head_bwd(p1, p2, v, 0.8, lam, dy)
+    rows = list(range(T))
+    got = O.relation_head_bwd_sampled(p1, p2, v, 0.8, lam, dy, rows, rows, block=8)
+    np.testing.assert_allclose(got["dP1"], full[0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["dP2"], full[1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["dV"], full[2], rtol=1e-10, atol=1e-12)
+    assert math.isclose(got["dtau"], full[3], rel_tol=1e-10, abs_tol=1e-12)
+    np.testing.assert_allclose(got["lse"], O.row_lse(p1, p2, 0.8, lam), rtol=1e-12)
+    np.testing.assert_allclose(got["Y"], O.relation_head(p1, p2, v, 0.8, lam), rtol=1e-12, atol=1e-12)
