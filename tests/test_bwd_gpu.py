@@ -216,27 +216,30 @@ def _sample(T, rng, n=24):
     return sorted(s)
 
 
-@pytest.mark.parametrize("h", [0, 13, 31])
-def test_bwd_long_config_sampled(h):
-    """The T = 8192 workload (B=1 H=32 d_h=128 bf16, the bench's backward call)
-    on sampled rows of dP1 and sampled key rows of dV / dP2 of one head, plus
-    the head's dtau and every row's LSE, each computed by the oracle from the
-    definition row by row / column by column."""
-    cfg = W.CONFIGS["long"]
+@pytest.mark.parametrize("name,b,h", [("long", 0, 0), ("long", 0, 13), ("long", 0, 31), ("mid", 0, 0),
+                                      ("mid", 3, 15)])
+def test_bwd_config_sampled(name, b, h):
+    """The T = 8192 workload (B=1 H=32 d_h=128, the bench's backward call) and
+    the Mid workload (B=4 H=16 T=2048 d_h=64), bf16, on sampled rows of dP1
+    and sampled key rows of dV / dP2 of one (b, h), every row's LSE, and (for
+    B = 1) the head's dtau, each computed by the oracle from the definition
+    row by row / column by column."""
+    cfg = W.CONFIGS[name]
     inp = W.make_bwd_inputs(cfg, 42)
     Y, L, g = _gpu_train(inp, 0.0)
-    rng = np.random.default_rng(100 + h)
+    rng = np.random.default_rng(100 + 17 * b + h)
     rows, cols = _sample(cfg.T, rng), _sample(cfg.T, rng)
-    p1, p2, v, dy = (f64(inp[k])[0, h] for k in ("P1", "P2", "V", "dY"))
+    p1, p2, v, dy = (f64(inp[k])[b, h] for k in ("P1", "P2", "V", "dY"))
     tau = float(inp["tau"][h])
     ref = O.relation_head_bwd_sampled(p1, p2, v, tau, 0.0, dy, rows, cols)
-    assert float(np.max(np.abs(f64(L)[0, h] - ref["lse"]))) <= LSE_ATOL
-    errs = {"dP1": row_err(f64(g[0])[0, h, rows], ref["dP1"]),
-            "dP2": row_err(f64(g[1])[0, h, cols], ref["dP2"]),
-            "dV": row_err(f64(g[2])[0, h, cols], ref["dV"])}
-    print(f"\nlong h={h}: " + " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    assert float(np.max(np.abs(f64(L)[b, h] - ref["lse"]))) <= LSE_ATOL
+    errs = {"dP1": row_err(f64(g[0])[b, h, rows], ref["dP1"]),
+            "dP2": row_err(f64(g[1])[b, h, cols], ref["dP2"]),
+            "dV": row_err(f64(g[2])[b, h, cols], ref["dV"])}
+    print(f"\n{name} b={b} h={h}: " + " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
     for k, e in errs.items():
         assert e <= TOL["bf16"], (k, e)
-    size = ref["F_self"] * np.sum(np.abs(dy) * (np.abs(v) + np.abs(ref["Y"])), axis=1)
-    scale = float(np.sum(size * ref["S"] * (1 - ref["S"]) * np.abs(ref["U_self"]) / tau ** 2))
-    assert abs(float(f64(g[3])[h]) - ref["dtau"]) <= TOL["bf16"] * scale + 1e-6
+    if cfg.B == 1:
+        size = ref["F_self"] * np.sum(np.abs(dy) * (np.abs(v) + np.abs(ref["Y"])), axis=1)
+        scale = float(np.sum(size * ref["S"] * (1 - ref["S"]) * np.abs(ref["U_self"]) / tau ** 2))
+        assert abs(float(f64(g[3])[h]) - ref["dtau"]) <= TOL["bf16"] * scale + 1e-6
