@@ -240,9 +240,9 @@ def bench_paper_geometry(torch, R, W, steps, warmup):
     (relation_fwd_ex, lambda = 0.5 as in the paper's models) against PyTorch
     FlashAttention (scaled_dot_product_attention, causal, flash backend
     forced) on the same MI355X, H = 8 and 131,072 tokens per step at the three
-    model geometries (d_h, T) = (48, 1024), (64, 2048), (80, 4096). Forward
-    for all three; forward + backward where relation_bwd has MFMA kernels
-    (d_h = 64). Tokens/s and the FR / FA ratio."""
+    model geometries (d_h, T) = (48, 1024), (64, 2048), (80, 4096), forward
+    and forward + backward (relation_fwd_lse + relation_bwd against SDPA with
+    autograd). Tokens/s and the FR / FA ratio."""
     from torch.nn.attention import sdpa_kernel
     be_name, be = _flash_sdpa(torch)
     out = {"attention_backend": be_name, "rows": []}
@@ -264,31 +264,30 @@ def bench_paper_geometry(torch, R, W, steps, warmup):
             fa_ms /= steps
             row.update({"FA_fwd_ms": round(fa_ms, 4), "FA_fwd_tok/s": round(B * T / (fa_ms * 1e-3), 0),
                         "FR_over_FA_fwd": round(fa_ms / fr_ms, 3)})
-        if d == 64:
-            Yl, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
-            grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
-                     torch.empty(H, device="cuda"), torch.empty(1, device="cuda"))
-            ws = torch.empty(R.bwd_workspace_bytes(B, H, T, d), dtype=torch.uint8, device="cuda")
+        Yl, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
+        grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
+                 torch.empty(H, device="cuda"), torch.empty(1, device="cuda"))
+        ws = torch.empty(R.bwd_workspace_bytes(B, H, T, d), dtype=torch.uint8, device="cuda")
 
-            def fr_train():
-                R.fwd_lse(P1, P2, V, inp["tau"], 0.5, out=Yl, lse=L)
-                R.bwd(P1, P2, V, inp["tau"], 0.5, Yl, L, dY, grads=grads, workspace=ws)
+        def fr_train():
+            R.fwd_lse(P1, P2, V, inp["tau"], 0.5, out=Yl, lse=L)
+            R.bwd(P1, P2, V, inp["tau"], 0.5, Yl, L, dY, grads=grads, workspace=ws)
 
-            _, frt, _ = time_launches(fr_train, steps, warmup, torch)
-            frt /= steps
-            row.update({"FR_fwd_bwd_ms": round(frt, 4), "FR_fwd_bwd_tok/s": round(B * T / (frt * 1e-3), 0)})
-            if be is not None:
-                q, k, v = (x.detach().clone().requires_grad_(True) for x in (P1, P2, V))
+        _, frt, _ = time_launches(fr_train, steps, warmup, torch)
+        frt /= steps
+        row.update({"FR_fwd_bwd_ms": round(frt, 4), "FR_fwd_bwd_tok/s": round(B * T / (frt * 1e-3), 0)})
+        if be is not None:
+            q, k, v = (x.detach().clone().requires_grad_(True) for x in (P1, P2, V))
 
-                def fa_train():
-                    with sdpa_kernel([be]):
-                        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
-                    o.backward(dY)
+            def fa_train():
+                with sdpa_kernel([be]):
+                    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                o.backward(dY)
 
-                _, fat, _ = time_launches(fa_train, steps, warmup, torch)
-                fat /= steps
-                row.update({"FA_fwd_bwd_ms": round(fat, 4), "FA_fwd_bwd_tok/s": round(B * T / (fat * 1e-3), 0),
-                            "FR_over_FA_fwd_bwd": round(fat / frt, 3)})
+            _, fat, _ = time_launches(fa_train, steps, warmup, torch)
+            fat /= steps
+            row.update({"FA_fwd_bwd_ms": round(fat, 4), "FA_fwd_bwd_tok/s": round(B * T / (fat * 1e-3), 0),
+                        "FR_over_FA_fwd_bwd": round(fat / frt, 3)})
         out["rows"].append(row)
         del P1, P2, V, dY, Y
     return out

@@ -176,8 +176,13 @@ __device__ __forceinline__ void load4(const __bf16* p, float (&x)[4]) {
 template <bool B>
 using Tag = std::integral_constant<bool, B>;
 
-template <int D>
+// D: head size of the tile layout (64 or 128); DR: the rows' real head size
+// (48 and 80 run on the 64 / 128 layouts with zero-filled pad chunks, as in
+// the forward: exact evidence, zero pad rows of the transports, pad columns
+// not stored).
+template <int D, int DR = D>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadParams hp) {
+  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
@@ -193,8 +198,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   const int lq = lane & 31;
   const int hf = lane >> 5;
 
-  const size_t head = (size_t)bh * (size_t)T * D;
-  const long long head_bytes = (long long)T * D * 2;
+  const size_t head = (size_t)bh * (size_t)T * DR;
+  const long long head_bytes = (long long)T * DR * 2;
   const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
   const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
   const __bf16* V = static_cast<const __bf16*>(a.V) + head;
@@ -211,11 +216,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   {
     const auto rP1 = rsrc(P1, head_bytes);
     const auto rdY = rsrc(dY, head_bytes);
-    const int qoff = qrow * (D * 2) + hf * 16;
+    const int qoff = qrow * (DR * 2) + hf * 16;
 #pragma unroll
     for (int ds = 0; ds < C::kDs; ++ds) {
-      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, qoff + ds * 32, 0, 0));
-      yf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdY, qoff + ds * 32, 0, 0));
+      const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;   // pad k-steps read 0
+      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, o, 0, 0));
+      yf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdY, o, 0, 0));
     }
   }
   const bool valid = qrow < T;
@@ -238,13 +244,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   int src_row[C::kPer], src_tr[C::kPer];
 #pragma unroll
   for (int u = 0; u < C::kPer; ++u) {
-    src_row[u] = C::row_src(wave + kDqWaves * u, lane);
-    src_tr[u] = C::tr_src(wave + kDqWaves * u, lane);
+    src_row[u] = C::template row_src_real<DR>(wave + kDqWaves * u, lane);
+    src_tr[u] = C::template tr_src_real<DR>(wave + kDqWaves * u, lane);
   }
   auto dma = [&](int t) {
-    const int left = hb - t * kTileRows * D * 2;
-    const auto rk = rsrc_words(P2 + (size_t)t * kTileRows * D, left);
-    const auto rv = rsrc_words(V + (size_t)t * kTileRows * D, left);
+    const int left = hb - t * kTileRows * DR * 2;
+    const auto rk = rsrc_words(P2 + (size_t)t * kTileRows * DR, left);
+    const auto rv = rsrc_words(V + (size_t)t * kTileRows * DR, left);
     char* slot = smem + (t % kDqSlots) * C::kSlotBytes;
 #pragma unroll
     for (int u = 0; u < C::kPer; ++u) {
@@ -305,11 +311,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h); the statistic holds
   // dU_ii / sqrt(d_h). Lane holds columns 32 db + 8 g4 + 4 hf + 0..3.
   const float us = a.stats[stat_at(bh, nt, qrow, 3)];
-  const size_t ro = (size_t)qrow * D;
+  const size_t ro = (size_t)qrow * DR;
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
+      if (32 * db + 8 * g4 >= DR) continue;          // padded columns
       const int col = 32 * db + 8 * g4 + 4 * hf;
       float p[4];
       load4(P2 + ro + col, p);
@@ -328,8 +335,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
 // a barrier each transports the partner's block. Both roles do the same MFMA
 // and VALU work, and each runs in its own code region so that two waves fit
 // per SIMD.
-template <int D>
+template <int D, int DR = D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
+  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
@@ -345,8 +353,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const int lq = lane & 31;
   const int hf = lane >> 5;
 
-  const size_t head = (size_t)bh * (size_t)T * D;
-  const long long head_bytes = (long long)T * D * 2;
+  const size_t head = (size_t)bh * (size_t)T * DR;
+  const long long head_bytes = (long long)T * DR * 2;
   const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
   const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
   const __bf16* V = static_cast<const __bf16*>(a.V) + head;
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   const int k0 = kt * kKvRows;
   const int krow = k0 + kg * 32 + lq;                  // may be >= T: loads give 0, stores drop
   const int own = k0 / 32 + kg;
-  const int koff = krow * (D * 2) + hf * 16;
+  const int koff = krow * (DR * 2) + hf * 16;
   const float c = hp.scale;
   const float k2 = c * kLog2e;
 
@@ -367,13 +375,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   int src_row[C::kPer], src_tr[C::kPer];
 #pragma unroll
   for (int u = 0; u < C::kPer; ++u) {
-    src_row[u] = C::row_src(wave + kKvWaves * u, lane);
-    src_tr[u] = C::tr_src(wave + kKvWaves * u, lane);
+    src_row[u] = C::template row_src_real<DR>(wave + kKvWaves * u, lane);
+    src_tr[u] = C::template tr_src_real<DR>(wave + kKvWaves * u, lane);
   }
   auto dma = [&](int t) {
-    const int left = hb - t * kTileRows * D * 2;
-    const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * D, left);
-    const auto ry = rsrc_words(dY + (size_t)t * kTileRows * D, left);
+    const int left = hb - t * kTileRows * DR * 2;
+    const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * DR, left);
+    const auto ry = rsrc_words(dY + (size_t)t * kTileRows * DR, left);
     char* slot = smem + ((t - t0) % kKvSlots) * C::kSlotBytes;
 #pragma unroll
     for (int u = 0; u < C::kPer; ++u) {
@@ -403,8 +411,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
       const auto rV = rsrc(V, head_bytes);
 #pragma unroll
       for (int ds = 0; ds < C::kDs; ++ds) {
-        kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, koff + ds * 32, 0, 0));
-        vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, koff + ds * 32, 0, 0));
+        const int o = ds < DR / 16 ? koff + ds * 32 : kOutOfRange;   // pad k-steps read 0
+        kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
+        vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, o, 0, 0));
       }
     }
     // The first two query tiles (issued after the key rows, so that the
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
     for (; t < nt; ++t) tile(t, Tag<true>{});
 
     if (krow >= T) return;
-    const size_t ro = (size_t)krow * D;
+    const size_t ro = (size_t)krow * DR;
     if constexpr (kP) {
       // dP2_j = (sum_i dU_ij p1_i + dU_jj p1_j) / sqrt(d_h).
       __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
@@ -480,6 +489,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
       for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+          if (32 * db + 8 * g4 >= DR) continue;      // padded columns
           const int col = 32 * db + 8 * g4 + 4 * hf;
           const int r = 4 * g4;
           float p[4];
@@ -496,6 +506,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
       for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
+          if (32 * db + 8 * g4 >= DR) continue;      // padded columns
           const int col = 32 * db + 8 * g4 + 4 * hf;
           const int r = 4 * g4;
           float y[4];
@@ -510,13 +521,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   else run(Tag<false>{});
 }
 
-template <int D>
+template <int D, int DR = D>
 hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nq = (a.T + kDqRows - 1) / kDqRows;
   const int nk = (a.T + kKvRows - 1) / kKvRows;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 
@@ -525,12 +536,14 @@ hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
 bool bwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including
   // the rows past T of the last tile.
-  return (d_h == 64 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
+  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
 }
 
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   switch (a.d_h) {
+    case 48: return launch_typed<64, 48>(a, hp, s);
     case 64: return launch_typed<64>(a, hp, s);
+    case 80: return launch_typed<128, 80>(a, hp, s);
     case 128: return launch_typed<128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }

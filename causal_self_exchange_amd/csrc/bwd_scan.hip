@@ -50,8 +50,12 @@ __device__ __forceinline__ void load8(const Tin* p, float (&x)[8]) {
 // last 64-row tile get the padding values) and one (dtau, dlambda) partial.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a, HeadParams hp) {
-  constexpr int kLpr = D / 8;                      // lanes per row
+  // Lanes per row: D / 8 loading lanes, rounded up to a power of two for the
+  // shuffle reduction (the extra lanes contribute 0).
+  constexpr int kUsed = D / 8;
+  constexpr int kLpr = kUsed <= 4 ? 4 : (kUsed <= 8 ? 8 : 16);
   constexpr int kRowsPerPass = kPrepThreads / kLpr;
+  static_assert(kUsed <= kLpr && kPrepRows % kRowsPerPass == 0, "prep lane layout");
   __shared__ float red[2][kPrepThreads / 64];
 
   const int T = a.T;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a, HeadP
   for (int pass = 0; pass < kPrepRows / kRowsPerPass; ++pass) {
     const int r = chunk * kPrepRows + pass * kRowsPerPass + tid / kLpr;
     float dyy = 0.0f, p12 = 0.0f, dyv = 0.0f;
-    if (r < T) {
+    if (r < T && sub < kUsed) {
       float x[8], y[8];
       const size_t off = (size_t)r * D + 8 * sub;
       load8(dY + off, x);
@@ -338,7 +342,9 @@ hipError_t launch_scan_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t
 hipError_t launch_bwd_prep(const BwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s) {
   switch (a.d_h) {
     case 32: return bf16 ? launch_prep_typed<__bf16, 32>(a, hp, s) : launch_prep_typed<float, 32>(a, hp, s);
+    case 48: return bf16 ? launch_prep_typed<__bf16, 48>(a, hp, s) : launch_prep_typed<float, 48>(a, hp, s);
     case 64: return bf16 ? launch_prep_typed<__bf16, 64>(a, hp, s) : launch_prep_typed<float, 64>(a, hp, s);
+    case 80: return bf16 ? launch_prep_typed<__bf16, 80>(a, hp, s) : launch_prep_typed<float, 80>(a, hp, s);
     case 128: return bf16 ? launch_prep_typed<__bf16, 128>(a, hp, s) : launch_prep_typed<float, 128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }
@@ -347,7 +353,9 @@ hipError_t launch_bwd_prep(const BwdArgs& a, const HeadParams& hp, bool bf16, hi
 hipError_t launch_bwd_scan(const BwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s) {
   switch (a.d_h) {
     case 32: return bf16 ? launch_scan_typed<__bf16, 32>(a, hp, s) : launch_scan_typed<float, 32>(a, hp, s);
+    case 48: return bf16 ? launch_scan_typed<__bf16, 48>(a, hp, s) : launch_scan_typed<float, 48>(a, hp, s);
     case 64: return bf16 ? launch_scan_typed<__bf16, 64>(a, hp, s) : launch_scan_typed<float, 64>(a, hp, s);
+    case 80: return bf16 ? launch_scan_typed<__bf16, 80>(a, hp, s) : launch_scan_typed<float, 80>(a, hp, s);
     case 128: return bf16 ? launch_scan_typed<__bf16, 128>(a, hp, s) : launch_scan_typed<float, 128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }

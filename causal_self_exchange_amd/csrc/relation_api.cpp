@@ -27,8 +27,8 @@ size_t elem_size(rel_dtype dt) { return dt == REL_BF16 ? 2 : 4; }
 bool dtype_ok(rel_dtype dt) { return dt == REL_F32 || dt == REL_BF16; }
 
 bool head_dim_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128; }
-// The forward, its training variant and the pre-steps also take the paper's
-// non-power-of-two head sizes.
+// The forward, its training variant, the backward and the pre-steps also take
+// the paper's non-power-of-two head sizes.
 bool fwd_head_dim_ok(int d_h) { return head_dim_ok(d_h) || d_h == 48 || d_h == 80; }
 
 // Product of positive ints; false if any is < 1 or the product exceeds 2^40
@@ -290,7 +290,7 @@ rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I, co
 
 size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h) {
   int64_t n = 0;
-  if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h)) return 0;
+  if (!count(n, {B, H, T, d_h}) || !fwd_head_dim_ok(d_h)) return 0;
   const int64_t BH = static_cast<int64_t>(B) * H;
   return align256(static_cast<size_t>(rel::bwd_stat_floats(BH, T)) * sizeof(float)) +
          align256(static_cast<size_t>(rel::bwd_part_floats(BH, T)) * sizeof(float));
@@ -306,7 +306,7 @@ rel_status relation_bwd(const void* P1, const void* P2, const void* V, const flo
   int64_t n = 0;
   if (!count(n, {B, H, T, d_h}) || H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
-  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!fwd_head_dim_ok(d_h)) return REL_E_HEADDIM;
   HeadParams hp;
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;

@@ -36,7 +36,7 @@
  *     range or another output range.
  *   - Supported: d_h in {32, 64, 128} for every entry point, and also 48 and
  *     80 (the paper's model geometries) for relation_fwd, relation_fwd_ex,
- *     relation_fwd_lse, relation_prestep and relation_fwd_model;
+ *     relation_fwd_lse, relation_bwd, relation_prestep and relation_fwd_model;
  *     1 <= H <= REL_MAX_HEADS; B <= 65535.
  */
 #ifndef RELATION_H
@@ -153,9 +153,10 @@ size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h);
  * Every output is overwritten (not accumulated into). The result is
  * deterministic: no atomics, scalar sums in a fixed order (fp64 across rows
  * chunks, heads and batch).
- * Numerics: REL_BF16 with d_h in {64, 128} recomputes both evidence products
- * on bf16 MFMA and rounds F and dU to bf16 as operands of the gradient
- * products (fp32 accumulation); other cases compute in fp32 throughout.
+ * Numerics: REL_BF16 with d_h in {48, 64, 80, 128} recomputes both evidence
+ * products on bf16 MFMA and rounds F and dU to bf16 as operands of the
+ * gradient products (fp32 accumulation); other cases compute in fp32
+ * throughout.
  */
 rel_status relation_bwd(const void* P1, const void* P2, const void* V,
                         const float* tau_s, float lambda, const void* Y,

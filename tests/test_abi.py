@@ -152,7 +152,8 @@ def test_bwd_workspace_bytes():
     assert lib.relation_bwd_workspace_bytes(2, 3, 1, 32) == want(2, 3, 1)
     assert lib.relation_bwd_workspace_bytes(4, 16, 2049, 64) == want(4, 16, 2049)
     assert lib.relation_bwd_workspace_bytes(0, 3, 10, 64) == 0
-    assert lib.relation_bwd_workspace_bytes(1, 1, 10, 48) == 0
+    assert lib.relation_bwd_workspace_bytes(1, 1, 10, 96) == 0
+    assert lib.relation_bwd_workspace_bytes(4, 8, 1024, 48) == want(4, 8, 1024)
 
 
 def bwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, dY=DY_, dP1=G1, dP2=G2, dV=G3,
@@ -168,7 +169,7 @@ def bwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, dY=DY_, dP1=G1,
     (dict(dY=None), E_NULL), (dict(L=None), E_NULL), (dict(dtau=None), E_NULL), (dict(dlam=None), E_NULL),
     (dict(dP2=None), E_NULL), (dict(tau=None), E_NULL),
     (dict(T=0), E_SHAPE), (dict(B=70000), E_SHAPE), (dict(H=257, tau=[1.0] * 257), E_SHAPE),
-    (dict(dt=3), E_DTYPE), (dict(D=80), E_HEADDIM), (dict(tau=(1.0, float("nan"))), E_TAU),
+    (dict(dt=3), E_DTYPE), (dict(D=96), E_HEADDIM), (dict(tau=(1.0, float("nan"))), E_TAU),
     (dict(lam=float("inf")), E_LAMBDA),
     (dict(ws=None), E_WS), (dict(ws_bytes=1000), E_WS),
     (dict(dP1=G1 + 8), E_ALIGN), (dict(ws=WS + 8), E_ALIGN), (dict(dtau=DT + 2), E_ALIGN),

@@ -124,6 +124,9 @@ SHAPES = [
     (1, 2, 129, 128, "bf16"), (3, 1, 191, 64, "bf16"), (1, 2, 300, 128, "bf16"), (1, 1, 513, 128, "bf16"),
     (2, 2, 100, 32, "bf16"), (1, 2, 77, 32, "f32"), (1, 1, 64, 64, "f32"), (1, 1, 150, 128, "f32"),
     (1, 1, 1, 32, "f32"),
+    # the paper's head sizes: MFMA kernels on the 64 / 128 layouts (bf16), row-scan kernels (fp32)
+    (2, 4, 300, 48, "bf16"), (1, 2, 257, 80, "bf16"), (1, 1, 1, 48, "bf16"), (1, 2, 130, 48, "f32"),
+    (1, 1, 99, 80, "f32"),
 ]
 
 
