@@ -25,8 +25,9 @@
  *     return). Every tau must be finite and > 0 (the paper requires tau_S > 0).
  *   - lambda is the count-calibration coefficient; 0 gives the operator without
  *     count calibration.
- *   - The caller owns every buffer. The library allocates nothing, keeps no
- *     pointer after returning and holds no mutable global state.
+ *   - The caller owns every buffer. The library allocates nothing and keeps
+ *     no pointer after returning; its only global state is a per-device cache
+ *     of the compute-unit count (written once, the same value by any caller).
  *   - All argument checks run on the host before any HIP call; on an error
  *     nothing is launched and no memory is touched.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
