@@ -22,80 +22,112 @@ namespace rel {
 namespace {
 
 constexpr int kL = kLinChunk;          // tokens per chunk
-constexpr int kThreads = 256;
+constexpr int kChunkThreads = 256;     // chunk kernel: 4 waves, 66 KB of LDS (two work-groups per CU)
+constexpr int kOutThreads = 512;       // output kernel: 8 waves, 152 KB of LDS
+constexpr int kScanThreads = 256;
 static_assert(kL == 64, "the output kernel's sub-block pairs assume 4 blocks of 16 rows");
+// A diagonal 16-row block of the intra-chunk weights factors through its
+// middle row when every exponent of the two factors lies in [-40, 40]: the
+// factors and their products then stay normal fp32 numbers.
+constexpr float kFactorBound = 40.0f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 
 template <typename Tin>
 __device__ __forceinline__ float ld_val(const Tin* p, size_t i) { return to_f32(p[i]); }
 
-// Copy of a chunk's rows (rows >= `rows` give 0) into an fp32 LDS array,
-// row-major [t][r] (ld = row stride) or channel-major [r][t]. Every thread
-// issues all of its 16-byte loads before it writes any of them, so one
-// memory latency covers the chunk.
-template <typename Tin, int D, bool kChannelMajor>
-__device__ __forceinline__ void stage_rows(const Tin* src, int rows, float* dst, int ld) {
-  constexpr int kVec = 16 / (int)sizeof(Tin);          // elements per 16-byte load
-  constexpr int kN = kL * D / (kVec * kThreads);        // loads per thread
-  static_assert(kN >= 1 && kL * D % (kVec * kThreads) == 0, "whole loads per thread");
-  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+// A chunk's rows (rows >= `rows` give 0) in registers: NT threads issue every
+// 16-byte load before any is used, so one memory latency covers the chunk.
+template <int NT, typename Tin, int D>
+struct Staged {
+  static constexpr int kVec = 16 / (int)sizeof(Tin);   // elements per 16-byte load
+  static constexpr int kTot = kL * D / kVec;            // loads per chunk
+  static constexpr int kN = (kTot + NT - 1) / NT;       // loads per thread
+  static_assert(kL * D % kVec == 0, "whole loads per row");
   u32x4v v[kN];
+
+  __device__ __forceinline__ void load(const Tin* src, int rows) {
 #pragma unroll
-  for (int i = 0; i < kN; ++i) {
-    const int e = (threadIdx.x + i * kThreads) * kVec;
-    v[i] = (e / D) < rows ? *reinterpret_cast<const u32x4v*>(src + e) : u32x4v{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int i = 0; i < kN; ++i) {
-    const int e = (threadIdx.x + i * kThreads) * kVec;
-    const int t = e / D, r0 = e % D;
-    float x[kVec];
-    if constexpr (sizeof(Tin) == 2) {
-      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-      const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
-#pragma unroll
-      for (int u = 0; u < kVec; ++u) x[u] = (float)b[u];
-    } else {
-#pragma unroll
-      for (int u = 0; u < kVec; ++u) x[u] = __uint_as_float(v[i][u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kVec; ++u) {
-      if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u];
-      else dst[t * ld + r0 + u] = x[u];
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * NT, e = idx * kVec;
+      v[i] = (idx < kTot && e / D < rows) ? *reinterpret_cast<const u32x4v*>(src + e) : u32x4v{0u, 0u, 0u, 0u};
     }
   }
-}
+  // Into an fp32 LDS array, row-major [t][r] (ld = row stride) or
+  // channel-major [r][t].
+  template <bool kChannelMajor>
+  __device__ __forceinline__ void store(float* dst, int ld) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * NT, e = idx * kVec;
+      if (idx >= kTot) break;
+      const int t = e / D, r0 = e % D;
+      float x[kVec];
+      if constexpr (sizeof(Tin) == 2) {
+        typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+        const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) x[u] = (float)b[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) x[u] = __uint_as_float(v[i][u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) {
+        if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u];
+        else dst[t * ld + r0 + u] = x[u];
+      }
+    }
+  }
+};
 
 // Row statistics from LDS copies of P1 and P2 (element (t, r) at
-// p[t * rs + r * cs]): S_t into s[], reciprocal row norms into n1[], n2[];
-// one wave per row at a time.
-template <int D>
+// p[t * rs + r * cs]): S_t into s[], reciprocal row norms into n1[], n2[].
+// Each wave takes kL / waves rows at once, so the cross-lane reductions of
+// all its rows are independent of one another.
+template <int NT, int D>
 __device__ __forceinline__ void row_stats(const float* p1, const float* p2, int rs, int cs, int rows, float inv_scale,
                                           float* s, float* n1, float* n2) {
+  constexpr int kW = NT / 64;
+  constexpr int kRows = kL / kW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = wave; t < kL; t += kThreads / 64) {
-    float d12 = 0.0f, d11 = 0.0f, d22 = 0.0f;
+  float d12[kRows], d11[kRows], d22[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int t = wave + kW * k;
+    d12[k] = 0.0f;
+    d11[k] = 0.0f;
+    d22[k] = 0.0f;
+#pragma unroll
     for (int r = lane; r < D; r += 64) {
       const float a = p1[t * rs + r * cs], b = p2[t * rs + r * cs];
-      d12 = fmaf(a, b, d12);
-      d11 = fmaf(a, a, d11);
-      d22 = fmaf(b, b, d22);
+      d12[k] = fmaf(a, b, d12[k]);
+      d11[k] = fmaf(a, a, d11[k]);
+      d22[k] = fmaf(b, b, d22[k]);
     }
+  }
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) {
-      d12 += __shfl_xor(d12, w, 64);
-      d11 += __shfl_xor(d11, w, 64);
-      d22 += __shfl_xor(d22, w, 64);
+  for (int w = 32; w >= 1; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      d12[k] += __shfl_xor(d12[k], w, 64);
+      d11[k] += __shfl_xor(d11[k], w, 64);
+      d22[k] += __shfl_xor(d22[k], w, 64);
     }
-    if (lane == 0) {
-      s[t] = t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
-      // A zero row has no direction: its normalised coordinate is 0.
-      n1[t] = d11 > 0.0f ? 1.0f / sqrtf(d11) : 0.0f;
-      n2[t] = d22 > 0.0f ? 1.0f / sqrtf(d22) : 0.0f;
-    }
+  if (lane < kRows) {
+    // Lane k writes row wave + kW k (a register array indexed by a uniform
+    // loop, so pick the lane's entry by comparison).
+    float a12 = 0.0f, a11 = 0.0f, a22 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+      if (lane == k) { a12 = d12[k]; a11 = d11[k]; a22 = d22[k]; }
+    const int t = wave + kW * lane;
+    s[t] = t < rows ? sigmoid_f32(a12 * inv_scale) : 0.0f;
+    // A zero row has no direction: its normalised coordinate is 0.
+    n1[t] = a11 > 0.0f ? 1.0f / sqrtf(a11) : 0.0f;
+    n2[t] = a22 > 0.0f ? 1.0f / sqrtf(a22) : 0.0f;
   }
 }
 
@@ -104,22 +136,31 @@ __device__ __forceinline__ void row_stats(const float* p1, const float* p2, int 
 // the last value). alpha is clamped to [1e-30, 1] (NaN to 1e-30): log alpha
 // stays finite, so differences of prefixes never form inf - inf, and a
 // retention below 1e-30 already wipes the state within one step to fp32
-// precision. A thread reads its whole channel before the first logarithm.
-template <int D>
-__device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows) {
-  for (int r = threadIdx.x; r < D; r += kThreads) {
-    float x[kL];
+// precision. NT / D threads share a channel, each a segment of consecutive
+// tokens: every thread takes the logarithms of its segment and their running
+// sum, then adds the totals of the earlier segments (in order). `tot` is NT
+// floats of LDS scratch. Contains a barrier: every thread must call it.
+template <int NT, int D>
+__device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows, float* tot) {
+  constexpr int kSeg = NT / D;
+  constexpr int kLen = kL / kSeg;
+  static_assert(NT % D == 0 && kL % kSeg == 0, "whole segments");
+  const int r = threadIdx.x % D, seg = threadIdx.x / D, t0 = seg * kLen;
+  float x[kLen];
 #pragma unroll
-    for (int t = 0; t < kL; ++t) x[t] = b[t * rs + r * cs];
-    float acc = 0.0f;
+  for (int i = 0; i < kLen; ++i) x[i] = b[(t0 + i) * rs + r * cs];
+  float acc = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kL; ++t) {
-      if (t < rows) acc += logf(fminf(fmaxf(x[t], 1e-30f), 1.0f));
-      x[t] = acc;
-    }
-#pragma unroll
-    for (int t = 0; t < kL; ++t) b[t * rs + r * cs] = x[t];
+  for (int i = 0; i < kLen; ++i) {
+    if (t0 + i < rows) acc += logf(fminf(fmaxf(x[i], 1e-30f), 1.0f));
+    x[i] = acc;
   }
+  tot[seg * D + r] = acc;
+  __syncthreads();
+  float off = 0.0f;
+  for (int q = 0; q < seg; ++q) off += tot[q * D + r];
+#pragma unroll
+  for (int i = 0; i < kLen; ++i) b[(t0 + i) * rs + r * cs] = x[i] + off;
 }
 
 // Phase 1: per (b*H + h, chunk): dC = sum_j S_j (k_j o e^{b_last - b_j}) I_j^T
@@ -128,12 +169,15 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows)
 // wave owns column block n and all row blocks (independent accumulators that
 // share the I operand, which comes straight from global memory into
 // registers). LDS holds Kt and the decay prefix only (P1 passes through the
-// prefix buffer first), 64 KB at d_h = 128, so two work-groups fit per CU.
+// prefix buffer first; alpha waits in registers meanwhile), 66 KB at
+// d_h = 128, so two work-groups fit per CU.
 template <typename Tin, int D>
-__global__ __launch_bounds__(kThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
+__global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
+  constexpr int NT = kChunkThreads;
   __shared__ float kt[kL][D];     // p2_j, then S_j k_j e^{b_last - b_j}
   __shared__ float bt[kL][D];     // p1_j, then alpha_j, then b_j
   __shared__ float s[kL], n1[kL], n2[kL];
+  __shared__ float tot[NT];
   const int nc = (a.T + kL - 1) / kL;
   const int c = blockIdx.x % nc;
   const int bh = blockIdx.x / nc;
@@ -158,16 +202,23 @@ __global__ __launch_bounds__(kThreads) void lin_chunk_kernel(LinArgs a, HeadPara
       bf[q][ks] = (n < kT && j < rows) ? ld_val(I, (size_t)j * D + 32 * n + l32) : 0.0f;
     }
   }
-  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.P1) + base, rows, &bt[0][0], D);
-  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.P2) + base, rows, &kt[0][0], D);
+  {
+    Staged<NT, Tin, D> g1, g2;
+    g1.load(static_cast<const Tin*>(a.P1) + base, rows);
+    g2.load(static_cast<const Tin*>(a.P2) + base, rows);
+    g1.template store<false>(&bt[0][0], D);
+    g2.template store<false>(&kt[0][0], D);
+  }
+  Staged<NT, float, D> ga;
+  ga.load(a.alpha + base, rows);
   __syncthreads();
-  row_stats<D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
+  row_stats<NT, D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
   __syncthreads();
-  stage_rows<float, D, false>(a.alpha + base, rows, &bt[0][0], D);
+  ga.template store<false>(&bt[0][0], D);
   __syncthreads();
-  decay_prefix<D>(&bt[0][0], D, 1, rows);
+  decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot);
   __syncthreads();
-  for (int e = threadIdx.x; e < kL * D; e += kThreads) {
+  for (int e = threadIdx.x; e < kL * D; e += NT) {
     const int t = e / D, r = e % D;
     kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
   }
@@ -200,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void lin_chunk_kernel(LinArgs a, HeadPara
 // Cin_{c+1} = e^{b_last,c}[r] Cin_c + dC_c; each chunk slot is overwritten
 // with its entering state, and the final state goes to a.final (if given).
 template <int D>
-__global__ __launch_bounds__(kThreads) void lin_scan_kernel(LinArgs a) {
-  const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
+__global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
+  const long long idx = (long long)blockIdx.x * kScanThreads + threadIdx.x;
   if (idx >= (long long)a.B * a.H * D * D) return;
   const int e = (int)(idx % (D * D));
   const long long bh = idx / (D * D);
@@ -221,23 +272,29 @@ __global__ __launch_bounds__(kThreads) void lin_scan_kernel(LinArgs a) {
 // Phase 3: per (b*H + h, chunk): Y = I + at I + Qt Cin, with
 //   at[t][j] = S_t S_j sum_r q_{t,r} k_{j,r} e^{b_{t,r} - b_{j,r}}  (j < t),
 //   Qt[t][r] = S_t q_{t,r} e^{b_{t,r}}.
-// at is built per 16-row sub-block pair: off the diagonal (tb > jb) the decay
-// factors through the reference row R = 16 jb + 15 (j <= R < t), as
-// e^{b_t - b_R} e^{b_R - b_j} with both exponents <= 0, and the sum over r runs
-// on v_mfma_f32_16x16x4_f32; the four diagonal blocks take the exact
-// per-element exponentials. The output is one v_mfma_f32_32x32x2_f32
-// accumulation over j (at I) and r (Qt Cin). LDS arrays are stored
-// channel-major ([r][t], rows padded to 65 floats) so that every operand read
-// and transposing write is conflict-free.
+// at is built per 16-row sub-block pair on v_mfma_f32_16x16x4_f32, the decay
+// factored through a reference row R as e^{b_t - b_R} e^{b_R - b_j}: off the
+// diagonal (tb > jb) R = 16 jb + 15 (j <= R < t, both exponents <= 0); on the
+// diagonal R is the block's middle row, which keeps every exponent within
+// +-40 unless the retention falls by more than e^-40 within 8 tokens on some
+// channel; such a block takes the exact per-element exponentials instead.
+// The output is one v_mfma_f32_32x32x2_f32 accumulation over j (at I) and r
+// (Qt Cin) per 32 x 32 tile, one tile per wave, with its column of Cin loaded
+// into registers at the start. LDS arrays are stored channel-major ([r][t],
+// rows padded to 65 floats) so that the operand reads and transposing writes
+// are conflict-free.
 template <typename Tin, int D>
-__global__ __launch_bounds__(kThreads) void lin_out_kernel(LinArgs a, HeadParams hp) {
+__global__ __launch_bounds__(kOutThreads) void lin_out_kernel(LinArgs a, HeadParams hp) {
+  constexpr int NT = kOutThreads;
+  constexpr int kW = NT / 64;
   constexpr int kP = kL + 1;      // padded row length of the channel-major arrays
-  __shared__ float qT[D][kP];     // S_t q_{t,r}
+  __shared__ float qT[D][kP];     // S_t q_{t,r}, then S_t q_{t,r} e^{b_{t,r}}
   __shared__ float kT[D][kP];     // S_j k_{j,r}
   __shared__ float bT[D][kP];     // b_{t,r}
   __shared__ float it[kL][D];     // I_j
-  __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t]
+  __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t] (the prefix's scratch before)
   __shared__ float s[kL], n1[kL], n2[kL];
+  static_assert(kL * kP >= NT, "prefix scratch fits in atT");
   const int nc = (a.T + kL - 1) / kL;
   const int c = blockIdx.x % nc;
   const int bh = blockIdx.x / nc;
@@ -247,92 +304,122 @@ __global__ __launch_bounds__(kThreads) void lin_out_kernel(LinArgs a, HeadParams
   const size_t base = ((size_t)bh * a.T + t0) * D;
   Tin* Y = static_cast<Tin*>(a.Y) + base;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, lh = lane >> 5;
+  constexpr int kTN = D / 32;
+  const bool has_tile = wave < 2 * kTN;              // output tile (m, n) of this wave
+  const int n_out = wave % kTN, m_out = wave / kTN;
 
-  stage_rows<Tin, D, true>(static_cast<const Tin*>(a.P1) + base, rows, &qT[0][0], kP);
-  stage_rows<Tin, D, true>(static_cast<const Tin*>(a.P2) + base, rows, &kT[0][0], kP);
-  stage_rows<Tin, D, false>(static_cast<const Tin*>(a.I) + base, rows, &it[0][0], D);
-  stage_rows<float, D, true>(a.alpha + base, rows, &bT[0][0], kP);
+  // The wave's column of Cin (B[r][col], r = 2 ks + lh) and the chunk's rows,
+  // all loads issued before any is used.
+  const float* cin = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
+  float cf[D / 2];
+  if (has_tile) {
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + 32 * n_out + l32];
+  }
+  {
+    Staged<NT, Tin, D> g1, g2, gi;
+    Staged<NT, float, D> ga;
+    g1.load(static_cast<const Tin*>(a.P1) + base, rows);
+    g2.load(static_cast<const Tin*>(a.P2) + base, rows);
+    gi.load(static_cast<const Tin*>(a.I) + base, rows);
+    ga.load(a.alpha + base, rows);
+    g1.template store<true>(&qT[0][0], kP);
+    g2.template store<true>(&kT[0][0], kP);
+    gi.template store<false>(&it[0][0], D);
+    ga.template store<true>(&bT[0][0], kP);
+  }
   __syncthreads();
-  row_stats<D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
-  decay_prefix<D>(&bT[0][0], 1, kP, rows);
+  row_stats<NT, D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
+  decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0]);
   __syncthreads();
-  for (int e = threadIdx.x; e < kL * D; e += kThreads) {
+  for (int e = threadIdx.x; e < kL * D; e += NT) {
     const int r = e / kL, t = e % kL;
     qT[r][t] *= s[t] * n1[t];
     kT[r][t] *= s[t] * n2[t];
   }
   __syncthreads();
 
-  // Off-diagonal sub-block pairs (tb, jb), tb > jb: 6 pairs.
+  // Sub-block tasks: 6 pairs below the diagonal, then the 4 diagonal blocks.
   {
     constexpr int kPairT[6] = {1, 2, 3, 2, 3, 3};
     constexpr int kPairJ[6] = {0, 0, 0, 1, 1, 2};
     const int l16 = lane & 15, lq = lane >> 4;
-    for (int p = wave; p < 6; p += kThreads / 64) {
-      const int tb = kPairT[p], jb = kPairJ[p];
-      const int t = 16 * tb + l16, j = 16 * jb + l16, R = 16 * jb + 15;
-      f32x4 acc = {};
-#pragma unroll 4
-      for (int ks = 0; ks < D / 4; ++ks) {
-        const int r = 4 * ks + lq;
-        const float ref = bT[r][R];
-        const float av = qT[r][t] * __expf(bT[r][t] - ref);
-        const float bv = kT[r][j] * __expf(ref - bT[r][j]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    for (int p = wave; p < 10; p += kW) {
+      const bool diag = p >= 6;
+      const int tb = diag ? p - 6 : kPairT[p];
+      const int jb = diag ? p - 6 : kPairJ[p];
+      const int R = diag ? 16 * tb + 7 : 16 * jb + 15;
+      bool factor = true;
+      if (diag) {
+        // b is non-increasing in t, so the extreme exponents are those of the
+        // block's first and last rows.
+        int ok = 1;
+        for (int r = lane; r < D; r += 64) {
+          const float br = bT[r][R];
+          ok &= (bT[r][16 * tb] - br <= kFactorBound) & (br - bT[r][16 * tb + 15] <= kFactorBound);
+        }
+        factor = __all(ok);
       }
-      // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16.
+      if (factor) {
+        const int t = 16 * tb + l16, j = 16 * jb + l16;
+        f32x4 acc = {};
+#pragma unroll 4
+        for (int ks = 0; ks < D / 4; ++ks) {
+          const int r = 4 * ks + lq;
+          const float ref = bT[r][R];
+          const float av = qT[r][t] * __expf(bT[r][t] - ref);
+          const float bv = kT[r][j] * __expf(ref - bT[r][j]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+        }
+        // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16; on the
+        // diagonal only j < t is history.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atT[16 * jb + l16][16 * tb + 4 * lq + i] = acc[i];
+        for (int i = 0; i < 4; ++i)
+          atT[16 * jb + l16][16 * tb + 4 * lq + i] = (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f;
+      } else {
+        for (int e = lane; e < 256; e += 64) {
+          const int tl = e >> 4, jl = e & 15;
+          const int t = 16 * tb + tl, j = 16 * tb + jl;
+          float acc = 0.0f;
+          if (jl < tl) {
+            for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
+          }
+          atT[j][t] = acc;
+        }
+      }
     }
   }
-  // Diagonal blocks (exact) and the zero blocks above the diagonal.
-  for (int e = threadIdx.x; e < 4 * 256; e += kThreads) {
-    const int blk = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
-    const int t = 16 * blk + tl, j = 16 * blk + jl;
-    float acc = 0.0f;
-    if (jl < tl) {
-      for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
-    }
-    atT[j][t] = acc;
-  }
-  for (int e = threadIdx.x; e < 6 * 256; e += kThreads) {
+  // The zero blocks above the diagonal.
+  for (int e = threadIdx.x; e < 6 * 256; e += NT) {
     constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
     constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
     const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
     atT[16 * kUpJ[p] + jl][16 * kUpT[p] + tl] = 0.0f;
   }
   __syncthreads();
+  // Qt = S q o e^{b} in place (every exponent <= 0).
+  for (int e = threadIdx.x; e < kL * D; e += NT) {
+    const int r = e / kL, t = e % kL;
+    qT[r][t] *= __expf(bT[r][t]);
+  }
+  __syncthreads();
 
-  // Y tiles (m, n): rows 32 m .., columns 32 n ..; a wave takes column block
-  // n for both row blocks, with its column of Cin preloaded into registers.
-  const int l32 = lane & 31, lh = lane >> 5;
-  constexpr int kTN = D / 32;
-  const float* cin = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
-  for (int n = wave; n < kTN; n += kThreads / 64) {
-    const int col = 32 * n + l32;
-    float cf[D / 2];
-#pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + col];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int t = 32 * m + l32;
-      f32x16 acc = {};
+  // Y tile (m, n): rows 32 m .., columns 32 n ...
+  if (has_tile) {
+    const int col = 32 * n_out + l32, t = 32 * m_out + l32;
+    f32x16 acc = {};
 #pragma unroll 8
-      for (int ks = 0; ks < kL / 2; ++ks) {
-        const int j = 2 * ks + lh;
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(atT[j][t], it[j][col], acc, 0, 0, 0);
-      }
+    for (int ks = 0; ks < kL / 2; ++ks) {
+      const int j = 2 * ks + lh;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(atT[j][t], it[j][col], acc, 0, 0, 0);
+    }
+#pragma unroll 8
+    for (int ks = 0; ks < D / 2; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qT[2 * ks + lh][t], cf[ks], acc, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < D / 2; ++ks) {
-        const int r = 2 * ks + lh;
-        const float qv = qT[r][t] * __expf(bT[r][t]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, cf[ks], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = 32 * m + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int tr = 32 * m_out + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
     }
   }
 }
@@ -342,11 +429,11 @@ hipError_t launch_typed(const LinArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nc = (a.T + kL - 1) / kL;
   const long long wg = (long long)a.B * a.H * nc;
   const long long scan_threads = (long long)a.B * a.H * D * D;
-  if (wg > 0x7fffffffLL || (scan_threads + kThreads - 1) / kThreads > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((lin_chunk_kernel<Tin, D>), dim3((unsigned)wg), dim3(kThreads), 0, s, a, hp);
-  hipLaunchKernelGGL((lin_scan_kernel<D>), dim3((unsigned)((scan_threads + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)wg), dim3(kThreads), 0, s, a, hp);
+  if (wg > 0x7fffffffLL || (scan_threads + kScanThreads - 1) / kScanThreads > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((lin_chunk_kernel<Tin, D>), dim3((unsigned)wg), dim3(kChunkThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((lin_scan_kernel<D>), dim3((unsigned)((scan_threads + kScanThreads - 1) / kScanThreads)),
+                     dim3(kScanThreads), 0, s, a);
+  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)wg), dim3(kOutThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 
