@@ -83,6 +83,30 @@ struct Staged {
   }
 };
 
+// Runs mma(ks, op) for ks = 0 .. KS-1 with the LDS operands of each group of
+// G k-steps fetched by load(ks, op) while the previous group's MFMAs run (the
+// scheduling barriers keep the compiler from trading that overlap for
+// registers). Fully unrolled: every index is a compile-time constant.
+template <int KS, int G, typename Op, typename Load, typename Mma>
+__device__ __forceinline__ void pipelined(Load load, Mma mma) {
+  static_assert(KS % G == 0, "whole groups");
+  constexpr int NG = KS / G;
+  Op op[2][G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) load(u, op[0][u]);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g + 1 < NG) {
+#pragma unroll
+      for (int u = 0; u < G; ++u) load(G * (g + 1) + u, op[(g + 1) & 1][u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < G; ++u) mma(G * g + u, op[g & 1][u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Row statistics from LDS copies of P1 and P2 (element (t, r) at
 // p[t * rs + r * cs]): S_t into s[], reciprocal row norms into n1[], n2[].
 // Each wave takes kL / waves rows at once, so the cross-lane reductions of
@@ -191,16 +215,18 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   constexpr int kNPerWave = (kT + 3) / 4;            // column blocks per wave (ceil)
 
   // I operands (B[j][col] = I_j[col], j = 2 ks + lh) of this wave's column
-  // blocks: issued first, consumed last.
+  // blocks: issued first, consumed last. Rows past the chunk's end read the
+  // last row (an address inside the tensor) and are zeroed afterwards, so
+  // no load sits behind a per-lane branch.
   float bf[kNPerWave][kL / 2];
 #pragma unroll
   for (int q = 0; q < kNPerWave; ++q) {
     const int n = wave + 4 * q;
+    if (n >= kT) break;
 #pragma unroll
-    for (int ks = 0; ks < kL / 2; ++ks) {
-      const int j = 2 * ks + lh;
-      bf[q][ks] = (n < kT && j < rows) ? ld_val(I, (size_t)j * D + 32 * n + l32) : 0.0f;
-    }
+    for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
+#pragma unroll
+    for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
   }
   {
     Staged<NT, Tin, D> g1, g2;
@@ -231,13 +257,16 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
     f32x16 acc[kT];
 #pragma unroll
     for (int m = 0; m < kT; ++m) acc[m] = f32x16{};
-#pragma unroll 4
-    for (int ks = 0; ks < kL / 2; ++ks) {
-      const int j = 2 * ks + lh;
+    struct Op { float a[kT]; };
+    pipelined<kL / 2, 4, Op>(
+        [&](int ks, Op& o) {
 #pragma unroll
-      for (int m = 0; m < kT; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[j][32 * m + l32], bf[q][ks], acc[m], 0, 0, 0);
-    }
+          for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
+        },
+        [&](int ks, const Op& o) {
+#pragma unroll
+          for (int m = 0; m < kT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[m], 0, 0, 0);
+        });
 #pragma unroll
     for (int m = 0; m < kT; ++m)
 #pragma unroll
@@ -284,7 +313,7 @@ __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
 // rows padded to 65 floats) so that the operand reads and transposing writes
 // are conflict-free.
 template <typename Tin, int D>
-__global__ __launch_bounds__(kOutThreads) void lin_out_kernel(LinArgs a, HeadParams hp) {
+__global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void lin_out_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kOutThreads;
   constexpr int kW = NT / 64;
   constexpr int kP = kL + 1;      // padded row length of the channel-major arrays
@@ -409,13 +438,15 @@ __global__ __launch_bounds__(kOutThreads) void lin_out_kernel(LinArgs a, HeadPar
   if (has_tile) {
     const int col = 32 * n_out + l32, t = 32 * m_out + l32;
     f32x16 acc = {};
-#pragma unroll 8
-    for (int ks = 0; ks < kL / 2; ++ks) {
-      const int j = 2 * ks + lh;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(atT[j][t], it[j][col], acc, 0, 0, 0);
-    }
-#pragma unroll 8
-    for (int ks = 0; ks < D / 2; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qT[2 * ks + lh][t], cf[ks], acc, 0, 0, 0);
+    struct Op2 { float a, b; };
+    pipelined<kL / 2, 8, Op2>(
+        [&](int ks, Op2& o) {
+          o.a = atT[2 * ks + lh][t];
+          o.b = it[2 * ks + lh][col];
+        },
+        [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
+    pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
+                               [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = 32 * m_out + 8 * (r >> 2) + 4 * lh + (r & 3);
