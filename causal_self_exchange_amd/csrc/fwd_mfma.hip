@@ -592,27 +592,34 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kBM - 1) / kBM;
   const long long nwork = (long long)((nq + 1) / 2) * a.B * a.H;
   if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
-  // One persistent work-group per compute unit (the LDS rings admit one). The
-  // count is cached per device; concurrent first calls store the same value.
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  // One persistent work-group per compute unit (the LDS rings admit one).
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int n_cu = cus[dev].load(std::memory_order_relaxed);
-  if (n_cu == 0) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    n_cu = n > 0 ? n : 1;
-    cus[dev].store(n_cu, std::memory_order_relaxed);
-  }
   const long long grid = nwork < n_cu ? nwork : n_cu;
   hipLaunchKernelGGL((fwd_mfma_kernel<D, DR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t device_cu_count(int* n_cu) {
+  // Cached per device; concurrent first calls store the same value.
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    n = n > 0 ? n : 1;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *n_cu = n;
+  return hipSuccess;
+}
 
 bool fwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including

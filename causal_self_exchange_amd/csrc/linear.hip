@@ -38,8 +38,9 @@ typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 template <typename Tin>
 __device__ __forceinline__ float ld_val(const Tin* p, size_t i) { return to_f32(p[i]); }
 
-// A chunk's rows (rows >= `rows` give 0) in registers: NT threads issue every
-// 16-byte load before any is used, so one memory latency covers the chunk.
+// A chunk's rows (rows >= `rows` give 0) in registers: NT threads (tid = the
+// thread's index) issue every 16-byte load before any is used, so one memory
+// latency covers the chunk.
 template <int NT, typename Tin, int D>
 struct Staged {
   static constexpr int kVec = 16 / (int)sizeof(Tin);   // elements per 16-byte load
@@ -48,20 +49,20 @@ struct Staged {
   static_assert(kL * D % kVec == 0, "whole loads per row");
   u32x4v v[kN];
 
-  __device__ __forceinline__ void load(const Tin* src, int rows) {
+  __device__ __forceinline__ void load(const Tin* src, int rows, int tid) {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int idx = threadIdx.x + i * NT, e = idx * kVec;
+      const int idx = tid + i * NT, e = idx * kVec;
       v[i] = (idx < kTot && e / D < rows) ? *reinterpret_cast<const u32x4v*>(src + e) : u32x4v{0u, 0u, 0u, 0u};
     }
   }
   // Into an fp32 LDS array, row-major [t][r] (ld = row stride) or
   // channel-major [r][t].
   template <bool kChannelMajor>
-  __device__ __forceinline__ void store(float* dst, int ld) const {
+  __device__ __forceinline__ void store(float* dst, int ld, int tid) const {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int idx = threadIdx.x + i * NT, e = idx * kVec;
+      const int idx = tid + i * NT, e = idx * kVec;
       if (idx >= kTot) break;
       const int t = e / D, r0 = e % D;
       float x[kVec];
@@ -113,10 +114,10 @@ __device__ __forceinline__ void pipelined(Load load, Mma mma) {
 // all its rows are independent of one another.
 template <int NT, int D>
 __device__ __forceinline__ void row_stats(const float* p1, const float* p2, int rs, int cs, int rows, float inv_scale,
-                                          float* s, float* n1, float* n2) {
+                                          float* s, float* n1, float* n2, int tid) {
   constexpr int kW = NT / 64;
   constexpr int kRows = kL / kW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float d12[kRows], d11[kRows], d22[kRows];
 #pragma unroll
   for (int k = 0; k < kRows; ++k) {
@@ -165,11 +166,11 @@ __device__ __forceinline__ void row_stats(const float* p1, const float* p2, int 
 // sum, then adds the totals of the earlier segments (in order). `tot` is NT
 // floats of LDS scratch. Contains a barrier: every thread must call it.
 template <int NT, int D>
-__device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows, float* tot) {
+__device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows, float* tot, int tid) {
   constexpr int kSeg = NT / D;
   constexpr int kLen = kL / kSeg;
   static_assert(NT % D == 0 && kL % kSeg == 0, "whole segments");
-  const int r = threadIdx.x % D, seg = threadIdx.x / D, t0 = seg * kLen;
+  const int r = tid % D, seg = tid / D, t0 = seg * kLen;
   float x[kLen];
 #pragma unroll
   for (int i = 0; i < kLen; ++i) x[i] = b[(t0 + i) * rs + r * cs];
@@ -230,19 +231,19 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   }
   {
     Staged<NT, Tin, D> g1, g2;
-    g1.load(static_cast<const Tin*>(a.P1) + base, rows);
-    g2.load(static_cast<const Tin*>(a.P2) + base, rows);
-    g1.template store<false>(&bt[0][0], D);
-    g2.template store<false>(&kt[0][0], D);
+    g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
+    g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
+    g1.template store<false>(&bt[0][0], D, threadIdx.x);
+    g2.template store<false>(&kt[0][0], D, threadIdx.x);
   }
   Staged<NT, float, D> ga;
-  ga.load(a.alpha + base, rows);
+  ga.load(a.alpha + base, rows, threadIdx.x);
   __syncthreads();
-  row_stats<NT, D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
+  row_stats<NT, D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2, threadIdx.x);
   __syncthreads();
-  ga.template store<false>(&bt[0][0], D);
+  ga.template store<false>(&bt[0][0], D, threadIdx.x);
   __syncthreads();
-  decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot);
+  decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
   __syncthreads();
   for (int e = threadIdx.x; e < kL * D; e += NT) {
     const int t = e / D, r = e % D;
@@ -308,10 +309,18 @@ __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
 // +-40 unless the retention falls by more than e^-40 within 8 tokens on some
 // channel; such a block takes the exact per-element exponentials instead.
 // The output is one v_mfma_f32_32x32x2_f32 accumulation over j (at I) and r
-// (Qt Cin) per 32 x 32 tile, one tile per wave, with its column of Cin loaded
-// into registers at the start. LDS arrays are stored channel-major ([r][t],
-// rows padded to 65 floats) so that the operand reads and transposing writes
-// are conflict-free.
+// (Qt Cin) per 32 x 32 tile, one tile per wave, with its column of Cin in
+// registers. LDS arrays are stored channel-major ([r][t], rows padded to 65
+// floats) so that the operand reads and transposing writes are conflict-free.
+// Persistent: a work-group takes chunks blockIdx.x + k gridDim.x, and the
+// next chunk's rows are loaded into registers while the current one is
+// computed (its Cin column, needed last, is loaded at the iteration's start).
+template <typename Tin, int D>
+struct OutPrefetch {
+  Staged<kOutThreads, Tin, D> p1, p2, in;
+  Staged<kOutThreads, float, D> al;
+};
+
 template <typename Tin, int D>
 __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void lin_out_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kOutThreads;
@@ -325,133 +334,154 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ float s[kL], n1[kL], n2[kL];
   static_assert(kL * kP >= NT, "prefix scratch fits in atT");
   const int nc = (a.T + kL - 1) / kL;
-  const int c = blockIdx.x % nc;
-  const int bh = blockIdx.x / nc;
-  const int h = bh % a.H;
-  const int t0 = c * kL;
-  const int rows = min(kL, a.T - t0);
-  const size_t base = ((size_t)bh * a.T + t0) * D;
-  Tin* Y = static_cast<Tin*>(a.Y) + base;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l32 = lane & 31, lh = lane >> 5;
+  const int total = a.B * a.H * nc;
   constexpr int kTN = D / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool has_tile = wave < 2 * kTN;              // output tile (m, n) of this wave
   const int n_out = wave % kTN, m_out = wave / kTN;
+  // Lane-dependent indices are re-formed from an opaque copy of threadIdx.x
+  // in every iteration of the chunk loop: otherwise the compiler hoists every
+  // unrolled LDS address out of the loop and runs out of registers.
+  int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
 
-  // The wave's column of Cin (B[r][col], r = 2 ks + lh) and the chunk's rows,
-  // all loads issued before any is used.
-  const float* cin = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
-  float cf[D / 2];
-  if (has_tile) {
-#pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + 32 * n_out + l32];
-  }
-  {
-    Staged<NT, Tin, D> g1, g2, gi;
-    Staged<NT, float, D> ga;
-    g1.load(static_cast<const Tin*>(a.P1) + base, rows);
-    g2.load(static_cast<const Tin*>(a.P2) + base, rows);
-    gi.load(static_cast<const Tin*>(a.I) + base, rows);
-    ga.load(a.alpha + base, rows);
-    g1.template store<true>(&qT[0][0], kP);
-    g2.template store<true>(&kT[0][0], kP);
-    gi.template store<false>(&it[0][0], D);
-    ga.template store<true>(&bT[0][0], kP);
-  }
-  __syncthreads();
-  row_stats<NT, D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2);
-  decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0]);
-  __syncthreads();
-  for (int e = threadIdx.x; e < kL * D; e += NT) {
-    const int r = e / kL, t = e % kL;
-    qT[r][t] *= s[t] * n1[t];
-    kT[r][t] *= s[t] * n2[t];
-  }
-  __syncthreads();
+  // Loads of chunk g's rows (global index g = bh * nc + c) into registers.
+  auto fetch = [&](int g, OutPrefetch<Tin, D>& f) __attribute__((always_inline)) {
+    const int c = g % nc, bh = g / nc;
+    const int rows = min(kL, a.T - c * kL);
+    const size_t base = ((size_t)bh * a.T + (size_t)c * kL) * D;
+    f.p1.load(static_cast<const Tin*>(a.P1) + base, rows, tid);
+    f.p2.load(static_cast<const Tin*>(a.P2) + base, rows, tid);
+    f.in.load(static_cast<const Tin*>(a.I) + base, rows, tid);
+    f.al.load(a.alpha + base, rows, tid);
+  };
 
-  // Sub-block tasks: 6 pairs below the diagonal, then the 4 diagonal blocks.
-  {
-    constexpr int kPairT[6] = {1, 2, 3, 2, 3, 3};
-    constexpr int kPairJ[6] = {0, 0, 0, 1, 1, 2};
-    const int l16 = lane & 15, lq = lane >> 4;
-    for (int p = wave; p < 10; p += kW) {
-      const bool diag = p >= 6;
-      const int tb = diag ? p - 6 : kPairT[p];
-      const int jb = diag ? p - 6 : kPairJ[p];
-      const int R = diag ? 16 * tb + 7 : 16 * jb + 15;
-      bool factor = true;
-      if (diag) {
-        // b is non-increasing in t, so the extreme exponents are those of the
-        // block's first and last rows.
-        int ok = 1;
-        for (int r = lane; r < D; r += 64) {
-          const float br = bT[r][R];
-          ok &= (bT[r][16 * tb] - br <= kFactorBound) & (br - bT[r][16 * tb + 15] <= kFactorBound);
-        }
-        factor = __all(ok);
-      }
-      if (factor) {
-        const int t = 16 * tb + l16, j = 16 * jb + l16;
-        f32x4 acc = {};
-#pragma unroll 4
-        for (int ks = 0; ks < D / 4; ++ks) {
-          const int r = 4 * ks + lq;
-          const float ref = bT[r][R];
-          const float av = qT[r][t] * __expf(bT[r][t] - ref);
-          const float bv = kT[r][j] * __expf(ref - bT[r][j]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-        }
-        // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16; on the
-        // diagonal only j < t is history.
+  OutPrefetch<Tin, D> nx;
+  if ((int)blockIdx.x < total) fetch(blockIdx.x, nx);
+  for (int g = blockIdx.x; g < total; g += gridDim.x) {
+    tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    l32 = lane & 31;
+    lh = lane >> 5;
+    const int c = g % nc, bh = g / nc;
+    const int h = bh % a.H;
+    const int rows = min(kL, a.T - c * kL);
+    Tin* Y = static_cast<Tin*>(a.Y) + ((size_t)bh * a.T + (size_t)c * kL) * D;
+    // The previous chunk's LDS is free (the barrier that ends its iteration).
+    nx.p1.template store<true>(&qT[0][0], kP, tid);
+    nx.p2.template store<true>(&kT[0][0], kP, tid);
+    nx.in.template store<false>(&it[0][0], D, tid);
+    nx.al.template store<true>(&bT[0][0], kP, tid);
+    float cf[D / 2];
+    if (has_tile) {
+      const float* cin = a.state + (size_t)g * D * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atT[16 * jb + l16][16 * tb + 4 * lq + i] = (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f;
-      } else {
-        for (int e = lane; e < 256; e += 64) {
-          const int tl = e >> 4, jl = e & 15;
-          const int t = 16 * tb + tl, j = 16 * tb + jl;
-          float acc = 0.0f;
-          if (jl < tl) {
-            for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
+      for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + 32 * n_out + l32];
+    }
+    if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
+    __syncthreads();
+    row_stats<NT, D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
+    decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0], tid);
+    __syncthreads();
+    for (int e = tid; e < kL * D; e += NT) {
+      const int r = e / kL, t = e % kL;
+      qT[r][t] *= s[t] * n1[t];
+      kT[r][t] *= s[t] * n2[t];
+    }
+    __syncthreads();
+
+    // Sub-block tasks: 6 pairs below the diagonal, then the 4 diagonal blocks.
+    {
+      constexpr int kPairT[6] = {1, 2, 3, 2, 3, 3};
+      constexpr int kPairJ[6] = {0, 0, 0, 1, 1, 2};
+      const int l16 = lane & 15, lq = lane >> 4;
+      for (int p = wave; p < 10; p += kW) {
+        const bool diag = p >= 6;
+        const int tb = diag ? p - 6 : kPairT[p];
+        const int jb = diag ? p - 6 : kPairJ[p];
+        const int R = diag ? 16 * tb + 7 : 16 * jb + 15;
+        bool factor = true;
+        if (diag) {
+          // b is non-increasing in t, so the extreme exponents are those of
+          // the block's first and last rows.
+          int ok = 1;
+          for (int r = lane; r < D; r += 64) {
+            const float br = bT[r][R];
+            ok &= (bT[r][16 * tb] - br <= kFactorBound) & (br - bT[r][16 * tb + 15] <= kFactorBound);
           }
-          atT[j][t] = acc;
+          factor = __all(ok);
+        }
+        if (factor) {
+          const int t = 16 * tb + l16, j = 16 * jb + l16;
+          f32x4 acc = {};
+          struct OpAt { float ref, q, bq, k, bk; };
+          pipelined<D / 4, 8, OpAt>(
+              [&](int ks, OpAt& o) {
+                const int r = 4 * ks + lq;
+                o.ref = bT[r][R];
+                o.q = qT[r][t];
+                o.bq = bT[r][t];
+                o.k = kT[r][j];
+                o.bk = bT[r][j];
+              },
+              [&](int ks, const OpAt& o) {
+                const float av = o.q * __expf(o.bq - o.ref);
+                const float bv = o.k * __expf(o.ref - o.bk);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+              });
+          // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16; on the
+          // diagonal only j < t is history.
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            atT[16 * jb + l16][16 * tb + 4 * lq + i] = (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f;
+        } else {
+          for (int e = lane; e < 256; e += 64) {
+            const int tl = e >> 4, jl = e & 15;
+            const int t = 16 * tb + tl, j = 16 * tb + jl;
+            float acc = 0.0f;
+            if (jl < tl) {
+              for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
+            }
+            atT[j][t] = acc;
+          }
         }
       }
     }
-  }
-  // The zero blocks above the diagonal.
-  for (int e = threadIdx.x; e < 6 * 256; e += NT) {
-    constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
-    constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
-    const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
-    atT[16 * kUpJ[p] + jl][16 * kUpT[p] + tl] = 0.0f;
-  }
-  __syncthreads();
-  // Qt = S q o e^{b} in place (every exponent <= 0).
-  for (int e = threadIdx.x; e < kL * D; e += NT) {
-    const int r = e / kL, t = e % kL;
-    qT[r][t] *= __expf(bT[r][t]);
-  }
-  __syncthreads();
-
-  // Y tile (m, n): rows 32 m .., columns 32 n ...
-  if (has_tile) {
-    const int col = 32 * n_out + l32, t = 32 * m_out + l32;
-    f32x16 acc = {};
-    struct Op2 { float a, b; };
-    pipelined<kL / 2, 8, Op2>(
-        [&](int ks, Op2& o) {
-          o.a = atT[2 * ks + lh][t];
-          o.b = it[2 * ks + lh][col];
-        },
-        [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
-    pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
-                               [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = 32 * m_out + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
+    // The zero blocks above the diagonal.
+    for (int e = tid; e < 6 * 256; e += NT) {
+      constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
+      constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
+      const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
+      atT[16 * kUpJ[p] + jl][16 * kUpT[p] + tl] = 0.0f;
     }
+    __syncthreads();
+    // Qt = S q o e^{b} in place (every exponent <= 0).
+    for (int e = tid; e < kL * D; e += NT) {
+      const int r = e / kL, t = e % kL;
+      qT[r][t] *= __expf(bT[r][t]);
+    }
+    __syncthreads();
+
+    // Y tile (m, n): rows 32 m .., columns 32 n ...
+    if (has_tile) {
+      const int col = 32 * n_out + l32, t = 32 * m_out + l32;
+      f32x16 acc = {};
+      struct Op2 { float a, b; };
+      pipelined<kL / 2, 8, Op2>(
+          [&](int ks, Op2& o) {
+            o.a = atT[2 * ks + lh][t];
+            o.b = it[2 * ks + lh][col];
+          },
+          [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
+      pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
+                                 [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = 32 * m_out + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -461,10 +491,15 @@ hipError_t launch_typed(const LinArgs& a, const HeadParams& hp, hipStream_t s) {
   const long long wg = (long long)a.B * a.H * nc;
   const long long scan_threads = (long long)a.B * a.H * D * D;
   if (wg > 0x7fffffffLL || (scan_threads + kScanThreads - 1) / kScanThreads > 0x7fffffffLL) return hipErrorInvalidValue;
+  // The output kernel is persistent: one work-group per compute unit (its LDS
+  // admits one).
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((lin_chunk_kernel<Tin, D>), dim3((unsigned)wg), dim3(kChunkThreads), 0, s, a, hp);
   hipLaunchKernelGGL((lin_scan_kernel<D>), dim3((unsigned)((scan_threads + kScanThreads - 1) / kScanThreads)),
                      dim3(kScanThreads), 0, s, a);
-  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)wg), dim3(kOutThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)(wg < n_cu ? wg : n_cu)), dim3(kOutThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 

@@ -113,6 +113,9 @@ constexpr int kDecodeChunk = 256;
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
+// Compute units of the current device (queried once per device, then cached:
+// the library's only global state).
+hipError_t device_cu_count(int* n_cu);
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s);
 bool fwd_mfma_supported(int d_h, int T);
 // Backward: prep (row statistics, dtau / dlambda partials) then the query and
