@@ -156,6 +156,39 @@ __device__ __forceinline__ void row_stats(const float* p1, const float* p2, int 
   }
 }
 
+// The same statistics from channel-major LDS copies (element (t, r) at
+// p[r * ld + t]): NT / kL adjacent threads share a row, each summing a
+// contiguous run of channels, then reduce across their lanes (a few shuffles
+// instead of a full wave reduction per row).
+template <int NT, int D>
+__device__ __forceinline__ void row_stats_cm(const float* p1, const float* p2, int ld, int rows, float inv_scale,
+                                             float* s, float* n1, float* n2, int tid) {
+  constexpr int kPer = NT / kL;                     // threads per row
+  constexpr int kRun = D / kPer;                    // channels per thread
+  static_assert(NT % kL == 0 && D % kPer == 0 && kPer <= 64, "whole runs");
+  const int t = tid / kPer, part = tid % kPer;
+  float d12 = 0.0f, d11 = 0.0f, d22 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int r = part * kRun + i;
+    const float a = p1[r * ld + t], b = p2[r * ld + t];
+    d12 = fmaf(a, b, d12);
+    d11 = fmaf(a, a, d11);
+    d22 = fmaf(b, b, d22);
+  }
+#pragma unroll
+  for (int w = kPer / 2; w >= 1; w >>= 1) {
+    d12 += __shfl_xor(d12, w, kPer);
+    d11 += __shfl_xor(d11, w, kPer);
+    d22 += __shfl_xor(d22, w, kPer);
+  }
+  if (part == 0) {
+    s[t] = t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
+    n1[t] = d11 > 0.0f ? 1.0f / sqrtf(d11) : 0.0f;
+    n2[t] = d22 > 0.0f ? 1.0f / sqrtf(d22) : 0.0f;
+  }
+}
+
 // In-place inclusive per-channel prefix of log alpha over the chunk (element
 // (t, r) at b[t * rs + r * cs], holding alpha on entry; rows >= `rows` repeat
 // the last value). alpha is clamped to [1e-30, 1] (NaN to 1e-30): log alpha
@@ -380,7 +413,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
     __syncthreads();
-    row_stats<NT, D>(&qT[0][0], &kT[0][0], 1, kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
+    row_stats_cm<NT, D>(&qT[0][0], &kT[0][0], kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
     decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0], tid);
     __syncthreads();
     for (int e = tid; e < kL * D; e += NT) {
