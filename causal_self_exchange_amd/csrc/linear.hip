@@ -56,6 +56,18 @@ struct Staged {
       v[i] = (idx < kTot && e / D < rows) ? *reinterpret_cast<const u32x4v*>(src + e) : u32x4v{0u, 0u, 0u, 0u};
     }
   }
+  // Load i as fp32: row (tid + i NT) / (D / kVec), kVec consecutive channels.
+  __device__ __forceinline__ void unpack(int i, float (&x)[kVec]) const {
+    if constexpr (sizeof(Tin) == 2) {
+      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+      const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) x[u] = (float)b[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) x[u] = __uint_as_float(v[i][u]);
+    }
+  }
   // Into an fp32 LDS array, row-major [t][r] (ld = row stride) or
   // channel-major [r][t].
   template <bool kChannelMajor>
@@ -66,15 +78,7 @@ struct Staged {
       if (idx >= kTot) break;
       const int t = e / D, r0 = e % D;
       float x[kVec];
-      if constexpr (sizeof(Tin) == 2) {
-        typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-        const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
-#pragma unroll
-        for (int u = 0; u < kVec; ++u) x[u] = (float)b[u];
-      } else {
-#pragma unroll
-        for (int u = 0; u < kVec; ++u) x[u] = __uint_as_float(v[i][u]);
-      }
+      unpack(i, x);
 #pragma unroll
       for (int u = 0; u < kVec; ++u) {
         if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u];
@@ -83,6 +87,45 @@ struct Staged {
     }
   }
 };
+
+// Row statistics of a chunk from its staged P1 and P2 rows: S_t into s[],
+// reciprocal row norms into n1[], n2[]. A row's D / kVec loads sit in
+// adjacent lanes, so each row takes a partial dot product per lane and a
+// short shuffle reduction; rows >= `rows` were loaded as zeros.
+template <int NT, typename Tin, int D>
+__device__ __forceinline__ void staged_row_stats(const Staged<NT, Tin, D>& g1, const Staged<NT, Tin, D>& g2, int rows,
+                                                 float inv_scale, float* s, float* n1, float* n2, int tid) {
+  using St = Staged<NT, Tin, D>;
+  constexpr int kLanes = D / St::kVec;              // lanes per row
+  static_assert(kLanes <= 64 && 64 % kLanes == 0 && NT % 64 == 0, "a row's loads share a wave");
+#pragma unroll
+  for (int i = 0; i < St::kN; ++i) {
+    const int idx = tid + i * NT;
+    float x[St::kVec], y[St::kVec];
+    g1.unpack(i, x);
+    g2.unpack(i, y);
+    float d12 = 0.0f, d11 = 0.0f, d22 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < St::kVec; ++u) {
+      d12 = fmaf(x[u], y[u], d12);
+      d11 = fmaf(x[u], x[u], d11);
+      d22 = fmaf(y[u], y[u], d22);
+    }
+#pragma unroll
+    for (int w = kLanes / 2; w >= 1; w >>= 1) {
+      d12 += __shfl_xor(d12, w, kLanes);
+      d11 += __shfl_xor(d11, w, kLanes);
+      d22 += __shfl_xor(d22, w, kLanes);
+    }
+    if (idx < St::kTot && idx % kLanes == 0) {
+      const int t = idx / kLanes;
+      s[t] = t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
+      // A zero row has no direction: its normalised coordinate is 0.
+      n1[t] = d11 > 0.0f ? 1.0f / sqrtf(d11) : 0.0f;
+      n2[t] = d22 > 0.0f ? 1.0f / sqrtf(d22) : 0.0f;
+    }
+  }
+}
 
 // Runs mma(ks, op) for ks = 0 .. KS-1 with the LDS operands of each group of
 // G k-steps fetched by load(ks, op) while the previous group's MFMAs run (the
@@ -105,87 +148,6 @@ __device__ __forceinline__ void pipelined(Load load, Mma mma) {
 #pragma unroll
     for (int u = 0; u < G; ++u) mma(G * g + u, op[g & 1][u]);
     __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Row statistics from LDS copies of P1 and P2 (element (t, r) at
-// p[t * rs + r * cs]): S_t into s[], reciprocal row norms into n1[], n2[].
-// Each wave takes kL / waves rows at once, so the cross-lane reductions of
-// all its rows are independent of one another.
-template <int NT, int D>
-__device__ __forceinline__ void row_stats(const float* p1, const float* p2, int rs, int cs, int rows, float inv_scale,
-                                          float* s, float* n1, float* n2, int tid) {
-  constexpr int kW = NT / 64;
-  constexpr int kRows = kL / kW;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float d12[kRows], d11[kRows], d22[kRows];
-#pragma unroll
-  for (int k = 0; k < kRows; ++k) {
-    const int t = wave + kW * k;
-    d12[k] = 0.0f;
-    d11[k] = 0.0f;
-    d22[k] = 0.0f;
-#pragma unroll
-    for (int r = lane; r < D; r += 64) {
-      const float a = p1[t * rs + r * cs], b = p2[t * rs + r * cs];
-      d12[k] = fmaf(a, b, d12[k]);
-      d11[k] = fmaf(a, a, d11[k]);
-      d22[k] = fmaf(b, b, d22[k]);
-    }
-  }
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1)
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      d12[k] += __shfl_xor(d12[k], w, 64);
-      d11[k] += __shfl_xor(d11[k], w, 64);
-      d22[k] += __shfl_xor(d22[k], w, 64);
-    }
-  if (lane < kRows) {
-    // Lane k writes row wave + kW k (a register array indexed by a uniform
-    // loop, so pick the lane's entry by comparison).
-    float a12 = 0.0f, a11 = 0.0f, a22 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kRows; ++k)
-      if (lane == k) { a12 = d12[k]; a11 = d11[k]; a22 = d22[k]; }
-    const int t = wave + kW * lane;
-    s[t] = t < rows ? sigmoid_f32(a12 * inv_scale) : 0.0f;
-    // A zero row has no direction: its normalised coordinate is 0.
-    n1[t] = a11 > 0.0f ? 1.0f / sqrtf(a11) : 0.0f;
-    n2[t] = a22 > 0.0f ? 1.0f / sqrtf(a22) : 0.0f;
-  }
-}
-
-// The same statistics from channel-major LDS copies (element (t, r) at
-// p[r * ld + t]): NT / kL adjacent threads share a row, each summing a
-// contiguous run of channels, then reduce across their lanes (a few shuffles
-// instead of a full wave reduction per row).
-template <int NT, int D>
-__device__ __forceinline__ void row_stats_cm(const float* p1, const float* p2, int ld, int rows, float inv_scale,
-                                             float* s, float* n1, float* n2, int tid) {
-  constexpr int kPer = NT / kL;                     // threads per row
-  constexpr int kRun = D / kPer;                    // channels per thread
-  static_assert(NT % kL == 0 && D % kPer == 0 && kPer <= 64, "whole runs");
-  const int t = tid / kPer, part = tid % kPer;
-  float d12 = 0.0f, d11 = 0.0f, d22 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kRun; ++i) {
-    const int r = part * kRun + i;
-    const float a = p1[r * ld + t], b = p2[r * ld + t];
-    d12 = fmaf(a, b, d12);
-    d11 = fmaf(a, a, d11);
-    d22 = fmaf(b, b, d22);
-  }
-#pragma unroll
-  for (int w = kPer / 2; w >= 1; w >>= 1) {
-    d12 += __shfl_xor(d12, w, kPer);
-    d11 += __shfl_xor(d11, w, kPer);
-    d22 += __shfl_xor(d22, w, kPer);
-  }
-  if (part == 0) {
-    s[t] = t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
-    n1[t] = d11 > 0.0f ? 1.0f / sqrtf(d11) : 0.0f;
-    n2[t] = d22 > 0.0f ? 1.0f / sqrtf(d22) : 0.0f;
   }
 }
 
@@ -226,14 +188,14 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
 // d_h x d_h x 64 product on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 out): a
 // wave owns column block n and all row blocks (independent accumulators that
 // share the I operand, which comes straight from global memory into
-// registers). LDS holds Kt and the decay prefix only (P1 passes through the
-// prefix buffer first; alpha waits in registers meanwhile), 66 KB at
-// d_h = 128, so two work-groups fit per CU.
+// registers). P1 is only needed for the row statistics, which come from the
+// staged registers; LDS holds Kt and the decay prefix, 66 KB at d_h = 128, so
+// two work-groups fit per CU.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kChunkThreads;
   __shared__ float kt[kL][D];     // p2_j, then S_j k_j e^{b_last - b_j}
-  __shared__ float bt[kL][D];     // p1_j, then alpha_j, then b_j
+  __shared__ float bt[kL][D];     // alpha_j, then b_j
   __shared__ float s[kL], n1[kL], n2[kL];
   __shared__ float tot[NT];
   const int nc = (a.T + kL - 1) / kL;
@@ -264,17 +226,14 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   }
   {
     Staged<NT, Tin, D> g1, g2;
+    Staged<NT, float, D> ga;
     g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
     g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
-    g1.template store<false>(&bt[0][0], D, threadIdx.x);
+    ga.load(a.alpha + base, rows, threadIdx.x);
+    staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], s, n1, n2, threadIdx.x);
     g2.template store<false>(&kt[0][0], D, threadIdx.x);
+    ga.template store<false>(&bt[0][0], D, threadIdx.x);
   }
-  Staged<NT, float, D> ga;
-  ga.load(a.alpha + base, rows, threadIdx.x);
-  __syncthreads();
-  row_stats<NT, D>(&bt[0][0], &kt[0][0], D, 1, rows, hp.scale * hp.inv_tau[h], s, n1, n2, threadIdx.x);
-  __syncthreads();
-  ga.template store<false>(&bt[0][0], D, threadIdx.x);
   __syncthreads();
   decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
   __syncthreads();
@@ -401,6 +360,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int rows = min(kL, a.T - c * kL);
     Tin* Y = static_cast<Tin*>(a.Y) + ((size_t)bh * a.T + (size_t)c * kL) * D;
     // The previous chunk's LDS is free (the barrier that ends its iteration).
+    staged_row_stats(nx.p1, nx.p2, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
     nx.p1.template store<true>(&qT[0][0], kP, tid);
     nx.p2.template store<true>(&kT[0][0], kP, tid);
     nx.in.template store<false>(&it[0][0], D, tid);
@@ -413,7 +373,6 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
     __syncthreads();
-    row_stats_cm<NT, D>(&qT[0][0], &kT[0][0], kP, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
     decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0], tid);
     __syncthreads();
     for (int e = tid; e < kL * D; e += NT) {
