@@ -7,14 +7,15 @@
 // One thread per (b, h, t, group of 8 rotary pairs): it loads 16 elements of
 // P1 and of P2, rotates them with the same 8 angles and stores them; if h is
 // the first head of its Givens pair it also mixes the pair's 16 information
-// elements at the same (b, t) and stores both heads. Every output element is
-// written by the thread that read its inputs, after reading them, so the
-// outputs may be the inputs (in place).
+// elements at the same (b, t) and stores both heads. A thread issues all of
+// its loads before its first store (one memory round trip), and every output
+// element is written by the thread that read its inputs, so the outputs may
+// be the inputs (in place).
 //
 // Rotary pair k (k = 0 .. d_h/2 - 1) turns by pos * base^(-2k/d_h):
 //   interleaved: (x_{2k}, x_{2k+1});   half: (x_k, x_{k + d_h/2}).
-// The angle is formed and reduced to [-pi, pi] in fp64 before the fp32
-// sincos, so positions in the thousands keep full fp32 accuracy.
+// The angle is formed and reduced in fp64 before the fp32 sine and cosine,
+// so positions in the thousands keep full fp32 accuracy.
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -53,6 +54,26 @@ __device__ __forceinline__ void store8(Tin* p, const float (&x)[8]) {
   }
 }
 
+// sin and cos of an angle held in fp64: reduced by pi/2 in fp64 (the
+// remainder r, |r| <= pi/4, is exact to far below fp32 resolution for the
+// angles a position count produces), then the single-precision minimax
+// polynomials for sin and cos on [-pi/4, pi/4] published with S. Moshier's
+// Cephes library (sinf / cosf), and the quadrant's swap and signs. Accurate
+// to a few fp32 ulps, with none of a general sincosf's large-argument path.
+__device__ __forceinline__ void sincos_of(double ang, float* s, float* c) {
+  const double k = rint(ang * 0.63661977236758134);           // 2 / pi
+  const float r = (float)fma(-k, 1.5707963267948966, ang);     // ang - k pi / 2
+  const int q = (int)(long long)k & 3;                          // quadrant (two's complement mod 4)
+  const float z = r * r;
+  const float sr = fmaf(r * z, fmaf(z, fmaf(z, -1.9515295891e-4f, 8.3321608736e-3f), -1.6666654611e-1f), r);
+  const float cr = fmaf(z * z, fmaf(z, fmaf(z, 2.443315711809948e-5f, -1.388731625493765e-3f), 4.166664568298827e-2f),
+                        fmaf(-0.5f, z, 1.0f));
+  const float sv = (q & 1) ? cr : sr;                          // sin(r + q pi/2), cos(r + q pi/2)
+  const float cv = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -sv : sv;
+  *c = ((q + 1) & 2) ? -cv : cv;
+}
+
 // Rotate 8 pairs (a[e], b[e]) by angles with cosines c[e], sines s[e].
 __device__ __forceinline__ void rotate(float (&a)[8], float (&b)[8], const float (&c)[8], const float (&s)[8]) {
 #pragma unroll
@@ -70,107 +91,101 @@ __global__ __launch_bounds__(kThreads) void prestep_kernel(PrestepArgs a, Preste
   const long long total = (long long)a.B * a.H * a.T * kGroups;
   if (idx >= total) return;
   const int g = (int)(idx % kGroups);
-  long long row = idx / kGroups;                     // (b, h, t) row index
+  const long long row = idx / kGroups;               // (b, h, t) row index
   const int t = (int)(row % a.T);
   const int h = (int)((row / a.T) % a.H);
   const int b = (int)(row / ((long long)a.T * a.H));
   const size_t ro = (size_t)row * D;
 
-  if (a.rope != 0) {
-    // Element offsets of the two halves of the 8 pairs.
-    int oa, ob;
-    if (a.rope == 1) {                               // interleaved: elements 16 g .. 16 g + 15
-      oa = 16 * g;
-      ob = -1;
-    } else {                                         // half: 8 g .. +7 and d/2 + 8 g .. +7
-      oa = 8 * g;
-      ob = D / 2 + 8 * g;
-    }
-    const long long pos = (long long)(a.pos0 ? a.pos0[b] : 0) + t;
-    float c[8], s[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double ang = (double)pos * pp.inv_freq[8 * g + e];
-      const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
-      sincosf((float)red, &s[e], &c[e]);
-    }
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const Tin* src = static_cast<const Tin*>(w ? a.P2 : a.P1) + ro;
-      Tin* dst = static_cast<Tin*>(w ? a.P2o : a.P1o) + ro;
-      float x[8], y[8], p[8], q[8];
-      if (a.rope == 1) {
-        load8(src + oa, x);
-        load8(src + oa + 8, y);
-        // pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7) (y0,y1) ...
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = x[2 * e]; q[e] = x[2 * e + 1];
-          p[4 + e] = y[2 * e]; q[4 + e] = y[2 * e + 1];
-        }
-        rotate(p, q, c, s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = p[e]; x[2 * e + 1] = q[e];
-          y[2 * e] = p[4 + e]; y[2 * e + 1] = q[4 + e];
-        }
-        store8(dst + oa, x);
-        store8(dst + oa + 8, y);
-      } else {
-        load8(src + oa, p);
-        load8(src + ob, q);
-        rotate(p, q, c, s);
-        store8(dst + oa, p);
-        store8(dst + ob, q);
-      }
-    }
-  } else if (a.P1o != a.P1 || a.P2o != a.P2) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const Tin* src = static_cast<const Tin*>(w ? a.P2 : a.P1) + ro + 16 * g;
-      Tin* dst = static_cast<Tin*>(w ? a.P2o : a.P1o) + ro + 16 * g;
-      if (src == dst) continue;
-      float x[8];
-      load8(src, x);
-      store8(dst, x);
-      load8(src + 8, x);
-      store8(dst + 8, x);
+  // Every load of the thread is issued before its first store, so one memory
+  // round trip covers it (in place, each element is stored by the thread
+  // that loaded it).
+  // Coordinates: the two 8-element halves of this group's 8 rotary pairs.
+  //   interleaved: elements 16 g .. 16 g + 15;  half: 8 g .. +7 and d/2 + 8 g .. +7.
+  const int oa = a.rope == 2 ? 8 * g : 16 * g;
+  const int ob = a.rope == 2 ? D / 2 + 8 * g : 16 * g + 8;
+  const bool copy_coords = a.rope != 0 || a.P1o != a.P1 || a.P2o != a.P2;
+  float c1[2][8], c2[2][8];                          // [half][element] of P1 and P2
+  if (copy_coords) {
+    const Tin* P1 = static_cast<const Tin*>(a.P1) + ro;
+    const Tin* P2 = static_cast<const Tin*>(a.P2) + ro;
+    load8(P1 + oa, c1[0]);
+    load8(P1 + ob, c1[1]);
+    load8(P2 + oa, c2[0]);
+    load8(P2 + ob, c2[1]);
+  }
+  // Information heads: this head's 16 elements, and its partner's when it
+  // leads a Givens pair (pairing A: (2p, 2p+1); pairing B: (2p+1, (2p+2) mod H)).
+  const Tin* I = static_cast<const Tin*>(a.I);
+  Tin* Io = static_cast<Tin*>(a.Io);
+  const bool lead = a.mix && (a.pairing == 0 ? (h % 2 == 0) : (h % 2 == 1));
+  const bool copy_info = a.mix ? lead : Io != I;
+  const int partner = a.pairing == 0 ? h + 1 : (h + 1) % a.H;
+  const size_t ra = ro + 16 * g;
+  const size_t rb = (((size_t)b * a.H + partner) * a.T + t) * D + 16 * g;
+  float xi[2][8], yi[2][8];
+  if (copy_info) {
+    load8(I + ra, xi[0]);
+    load8(I + ra + 8, xi[1]);
+    if (lead) {
+      load8(I + rb, yi[0]);
+      load8(I + rb + 8, yi[1]);
     }
   }
 
-  // Information heads.
-  const Tin* I = static_cast<const Tin*>(a.I);
-  Tin* Io = static_cast<Tin*>(a.Io);
-  if (a.mix) {
-    // Pairing A: (2p, 2p+1); pairing B: (2p+1, (2p+2) mod H). Head h leads a pair
-    // when it is its first head.
-    const bool lead = a.pairing == 0 ? (h % 2 == 0) : (h % 2 == 1);
-    if (!lead) return;
-    const int partner = a.pairing == 0 ? h + 1 : (h + 1) % a.H;
-    const int pr = a.pairing == 0 ? h / 2 : (h - 1) / 2;
-    const float ct = pp.cos_theta[pr], st = pp.sin_theta[pr];
-    const size_t ra = ro + 16 * g;
-    const size_t rb = (((size_t)b * a.H + partner) * a.T + t) * D + 16 * g;
+  if (a.rope != 0) {
+    const long long pos = (long long)(a.pos0 ? a.pos0[b] : 0) + t;
+    float c[8], sn[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float x[8], y[8];
-      load8(I + ra + 8 * half, x);
-      load8(I + rb + 8 * half, y);
+    for (int e = 0; e < 8; ++e) sincos_of((double)pos * pp.inv_freq[8 * g + e], &sn[e], &c[e]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float u = x[e], v = y[e];
-        x[e] = fmaf(ct, u, -st * v);
-        y[e] = fmaf(st, u, ct * v);
+    for (int w = 0; w < 2; ++w) {
+      float(&x)[2][8] = w ? c2 : c1;
+      if (a.rope == 1) {
+        // pairs (x0,x1) (x2,x3) ... of the 16 consecutive elements
+        float p[8], q[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = x[0][2 * e]; q[e] = x[0][2 * e + 1];
+          p[4 + e] = x[1][2 * e]; q[4 + e] = x[1][2 * e + 1];
+        }
+        rotate(p, q, c, sn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[0][2 * e] = p[e]; x[0][2 * e + 1] = q[e];
+          x[1][2 * e] = p[4 + e]; x[1][2 * e + 1] = q[4 + e];
+        }
+      } else {
+        rotate(x[0], x[1], c, sn);
       }
-      store8(Io + ra + 8 * half, x);
-      store8(Io + rb + 8 * half, y);
     }
-  } else if (Io != I) {
-    float x[8];
-    load8(I + ro + 16 * g, x);
-    store8(Io + ro + 16 * g, x);
-    load8(I + ro + 16 * g + 8, x);
-    store8(Io + ro + 16 * g + 8, x);
+  }
+  if (copy_coords) {
+    Tin* P1o = static_cast<Tin*>(a.P1o) + ro;
+    Tin* P2o = static_cast<Tin*>(a.P2o) + ro;
+    store8(P1o + oa, c1[0]);
+    store8(P1o + ob, c1[1]);
+    store8(P2o + oa, c2[0]);
+    store8(P2o + ob, c2[1]);
+  }
+
+  if (copy_info) {
+    if (lead) {
+      const int pr = a.pairing == 0 ? h / 2 : (h - 1) / 2;
+      const float ct = pp.cos_theta[pr], st = pp.sin_theta[pr];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float u = xi[half][e], v = yi[half][e];
+          xi[half][e] = fmaf(ct, u, -st * v);
+          yi[half][e] = fmaf(st, u, ct * v);
+        }
+      store8(Io + rb, yi[0]);
+      store8(Io + rb + 8, yi[1]);
+    }
+    store8(Io + ra, xi[0]);
+    store8(Io + ra + 8, xi[1]);
   }
 }
 
