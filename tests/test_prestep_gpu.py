@@ -69,6 +69,24 @@ def test_prestep_matches_oracle(case, mode, pairing):
     _check_rows(f64(o3), r3, np.broadcast_to(imax, r3.shape[:3]), dt, f"{case} {pairing} I")
 
 
+@pytest.mark.parametrize("D", [48, 80, 128])
+def test_prestep_far_positions(D):
+    """Positions up to 2^31 - 2 (the angle is formed and reduced in fp64):
+    fp32 rows, both rotary layouts, head sizes off and on powers of two."""
+    B, H, T = 4, 2, 40
+    inp, theta, _ = _inputs(B, H, T, D, "f32", 11 + D)
+    pos0 = np.array([0, 123456, 16777000, 2 ** 31 - T - 1], dtype=np.int32)
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    p0 = torch.from_numpy(pos0).to(DEV)
+    for mode in ("interleaved", "half"):
+        o1, o2, _ = R.prestep(P1, P2, I, p0, mode, 1e4, theta, "A")
+        torch.cuda.synchronize()
+        r1, r2, _ = PO.prestep(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), pos0, 1e4, mode,
+                               theta.astype(np.float64), "A")
+        for got, ref, src, name in ((o1, r1, inp["P1"], "P1"), (o2, r2, inp["P2"], "P2")):
+            _check_rows(f64(got), ref, np.max(np.abs(f64(src)), axis=-1), "f32", f"far D={D} {mode} {name}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_prestep_in_place_equals_out_of_place(dt):
     inp, theta, pos0 = _inputs(2, 4, 100, 64, dt, 5)
