@@ -205,6 +205,24 @@ def prestep(P1, P2, I, pos0=None, rope="interleaved", rope_base: float = 1e4, th
     return out
 
 
+def prestep_launcher(P1, P2, I, pos0, rope, rope_base, theta, pairing, out, stream=None):
+    """relation_prestep with its arguments marshalled once: returns a callable
+    that launches it again on the same tensors (for timing loops, where a
+    short kernel would otherwise wait on the per-call marshalling)."""
+    _require_cuda(P1, P2, I)
+    B, H, T, D = P1.shape
+    th_keep, th_p = _theta_arg(theta, H)
+    args = (_ptr(P1), _ptr(P2), _ptr(I), _ptr(pos0), ROPE[rope], float(rope_base), th_p, PAIRS[pairing],
+            _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), B, H, T, D, _dtype_code(P1), _stream(stream))
+    f = lib().relation_prestep
+
+    def launch():
+        _check("relation_prestep", f(*args))
+        return th_keep
+
+    return launch
+
+
 def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", rope_base: float = 1e4,
               theta=None, pairing="A", out=None, lse=None, workspace=None, stream=None):
     """The operator on raw projections: pre-steps, then the forward. Returns
