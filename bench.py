@@ -56,22 +56,28 @@ def _traffic(launch_bytes_key="bytes_per_launch"):
     return t.get(launch_bytes_key)
 
 
-def time_launches(fn, steps, warmup, torch):
-    """Per-launch durations (ms) from HIP events on the launching stream."""
+def time_launches(fn, steps, warmup, torch, batch=False):
+    """Per-launch durations (ms) from HIP events on the launching stream. With
+    batch=True only the first and last events are recorded (for kernels short
+    enough that an event between launches shows in the time); every launch
+    is then given the batch mean."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 if batch else steps + 1)]
     t0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(steps):
         fn()
-        evs[i + 1].record(stream)
+        if not batch:
+            evs[i + 1].record(stream)
+    if batch:
+        evs[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     total = evs[0].elapsed_time(evs[-1])
+    per = [total / steps] * steps if batch else [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     return per, total, wall
 
 
@@ -160,7 +166,7 @@ def bench_prestep(torch, R, W, steps, warmup):
     # Arguments marshalled once: the kernel is shorter than a call's Python
     # marshalling, which would otherwise be what the events time.
     pre = R.prestep_launcher(P1, P2, I, None, "interleaved", 1e4, theta, "A", out)
-    per, total, _ = time_launches(pre, steps, warmup, torch)
+    per, total, _ = time_launches(pre, steps, warmup, torch, batch=True)
     ms = total / steps
     nbytes = 6.0 * cfg.B * cfg.H * cfg.T * cfg.d_h * 2      # read P1, P2, I; write three outputs
     Y = torch.empty_like(I)

@@ -90,6 +90,22 @@ def test_linear_edge_retention_values():
     _check(inp, Y0, st0, "f32", "alpha=0 at one token")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_linear_fast_decay_takes_exact_diagonal_blocks(dt):
+    """Retention 1e-3 on a third of the channels (log alpha = -6.9 per token,
+    more than e^-40 within 8 tokens): every diagonal 16-row block of those
+    chunks leaves the factored path for the exact exponentials, while the
+    chunks of the second half keep alpha in [0.5, 1] and stay factored."""
+    cfg = W.FwdConfig("l", 1, 2, 256, 64, dt)
+    inp = W.make_linear_inputs(cfg, 9)
+    a = inp["alpha"].clone()
+    a[:, :, :128, ::3] = 1e-3
+    a[:, :, 128:] = a[:, :, 128:].clamp(0.5, 1.0)
+    inp["alpha"] = a
+    Y, st = _run(inp)
+    _check(inp, Y, st, dt, f"fast decay {dt}")
+
+
 def test_linear_deterministic():
     cfg = W.FwdConfig("l", 1, 4, 500, 128, "bf16")
     inp = W.make_linear_inputs(cfg, 5)
