@@ -29,6 +29,8 @@
 // The Self entries (diagonal) enter in the epilogues from the prep's
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -521,12 +523,260 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
   else run(Tag<false>{});
 }
 
+// ---- dkv with 16 keys per wave -------------------------------------------
+//
+// v_mfma_f32_16x16x32_bf16 operand layouts (lane l, element e, register r):
+//   A (16 x 32): lane l holds A[l % 16][8 (l / 16) + e]
+//   B (32 x 16): lane l holds B[8 (l / 16) + e][l % 16]
+//   C (16 x 16): lane l, register r holds C[4 (l / 16) + r][l % 16]
+// ds_read_b64_tr_b16: when lane m of a 16-lane group addresses row R_{m/4} at
+// columns 4 (m % 4) .. +3 of a 16-column span, lane i receives element i of
+// the span from rows R_0 .. R_3. Both were established by a probe.
+//
+// Each wave owns 16 keys and both of their accumulators (dV^T and dP2^T, d_h x
+// 16 each), so no operand changes hands between waves. Per 64-query tile and
+// 16-query block qb: U[q][key] = P1 . P2^T and G[q][key] = dY . V^T (A read
+// row-wise from LDS, the keys' P2 / V rows in registers as B); the C layout
+// puts queries 16 qb + 4 (l / 16) + r, key l % 16 in lane l. Two blocks
+// (qb0, qb1) then form one transport k-step: with the contraction index
+// permuted as {16 qb0 + 4 j + r, 16 qb1 + 4 j + r} for lane group j, the B
+// operand F[q][key] (or W) is the lane's own 8 weights, and the A operand
+// dY^T[d][q] (or P1^T) is two transposing reads of the same row layout. So a
+// tile needs P1 and dY in one layout only, and a ring of 3 tiles (114 KB at
+// d_h = 128) needs one barrier per tile.
+constexpr int kKvSlots16 = 3;
+
+template <int D>
+struct Kv16Cfg : TileLayout<D> {
+  using L = TileLayout<D>;
+  // Waves per work-group (16 keys each): d_h = 128 takes 12 (three per SIMD
+  // in one work-group per CU, as the 114 KB ring admits); d_h = 64 takes 8,
+  // and its 57 KB ring lets two work-groups share a CU.
+  static constexpr int kWaves = D == 128 ? 12 : 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kKeys = 16 * kWaves;    // keys per work-group
+  // Slot: [P1 row layout][dY row layout][statistics, 1 KB].
+  static constexpr int kStatOff = 2 * L::kKBytes;
+  static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
+  static constexpr int kLdsBytes = kKvSlots16 * kSlotBytes;
+  // Wave w moves blocks w, w + kWaves, ... of each tensor's tile; the waits
+  // count the fewest loads any wave issues per tile, which is conservative
+  // for the others (and for wave 0, which also moves the statistics).
+  static constexpr int kPer = (L::kBlocks + kWaves - 1) / kWaves;
+  static constexpr int kDmaTile = 2 * (L::kBlocks / kWaves);
+  static constexpr int kKs = D / 32;           // evidence k-steps
+  static constexpr int kDb = D / 16;           // 16-row blocks of the transports
+  // Row-layout byte offset of (row q, 16-byte chunk c):
+  //   kKBlock (q / 8 + 8 (c / 8)) + 16 (q % 8 + 8 (c % 8)).
+  // Evidence A operand: row 16 qb + l % 16, chunk 4 ks + l / 16.
+  __device__ static int e_base(int lane) {
+    const int q = lane & 15, c = lane >> 4;
+    return L::kKBlock * (q >> 3) + 16 * ((q & 7) + 8 * c);
+  }
+  static constexpr int e_imm(int qb, int ks) { return 2 * L::kKBlock * qb + 8 * L::kKBlock * (ks / 2) + 512 * (ks % 2); }
+  // Transposing read: lane m of group j addresses row 16 qb + 4 j + m / 4,
+  // columns 16 db + 4 (m % 4) .. +3 (8 bytes; half m % 2 of chunk 2 db + (m % 4) / 2).
+  __device__ static int t_base(int lane) {
+    const int m = lane & 15, q = 4 * (lane >> 4) + (m >> 2), c = (m & 3) >> 1;
+    return L::kKBlock * (q >> 3) + 16 * ((q & 7) + 8 * c) + 8 * (m & 1);
+  }
+  static constexpr int t_imm(int qb, int db) { return 2 * L::kKBlock * qb + 8 * L::kKBlock * (db / 4) + 256 * (db % 4); }
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* a, const char* b) {
+  const bf16x4 x = lds_tr_read(a), y = lds_tr_read(b);
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+template <int D, int DR = D>
+__global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdArgs a, HeadParams hp) {
+  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  using C = Kv16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
+
+  const int T = a.T;
+  const int BH = a.B * a.H;
+  const int kt = (int)blockIdx.x / BH;                 // earliest keys (longest futures) first
+  const int bh = (int)blockIdx.x % BH;
+  const int nt = (T + kStatRows - 1) / kStatRows;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int lj = lane >> 4;
+
+  const size_t head = (size_t)bh * (size_t)T * DR;
+  const long long head_bytes = (long long)T * DR * 2;
+  const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
+  const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + head;
+  const __bf16* dY = static_cast<const __bf16*>(a.dY) + head;
+  const float* stats = a.stats + (size_t)bh * nt * kStatTile;
+
+  const int k0 = kt * C::kKeys;
+  const int kq = k0 + 16 * wave;                       // this wave's 16 keys
+  const int kblk = kq / 16;
+  const float c = hp.scale;
+  const float k2 = c * kLog2e;
+
+  // The keys' P2 and V rows as B operands: lane l holds key kq + l % 16,
+  // columns 32 ks + 8 (l / 16) .. +7 (keys >= T and pad columns read 0).
+  bf16x8 kf[C::kKs], vf[C::kKs];
+  {
+    const auto rP2 = rsrc(P2, head_bytes);
+    const auto rV = rsrc(V, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < C::kKs; ++ks) {
+      const int cc = 4 * ks + lj;
+      const int o = cc < DR / 8 ? (kq + l16) * (DR * 2) + 16 * cc : kOutOfRange;
+      kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
+      vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, o, 0, 0));
+    }
+  }
+
+  // Query tiles t0 .. nt-1 hold every query i > j of this work-group's keys;
+  // from ts on, every 16-query block lies strictly below every key block.
+  const int t0 = k0 / kTileRows;
+  const int ts = (k0 / 16 + C::kWaves - 1) / 4 + 1;
+  const int hb = (int)head_bytes;
+  int src_row[C::kPer];
+#pragma unroll
+  for (int u = 0; u < C::kPer; ++u) src_row[u] = C::template row_src_real<DR>(wave + C::kWaves * u, lane);
+  auto dma = [&](int t) {
+    const int left = hb - t * kTileRows * DR * 2;
+    const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * DR, left);
+    const auto ry = rsrc_words(dY + (size_t)t * kTileRows * DR, left);
+    char* slot = smem + ((t - t0) % kKvSlots16) * C::kSlotBytes;
+#pragma unroll
+    for (int u = 0; u < C::kPer; ++u) {
+      const int k = wave + C::kWaves * u;
+      if (k < C::kBlocks) {
+        dma16(rq, slot + k * C::kKBlock, src_row[u]);
+        dma16(ry, slot + C::kKBytes + k * C::kKBlock, src_row[u]);
+      }
+    }
+    if (wave == 0) {
+      const auto rs = rsrc_words(stats + (size_t)t * kStatTile, kStatTile * 4);
+      dma16(rs, slot + C::kStatOff, 16 * lane);
+    }
+  };
+  const int eb = C::e_base(lane);
+  const int tb = C::t_base(lane);
+
+  f32x4 accV[C::kDb], accP[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+    accV[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    accP[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // The first two query tiles (issued after the key rows, so that the first
+  // wait covers both); tile t + 2 is loaded from the start of tile t, into
+  // the slot of tile t - 1.
+  if (t0 < nt) dma(t0);
+  if (t0 + 1 < nt) dma(t0 + 1);
+
+  auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
+    if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
+    else wait_vm_lgkm<0, 15>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < nt) dma(t + 2);
+    const unsigned so = (unsigned)(((t - t0) % kKvSlots16) * C::kSlotBytes);
+    unsigned oe1 = so + eb, oe2 = so + C::kKBytes + eb;  // P1 / dY evidence reads
+    unsigned ot1 = so + tb, ot2 = so + C::kKBytes + tb;  // P1 / dY transposing reads
+    asm volatile("" : "+v"(oe1), "+v"(oe2), "+v"(ot1), "+v"(ot2));
+    const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
+    int md[4] = {1, 1, 1, 1};                           // 0 none, 1 all, 2 diagonal
+    if constexpr (!decltype(steady)::value) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) md[qb] = mode_queries_above(4 * t + qb, kblk);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (md[2 * p] == 0 && md[2 * p + 1] == 0) continue;
+      u32x4 pf, pw;                                     // packed F and W of blocks 2p, 2p+1
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * p + h;
+        float f[4] = {0.0f, 0.0f, 0.0f, 0.0f}, w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (md[qb] != 0) {
+          f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 g = *reinterpret_cast<const f32x4*>(st + kStatRows + 16 * qb + 4 * lj);   // -D_q
+#pragma unroll
+          for (int ks = 0; ks < C::kKs; ++ks) {
+            const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(smem + oe1 + C::e_imm(qb, ks));
+            const bf16x8 x2 = *reinterpret_cast<const bf16x8*>(smem + oe2 + C::e_imm(qb, ks));
+            u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, kf[ks], u, 0, 0, 0);
+            g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x2, vf[ks], g, 0, 0, 0);
+          }
+          const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 16 * qb + 4 * lj);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const Terms tm(u[r], k2, c, L2[r]);
+            float F = tm.F;
+            if (md[qb] == 2) F = l16 < 4 * lj + r ? F : 0.0f;   // key < query within the diagonal block
+            f[r] = F;
+            w[r] = F * g[r] * tm.dsilu;
+          }
+        }
+        pf[2 * h + 0] = pack_bf16(f[0], f[1]);
+        pf[2 * h + 1] = pack_bf16(f[2], f[3]);
+        pw[2 * h + 0] = pack_bf16(w[0], w[1]);
+        pw[2 * h + 1] = pack_bf16(w[2], w[3]);
+      }
+      const bf16x8 bF = __builtin_bit_cast(bf16x8, pf), bW = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db) {
+        const bf16x8 ay = tr_pair(smem + ot2 + C::t_imm(2 * p, db), smem + ot2 + C::t_imm(2 * p + 1, db));
+        const bf16x8 ap = tr_pair(smem + ot1 + C::t_imm(2 * p, db), smem + ot1 + C::t_imm(2 * p + 1, db));
+        accV[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, bF, accV[db], 0, 0, 0);
+        accP[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bW, accP[db], 0, 0, 0);
+      }
+    }
+  };
+
+  int t = t0;
+  for (; t < min(ts, nt); ++t) tile(t, Tag<false>{});
+  for (; t < nt; ++t) tile(t, Tag<true>{});
+
+  const int krow = kq + l16;
+  if (krow >= T) return;
+  const size_t ro = (size_t)krow * DR;
+  // accV[db][r] = dV^T[16 db + 4 lj + r][key]: 4 consecutive columns of the key's row.
+  // dV_j = sum_i F_ij dY_i + F_jj dY_j;  dP2_j = (sum_i dU_ij p1_i + dU_jj p1_j) / sqrt(d_h).
+  __bf16* dV = static_cast<__bf16*>(a.dV) + head;
+  __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
+  const float fs = stats[stat_at(0, nt, krow, 2)];
+  const float us = stats[stat_at(0, nt, krow, 3)];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+    if (16 * db >= DR) continue;                       // padded columns
+    const int col = 16 * db + 4 * lj;
+    float y[4], q[4];
+    load4(dY + ro + col, y);
+    load4(P1 + ro + col, q);
+    store4(dV + ro + col, fmaf(fs, y[0], accV[db][0]), fmaf(fs, y[1], accV[db][1]), fmaf(fs, y[2], accV[db][2]),
+           fmaf(fs, y[3], accV[db][3]));
+    store4(dP2 + ro + col, fmaf(accP[db][0], c, us * q[0]), fmaf(accP[db][1], c, us * q[1]),
+           fmaf(accP[db][2], c, us * q[2]), fmaf(accP[db][3], c, us * q[3]));
+  }
+}
+
 template <int D, int DR = D>
 hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nq = (a.T + kDqRows - 1) / kDqRows;
   const int nk = (a.T + kKvRows - 1) / kKvRows;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
+  const char* env = std::getenv("RELATION_BWD_DKV");
+  if (env && std::strcmp(env, "pairs") == 0) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
+  } else {
+    using C16 = Kv16Cfg<D>;
+    const int nk16 = (a.T + C16::kKeys - 1) / C16::kKeys;
+    hipLaunchKernelGGL((bwd_dkv16_kernel<D, DR>), dim3(nk16 * BH), dim3(C16::kThreads), 0, s, a, hp);
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
   return hipGetLastError();
 }
