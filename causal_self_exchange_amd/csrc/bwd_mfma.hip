@@ -542,21 +542,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
 // permuted as {16 qb0 + 4 j + r, 16 qb1 + 4 j + r} for lane group j, the B
 // operand F[q][key] (or W) is the lane's own 8 weights, and the A operand
 // dY^T[d][q] (or P1^T) is two transposing reads of the same row layout. So a
-// tile needs P1 and dY in one layout only, and a ring of 3 tiles (114 KB at
+// tile needs P1 and dY in one layout only, and a ring of 3 tiles (99 KB at
 // d_h = 128) needs one barrier per tile.
+// The row layout here packs its 8-row blocks 1024 bytes apart (the forward's
+// 1152-byte stride suits the 32x32x16 read pattern only). Measured on gfx950:
+// a 16-byte LDS read serves, in each pass, the lane groups {0-7, 24-31},
+// {8-15, 16-23} and the same of the upper 32 lanes; with the 1152-byte stride
+// the 16x16x32 A-operand read puts both groups of every pass on the same
+// banks (two-way conflicts, half the throughput), with 1024 bytes they fall
+// in opposite halves. The transposing reads are conflict-free with either.
 constexpr int kKvSlots16 = 3;
 
 template <int D>
 struct Kv16Cfg : TileLayout<D> {
   using L = TileLayout<D>;
+  static constexpr int kBlk = 1024;                    // block stride of this layout
+  static constexpr int kTileBytes = L::kBlocks * kBlk;
   // Waves per work-group (16 keys each): d_h = 128 takes 12 (three per SIMD
-  // in one work-group per CU, as the 114 KB ring admits); d_h = 64 takes 8,
-  // and its 57 KB ring lets two work-groups share a CU.
+  // in one work-group per CU, as the 99 KB ring admits); d_h = 64 takes 8,
+  // and its 51 KB ring lets two work-groups share a CU.
   static constexpr int kWaves = D == 128 ? 12 : 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kKeys = 16 * kWaves;    // keys per work-group
   // Slot: [P1 row layout][dY row layout][statistics, 1 KB].
-  static constexpr int kStatOff = 2 * L::kKBytes;
+  static constexpr int kStatOff = 2 * kTileBytes;
   static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
   static constexpr int kLdsBytes = kKvSlots16 * kSlotBytes;
   // Wave w moves blocks w, w + kWaves, ... of each tensor's tile; the waits
@@ -566,21 +575,22 @@ struct Kv16Cfg : TileLayout<D> {
   static constexpr int kDmaTile = 2 * (L::kBlocks / kWaves);
   static constexpr int kKs = D / 32;           // evidence k-steps
   static constexpr int kDb = D / 16;           // 16-row blocks of the transports
-  // Row-layout byte offset of (row q, 16-byte chunk c):
-  //   kKBlock (q / 8 + 8 (c / 8)) + 16 (q % 8 + 8 (c % 8)).
+  // Byte offset of (row q, 16-byte chunk c) in a tile (blocks as in the
+  // forward's row layout: block q / 8 + 8 (c / 8), position q % 8 + 8 (c % 8)):
+  //   kBlk (q / 8 + 8 (c / 8)) + 16 (q % 8 + 8 (c % 8)).
   // Evidence A operand: row 16 qb + l % 16, chunk 4 ks + l / 16.
   __device__ static int e_base(int lane) {
     const int q = lane & 15, c = lane >> 4;
-    return L::kKBlock * (q >> 3) + 16 * ((q & 7) + 8 * c);
+    return kBlk * (q >> 3) + 16 * ((q & 7) + 8 * c);
   }
-  static constexpr int e_imm(int qb, int ks) { return 2 * L::kKBlock * qb + 8 * L::kKBlock * (ks / 2) + 512 * (ks % 2); }
+  static constexpr int e_imm(int qb, int ks) { return 2 * kBlk * qb + 8 * kBlk * (ks / 2) + 512 * (ks % 2); }
   // Transposing read: lane m of group j addresses row 16 qb + 4 j + m / 4,
   // columns 16 db + 4 (m % 4) .. +3 (8 bytes; half m % 2 of chunk 2 db + (m % 4) / 2).
   __device__ static int t_base(int lane) {
     const int m = lane & 15, q = 4 * (lane >> 4) + (m >> 2), c = (m & 3) >> 1;
-    return L::kKBlock * (q >> 3) + 16 * ((q & 7) + 8 * c) + 8 * (m & 1);
+    return kBlk * (q >> 3) + 16 * ((q & 7) + 8 * c) + 8 * (m & 1);
   }
-  static constexpr int t_imm(int qb, int db) { return 2 * L::kKBlock * qb + 8 * L::kKBlock * (db / 4) + 256 * (db % 4); }
+  static constexpr int t_imm(int qb, int db) { return 2 * kBlk * qb + 8 * kBlk * (db / 4) + 256 * (db % 4); }
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -653,8 +663,8 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
     for (int u = 0; u < C::kPer; ++u) {
       const int k = wave + C::kWaves * u;
       if (k < C::kBlocks) {
-        dma16(rq, slot + k * C::kKBlock, src_row[u]);
-        dma16(ry, slot + C::kKBytes + k * C::kKBlock, src_row[u]);
+        dma16(rq, slot + k * C::kBlk, src_row[u]);
+        dma16(ry, slot + C::kTileBytes + k * C::kBlk, src_row[u]);
       }
     }
     if (wave == 0) {
@@ -671,11 +681,15 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
     accV[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     accP[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // The first two query tiles (issued after the key rows, so that the first
-  // wait covers both); tile t + 2 is loaded from the start of tile t, into
-  // the slot of tile t - 1.
+  // The first two query tiles; tile t + 2 is loaded from the start of tile
+  // t, into the slot of tile t - 1. The full wait before the loop covers the
+  // key rows too: the compiler sees only the key-row loads (the direct loads
+  // are inline assembly), and once it knows they have completed it puts no
+  // wait of its own inside the loop, where any vmcnt wait would also stall on
+  // the tiles in flight.
   if (t0 < nt) dma(t0);
   if (t0 + 1 < nt) dma(t0 + 1);
+  wait_vm_lgkm<0, 15>();
 
   auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
     if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
@@ -684,8 +698,8 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
     asm volatile("" ::: "memory");
     if (t + 2 < nt) dma(t + 2);
     const unsigned so = (unsigned)(((t - t0) % kKvSlots16) * C::kSlotBytes);
-    unsigned oe1 = so + eb, oe2 = so + C::kKBytes + eb;  // P1 / dY evidence reads
-    unsigned ot1 = so + tb, ot2 = so + C::kKBytes + tb;  // P1 / dY transposing reads
+    unsigned oe1 = so + eb, oe2 = so + C::kTileBytes + eb;  // P1 / dY evidence reads
+    unsigned ot1 = so + tb, ot2 = so + C::kTileBytes + tb;  // P1 / dY transposing reads
     asm volatile("" : "+v"(oe1), "+v"(oe2), "+v"(ot1), "+v"(ot2));
     const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
     int md[4] = {1, 1, 1, 1};                           // 0 none, 1 all, 2 diagonal
