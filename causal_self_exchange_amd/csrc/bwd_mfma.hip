@@ -710,29 +710,41 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (md[2 * p] == 0 && md[2 * p + 1] == 0) continue;
+      // Evidence of both blocks, then the first transport operands (their
+      // LDS latency runs under the weights' VALU work), then the weights,
+      // then the transports with each operand read one d-block ahead.
+      f32x4 u[2], g[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * p + h;
+        u[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        g[h] = *reinterpret_cast<const f32x4*>(st + kStatRows + 16 * qb + 4 * lj);   // -D_q
+        if (md[qb] != 0) {
+#pragma unroll
+          for (int ks = 0; ks < C::kKs; ++ks) {
+            const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(smem + oe1 + C::e_imm(qb, ks));
+            const bf16x8 x2 = *reinterpret_cast<const bf16x8*>(smem + oe2 + C::e_imm(qb, ks));
+            u[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, kf[ks], u[h], 0, 0, 0);
+            g[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x2, vf[ks], g[h], 0, 0, 0);
+          }
+        }
+      }
+      bf16x8 ay = tr_pair(smem + ot2 + C::t_imm(2 * p, 0), smem + ot2 + C::t_imm(2 * p + 1, 0));
+      bf16x8 ap = tr_pair(smem + ot1 + C::t_imm(2 * p, 0), smem + ot1 + C::t_imm(2 * p + 1, 0));
       u32x4 pf, pw;                                     // packed F and W of blocks 2p, 2p+1
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int qb = 2 * p + h;
         float f[4] = {0.0f, 0.0f, 0.0f, 0.0f}, w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (md[qb] != 0) {
-          f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
-          f32x4 g = *reinterpret_cast<const f32x4*>(st + kStatRows + 16 * qb + 4 * lj);   // -D_q
-#pragma unroll
-          for (int ks = 0; ks < C::kKs; ++ks) {
-            const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(smem + oe1 + C::e_imm(qb, ks));
-            const bf16x8 x2 = *reinterpret_cast<const bf16x8*>(smem + oe2 + C::e_imm(qb, ks));
-            u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, kf[ks], u, 0, 0, 0);
-            g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x2, vf[ks], g, 0, 0, 0);
-          }
           const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 16 * qb + 4 * lj);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const Terms tm(u[r], k2, c, L2[r]);
+            const Terms tm(u[h][r], k2, c, L2[r]);
             float F = tm.F;
             if (md[qb] == 2) F = l16 < 4 * lj + r ? F : 0.0f;   // key < query within the diagonal block
             f[r] = F;
-            w[r] = F * g[r] * tm.dsilu;
+            w[r] = F * g[h][r] * tm.dsilu;
           }
         }
         pf[2 * h + 0] = pack_bf16(f[0], f[1]);
@@ -743,10 +755,15 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
       const bf16x8 bF = __builtin_bit_cast(bf16x8, pf), bW = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < C::kDb; ++db) {
-        const bf16x8 ay = tr_pair(smem + ot2 + C::t_imm(2 * p, db), smem + ot2 + C::t_imm(2 * p + 1, db));
-        const bf16x8 ap = tr_pair(smem + ot1 + C::t_imm(2 * p, db), smem + ot1 + C::t_imm(2 * p + 1, db));
+        bf16x8 ny = ay, np = ap;
+        if (db + 1 < C::kDb) {
+          ny = tr_pair(smem + ot2 + C::t_imm(2 * p, db + 1), smem + ot2 + C::t_imm(2 * p + 1, db + 1));
+          np = tr_pair(smem + ot1 + C::t_imm(2 * p, db + 1), smem + ot1 + C::t_imm(2 * p + 1, db + 1));
+        }
         accV[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, bF, accV[db], 0, 0, 0);
         accP[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bW, accP[db], 0, 0, 0);
+        ay = ny;
+        ap = np;
       }
     }
   };
