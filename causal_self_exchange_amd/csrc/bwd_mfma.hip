@@ -17,20 +17,16 @@
 //   dP1^T[d][q] += P2^T[d][key] W^T[key][q] (transport).
 //   LDS per key tile: P2 in the row layout and the transposed layout, V in
 //   the row layout; a ring of 3 tiles, one barrier per tile.
-// dkv (key/value gradients): 128 key rows, query tiles of 64 rows, 8 waves;
-//   per 32 keys two waves split each tile by 32-query block and form
-//   U[q][key] = P1 . P2^T, G[q][key] = dY . V^T (P2 and V rows of the keys in
-//   registers), F and W of their block; one accumulates
-//   dV^T[d][key] += dY^T[d][q] F[q][key], the other
-//   dP2^T[d][key] += P1^T[d][q] W[q][key], each taking the partner's block's
-//   operand through LDS. One d_h x 32 accumulator per wave lets two waves
-//   share a SIMD. LDS per query tile: P1 and dY in both layouts plus the
-//   tile's row statistics; a ring of 2 tiles and a 16 KB exchange area.
+// dkv (key/value gradients): 16 keys per wave, query tiles of 64 rows; per
+//   16-query block U[q][key] = P1 . P2^T and G[q][key] = dY . V^T (P2 and V
+//   rows of the wave's keys in registers), F and W, then
+//   dV^T[d][key] += dY^T[d][q] F[q][key] and dP2^T[d][key] += P1^T[d][q] W[q][key]
+//   on v_mfma_f32_16x16x32_bf16, both accumulators in the wave. LDS per query
+//   tile: P1 and dY in one row layout plus the tile's row statistics; a ring
+//   of 3 tiles, one barrier per tile.
 // The Self entries (diagonal) enter in the epilogues from the prep's
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -47,10 +43,6 @@ constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
 constexpr int kDqRows = kDqWaves * 32;     // query rows per dq work-group
 constexpr int kDqSlots = 3;
-constexpr int kKvWaves = 8;
-constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kKvRows = 4 * 32;            // key rows per dkv work-group (two waves per 32 keys)
-constexpr int kKvSlots = 2;
 
 template <int D>
 struct DqCfg : TileLayout<D> {
@@ -63,23 +55,6 @@ struct DqCfg : TileLayout<D> {
   static_assert(L::kBlocks % kDqWaves == 0, "each wave moves whole blocks");
 };
 
-template <int D>
-struct KvCfg : TileLayout<D> {
-  using L = TileLayout<D>;
-  // Slot: [P1 row][dY row][P1 transposed][dY transposed][statistics, 1 KB].
-  static constexpr int kStatOff = 2 * L::kKBytes + 2 * L::kVBytes;
-  static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
-  // Exchange area: per 32-key group and 32-query block, one packed bf16
-  // transport operand (64 lanes x 32 bytes).
-  static constexpr int kXBytes = 4 * 2 * 64 * 32;
-  static constexpr int kLdsBytes = kKvSlots * kSlotBytes + kXBytes;
-  static constexpr int kPer = L::kBlocks / kKvWaves;
-  // Direct loads per wave and tile (wave 0 also moves the statistics; the
-  // waits use the smaller count, which is conservative for wave 0).
-  static constexpr int kDmaTile = 4 * kPer;
-  static_assert(L::kBlocks % kKvWaves == 0, "each wave moves whole blocks");
-  static_assert(kStatTile * 4 == 1024, "statistics of one tile = one direct load");
-};
 
 // Mode of a 32-row block of the scanned operand for a wave whose own 32-row
 // block is `own`: 0 = no pair (i, j) with j < i, 1 = all pairs, 2 = diagonal
@@ -121,48 +96,6 @@ __device__ __forceinline__ void dq_weights(const f32x16& s, const f32x16& gm, fl
     }
     pw[r >> 3][(r & 7) >> 1] = pack_bf16(w[0], w[1]);
   }
-}
-
-// dkv weights of one 32-query block for this lane's key (row lq), register r
-// <-> query 8 (r / 4) + 4 hf + r % 4 of the block (qb0 = first query of the
-// block within the tile; st = the tile's statistics in LDS): the flow
-// F[q][key] and the gradient weight W[q][key] = F (dY_q . V_key - D_q) SiLU'(u)
-// (gm holds dY_q . V_key - D_q), as packed bf16 transport operands.
-__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& gm, float k2, float c, const float* st,
-                                           int qb0, bool diag, int hf, int lq, u32x4 (&pf)[2], u32x4 (&pw)[2]) {
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const float4 L2 = *reinterpret_cast<const float4*>(st + qb0 + 8 * g4 + 4 * hf);
-    const float l2v[4] = {L2.x, L2.y, L2.z, L2.w};
-    float f[4], w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g4 + e;
-      const Terms t(s[r], k2, c, l2v[e]);
-      float F = t.F;
-      if (diag) F = lq < 8 * g4 + 4 * hf + e ? F : 0.0f;
-      f[e] = F;
-      w[e] = F * gm[r] * t.dsilu;
-    }
-    pf[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(f[0], f[1]);
-    pf[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(f[2], f[3]);
-    pw[g4 >> 1][2 * (g4 & 1) + 0] = pack_bf16(w[0], w[1]);
-    pw[g4 >> 1][2 * (g4 & 1) + 1] = pack_bf16(w[2], w[3]);
-  }
-}
-
-// -D_q of the 16 queries of a 32-query block in C-layout register order.
-__device__ __forceinline__ f32x16 neg_d_block(const float* st, int qb0, int hf) {
-  f32x16 v;
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const float4 d = *reinterpret_cast<const float4*>(st + kStatRows + qb0 + 8 * g4 + 4 * hf);
-    v[4 * g4 + 0] = d.x;
-    v[4 * g4 + 1] = d.y;
-    v[4 * g4 + 2] = d.z;
-    v[4 * g4 + 3] = d.w;
-  }
-  return v;
 }
 
 // Store 4 consecutive bf16 of a row (8 bytes).
@@ -329,201 +262,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   }
 }
 
-// Key/value gradients. Waves w and w + 4 own the same 32 keys (group kg = w % 4)
-// and split each 64-query tile by 32-query block: wave w forms U, G, F and W
-// of block 0, wave w + 4 those of block 1. Each keeps one accumulator (waves
-// 0-3 dV^T, waves 4-7 dP2^T), transports its own block at once and hands the
-// other operand (W of block 0, F of block 1) to its partner through LDS; after
-// a barrier each transports the partner's block. Both roles do the same MFMA
-// and VALU work, and each runs in its own code region so that two waves fit
-// per SIMD.
-template <int D, int DR = D>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
-  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
-  using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
-
-  const int T = a.T;
-  const int BH = a.B * a.H;
-  const int kt = (int)blockIdx.x / BH;                 // earliest keys (longest futures) first
-  const int bh = (int)blockIdx.x % BH;
-  const int nt = (T + kStatRows - 1) / kStatRows;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave & 3;                             // the wave's 32-key group
-  const int lane = tid & 63;
-  const int lq = lane & 31;
-  const int hf = lane >> 5;
-
-  const size_t head = (size_t)bh * (size_t)T * DR;
-  const long long head_bytes = (long long)T * DR * 2;
-  const __bf16* P1 = static_cast<const __bf16*>(a.P1) + head;
-  const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
-  const __bf16* V = static_cast<const __bf16*>(a.V) + head;
-  const __bf16* dY = static_cast<const __bf16*>(a.dY) + head;
-  const float* stats = a.stats + (size_t)bh * nt * kStatTile;
-
-  const int k0 = kt * kKvRows;
-  const int krow = k0 + kg * 32 + lq;                  // may be >= T: loads give 0, stores drop
-  const int own = k0 / 32 + kg;
-  const int koff = krow * (DR * 2) + hf * 16;
-  const float c = hp.scale;
-  const float k2 = c * kLog2e;
-
-  // Query tiles t0 .. nt-1 hold every query i > j of this work-group's keys;
-  // from t0 + 2 on, every block lies strictly below every key block.
-  const int t0 = k0 / kTileRows;
-  const int hb = (int)head_bytes;
-  int src_row[C::kPer], src_tr[C::kPer];
-#pragma unroll
-  for (int u = 0; u < C::kPer; ++u) {
-    src_row[u] = C::template row_src_real<DR>(wave + kKvWaves * u, lane);
-    src_tr[u] = C::template tr_src_real<DR>(wave + kKvWaves * u, lane);
-  }
-  auto dma = [&](int t) {
-    const int left = hb - t * kTileRows * DR * 2;
-    const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * DR, left);
-    const auto ry = rsrc_words(dY + (size_t)t * kTileRows * DR, left);
-    char* slot = smem + ((t - t0) % kKvSlots) * C::kSlotBytes;
-#pragma unroll
-    for (int u = 0; u < C::kPer; ++u) {
-      const int k = wave + kKvWaves * u;
-      dma16(rq, slot + k * C::kKBlock, src_row[u]);
-      dma16(ry, slot + C::kKBytes + k * C::kKBlock, src_row[u]);
-      dma16(rq, slot + 2 * C::kKBytes + k * C::kVBlock, src_tr[u]);
-      dma16(ry, slot + 2 * C::kKBytes + C::kVBytes + k * C::kVBlock, src_tr[u]);
-    }
-    if (wave == 0) {
-      const auto rs = rsrc_words(stats + (size_t)t * kStatTile, kStatTile * 4);
-      dma16(rs, slot + C::kStatOff, 16 * lane);
-    }
-  };
-  const int row_base = C::row_base(lane);
-  const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
-  // Exchange slots of this key group: [block 0: W][block 1: F], 32 bytes per lane.
-  char* const xw = smem + kKvSlots * C::kSlotBytes + (kg * 2 + 0) * 2048 + 32 * lane;
-  char* const xf = smem + kKvSlots * C::kSlotBytes + (kg * 2 + 1) * 2048 + 32 * lane;
-
-  auto run = [&](auto role) __attribute__((always_inline)) {
-    constexpr bool kP = decltype(role)::value;        // false: block 0 and dV; true: block 1 and dP2
-    constexpr int qb = kP ? 1 : 0;                     // the block this wave forms
-    bf16x8 kf[C::kDs], vf[C::kDs];
-    {
-      const auto rP2 = rsrc(P2, head_bytes);
-      const auto rV = rsrc(V, head_bytes);
-#pragma unroll
-      for (int ds = 0; ds < C::kDs; ++ds) {
-        const int o = ds < DR / 16 ? koff + ds * 32 : kOutOfRange;   // pad k-steps read 0
-        kf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
-        vf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, o, 0, 0));
-      }
-    }
-    // The first two query tiles (issued after the key rows, so that the
-    // first wait covers both).
-    if (t0 < nt) dma(t0);
-    if (t0 + 1 < nt) dma(t0 + 1);
-    f32x16 acc[C::kDb];
-#pragma unroll
-    for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-
-    auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
-      if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
-      else wait_vm_lgkm<0, 15>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
-      unsigned orow = so + row_base;                                        // P1 row layout
-      unsigned oy = so + C::kKBytes + row_base;                             // dY row layout
-      unsigned te = so + 2 * C::kKBytes + (kP ? 0 : C::kVBytes) + tr_even;  // P1^T (dP2) or dY^T (dV)
-      unsigned to = so + 2 * C::kKBytes + (kP ? 0 : C::kVBytes) + tr_odd;
-      asm volatile("" : "+v"(orow), "+v"(oy), "+v"(te), "+v"(to));
-      const VBase xt{smem + te, smem + to};
-      const float* st = reinterpret_cast<const float*>(smem + so + C::kStatOff);
-      bool mine = true, other = true, diag = false;
-      if constexpr (!decltype(steady)::value) {
-        const int md = mode_queries_above(2 * t + qb, own);
-        mine = md != 0;
-        diag = md == 2;
-        other = mode_queries_above(2 * t + (1 - qb), own) != 0;
-      }
-      if (mine) {
-        const f32x16 s = evidence_block<D>(smem + orow, qb, kf);
-        const f32x16 g = evidence_block_from<D>(smem + oy, qb, vf, neg_d_block(st, 32 * qb, hf));
-        u32x4 pf[2], pw[2];
-        kv_weights(s, g, k2, c, st, 32 * qb, diag, hf, lq, pf, pw);
-        // Hand the partner its operand, then transport this block.
-        const u32x4(&give)[2] = kP ? pf : pw;
-        char* const xo = kP ? xf : xw;
-        *reinterpret_cast<u32x4*>(xo) = give[0];
-        *reinterpret_cast<u32x4*>(xo + 16) = give[1];
-        transport_block<D>(xt, qb, kP ? pw : pf, acc);
-      }
-      wait_vm_lgkm<63, 0>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (other) {
-        const char* xi = kP ? xw : xf;
-        u32x4 op[2];
-        op[0] = *reinterpret_cast<const u32x4*>(xi);
-        op[1] = *reinterpret_cast<const u32x4*>(xi + 16);
-        transport_block<D>(xt, 1 - qb, op, acc);
-      }
-      // Every wave is done with this slot (and the exchange area) before
-      // either is rewritten.
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 2 < nt) dma(t + 2);
-    };
-
-    int t = t0;
-    for (; t < min(t0 + 2, nt); ++t) tile(t, Tag<false>{});
-    for (; t < nt; ++t) tile(t, Tag<true>{});
-
-    if (krow >= T) return;
-    const size_t ro = (size_t)krow * DR;
-    if constexpr (kP) {
-      // dP2_j = (sum_i dU_ij p1_i + dU_jj p1_j) / sqrt(d_h).
-      __bf16* dP2 = static_cast<__bf16*>(a.dP2) + head;
-      const float us = stats[stat_at(0, nt, krow, 3)];
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          if (32 * db + 8 * g4 >= DR) continue;      // padded columns
-          const int col = 32 * db + 8 * g4 + 4 * hf;
-          const int r = 4 * g4;
-          float p[4];
-          load4(P1 + ro + col, p);
-          store4(dP2 + ro + col, fmaf(acc[db][r + 0], c, us * p[0]), fmaf(acc[db][r + 1], c, us * p[1]),
-                 fmaf(acc[db][r + 2], c, us * p[2]), fmaf(acc[db][r + 3], c, us * p[3]));
-        }
-      }
-    } else {
-      // dV_j = sum_i F_ij dY_i + F_jj dY_j.
-      __bf16* dV = static_cast<__bf16*>(a.dV) + head;
-      const float fs = stats[stat_at(0, nt, krow, 2)];
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          if (32 * db + 8 * g4 >= DR) continue;      // padded columns
-          const int col = 32 * db + 8 * g4 + 4 * hf;
-          const int r = 4 * g4;
-          float y[4];
-          load4(dY + ro + col, y);
-          store4(dV + ro + col, fmaf(fs, y[0], acc[db][r + 0]), fmaf(fs, y[1], acc[db][r + 1]),
-                 fmaf(fs, y[2], acc[db][r + 2]), fmaf(fs, y[3], acc[db][r + 3]));
-        }
-      }
-    }
-  };
-  if (wave >= 4) run(Tag<true>{});
-  else run(Tag<false>{});
-}
-
-// ---- dkv with 16 keys per wave -------------------------------------------
+// ---- key/value gradients ----------------------------------------------------
 //
 // v_mfma_f32_16x16x32_bf16 operand layouts (lane l, element e, register r):
 //   A (16 x 32): lane l holds A[l % 16][8 (l / 16) + e]
@@ -551,10 +290,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadP
 // the 16x16x32 A-operand read puts both groups of every pass on the same
 // banks (two-way conflicts, half the throughput), with 1024 bytes they fall
 // in opposite halves. The transposing reads are conflict-free with either.
-constexpr int kKvSlots16 = 3;
+constexpr int kKvSlots = 3;
 
 template <int D>
-struct Kv16Cfg : TileLayout<D> {
+struct KvCfg : TileLayout<D> {
   using L = TileLayout<D>;
   static constexpr int kBlk = 1024;                    // block stride of this layout
   static constexpr int kTileBytes = L::kBlocks * kBlk;
@@ -567,7 +306,7 @@ struct Kv16Cfg : TileLayout<D> {
   // Slot: [P1 row layout][dY row layout][statistics, 1 KB].
   static constexpr int kStatOff = 2 * kTileBytes;
   static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
-  static constexpr int kLdsBytes = kKvSlots16 * kSlotBytes;
+  static constexpr int kLdsBytes = kKvSlots * kSlotBytes;
   // Wave w moves blocks w, w + kWaves, ... of each tensor's tile; the waits
   // count the fewest loads any wave issues per tile, which is conservative
   // for the others (and for wave 0, which also moves the statistics).
@@ -601,9 +340,9 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* a, const char* b) {
 }
 
 template <int D, int DR = D>
-__global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdArgs a, HeadParams hp) {
+__global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
   static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
-  using C = Kv16Cfg<D>;
+  using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
   const int T = a.T;
@@ -658,7 +397,7 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
     const int left = hb - t * kTileRows * DR * 2;
     const auto rq = rsrc_words(P1 + (size_t)t * kTileRows * DR, left);
     const auto ry = rsrc_words(dY + (size_t)t * kTileRows * DR, left);
-    char* slot = smem + ((t - t0) % kKvSlots16) * C::kSlotBytes;
+    char* slot = smem + ((t - t0) % kKvSlots) * C::kSlotBytes;
 #pragma unroll
     for (int u = 0; u < C::kPer; ++u) {
       const int k = wave + C::kWaves * u;
@@ -697,7 +436,7 @@ __global__ __launch_bounds__(Kv16Cfg<D>::kThreads, 1) void bwd_dkv16_kernel(BwdA
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (t + 2 < nt) dma(t + 2);
-    const unsigned so = (unsigned)(((t - t0) % kKvSlots16) * C::kSlotBytes);
+    const unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
     unsigned oe1 = so + eb, oe2 = so + C::kTileBytes + eb;  // P1 / dY evidence reads
     unsigned ot1 = so + tb, ot2 = so + C::kTileBytes + tb;  // P1 / dY transposing reads
     asm volatile("" : "+v"(oe1), "+v"(oe2), "+v"(ot1), "+v"(ot2));
@@ -799,15 +538,9 @@ template <int D, int DR = D>
 hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nq = (a.T + kDqRows - 1) / kDqRows;
-  const int nk = (a.T + kKvRows - 1) / kKvRows;
-  const char* env = std::getenv("RELATION_BWD_DKV");
-  if (env && std::strcmp(env, "pairs") == 0) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(kKvThreads), 0, s, a, hp);
-  } else {
-    using C16 = Kv16Cfg<D>;
-    const int nk16 = (a.T + C16::kKeys - 1) / C16::kKeys;
-    hipLaunchKernelGGL((bwd_dkv16_kernel<D, DR>), dim3(nk16 * BH), dim3(C16::kThreads), 0, s, a, hp);
-  }
+  using Ckv = KvCfg<D>;
+  const int nk = (a.T + Ckv::kKeys - 1) / Ckv::kKeys;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(Ckv::kThreads), 0, s, a, hp);
   hipLaunchKernelGGL((bwd_dq_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
   return hipGetLastError();
 }
