@@ -158,6 +158,18 @@ __device__ __forceinline__ float block_max(const f32x16& s, int hf, int lq) {
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
+// Raw Self evidence p1_i . p2_i of the lane's query from its diagonal block's
+// evidence tile: register r holds key 8 (r / 4) + 4 hf + r % 4, which is the
+// query lq in the half hf = (lq / 4) % 2, register 4 (lq / 8) + lq % 4; the
+// other half contributes 0 (the halves are summed at the end).
+__device__ __forceinline__ float diag_entry(const f32x16& s, int hf, int lq) {
+  const int rs = 4 * (lq >> 3) + (lq & 3);
+  float v = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v = r == rs ? s[r] : v;
+  return ((lq >> 2) & 1) == hf ? v : 0.0f;
+}
+
 // Lazy stabiliser update from a tile's raw maximum: returns the factor the
 // accumulated O and row sum must be multiplied by (1 if m does not move).
 __device__ __forceinline__ float stabilise(float mx, float k2, float& m2) {
@@ -199,8 +211,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const int lq = lane & 31;                      // query (column) within the wave
   const int hf = lane >> 5;                      // lane half
 
-  // One query tile (256 rows) of one head, start to finish.
-  auto run_tile = [&](int qt, int bh) __attribute__((always_inline)) {
+  // P1 rows of a query tile as the evidence MFMA's B operand: lane holds
+  // p1[qrow][16 ds + 8 hf + 0..7]. They are loaded one tile ahead, before the
+  // previous tile's epilogue, so their latency hides behind it.
+  bf16x8 qf[C::kDs];
+  auto load_q = [&](int qt, int bh) __attribute__((always_inline)) {
+    const auto rP1 = rsrc(static_cast<const __bf16*>(a.P1) + (size_t)bh * (size_t)T * DR, (long long)T * DR * 2);
+    const int qoff = (qt * kBM + wave * 32 + lq) * (DR * 2) + hf * 16;
+#pragma unroll
+    for (int ds = 0; ds < C::kDs; ++ds) {
+      // k-steps past DR / 16 cover padded columns: out-of-range offsets read 0.
+      const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;
+      qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, o, 0, 0));
+    }
+  };
+
+  // One query tile (256 rows) of one head, start to finish; then, when nqt >=
+  // 0, the P1 rows of query tile nqt of head nbh are loaded before the
+  // epilogue.
+  auto run_tile = [&](int qt, int bh, int nqt, int nbh) __attribute__((always_inline)) {
   const int h = bh % a.H;
   const size_t head = (size_t)bh * (size_t)T * DR;
   const long long head_bytes = (long long)T * DR * 2;
@@ -208,26 +237,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
   const __bf16* V = static_cast<const __bf16*>(a.V) + head;
   __bf16* Y = static_cast<__bf16*>(a.Y) + head;
-  const auto rP1 = rsrc(P1, head_bytes);
-  const auto rP2 = rsrc(P2, head_bytes);
   const auto rY = rsrc(Y, head_bytes);
 
   const int q0 = qt * kBM;
   const int qrow = q0 + wave * 32 + lq;          // may be >= T: loads give 0, stores drop
   const int dblk = q0 / 32 + wave;               // the wave's diagonal 32-key block
 
-  // P1 rows as the evidence MFMA's B operand: lane holds p1[qrow][16 ds + 8 hf + 0..7];
-  // the same chunks of p2[qrow] give the Self evidence p1_i . p2_i.
-  const int qoff = qrow * (DR * 2) + hf * 16;
-  // (The dot product waits until the prologue's tile loads are issued too.)
-  bf16x8 qf[C::kDs], kv[C::kDs];
-#pragma unroll
-  for (int ds = 0; ds < C::kDs; ++ds) {
-    // k-steps past DR / 16 cover padded columns: out-of-range offsets read 0.
-    const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;
-    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, o, 0, 0));
-    kv[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
-  }
   const float inv_tau = hp.inv_tau[h];
 
   const float k2 = hp.scale * kLog2e;            // raw dot -> log2-domain evidence
@@ -294,11 +309,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   dma_k(2);
   dma_v(0);
   dma_v(1);
+  // Self evidence p1_i . p2_i: the diagonal block's evidence tile provides it
+  // (diag_entry) whenever the scan reaches that block. It does not only for a
+  // wave whose first row is T - 1 with T - 1 a multiple of 64 (its own key
+  // tile holds no history), or whose rows all lie past T; such a wave takes
+  // the dot product of the rows.
   float dself = 0.0f;
+  if (dblk >= 2 * ntiles) {
+    const auto rP2 = rsrc(P2, head_bytes);
+    const int qoff = qrow * (DR * 2) + hf * 16;
 #pragma unroll
-  for (int ds = 0; ds < C::kDs; ++ds)
+    for (int ds = 0; ds < C::kDs; ++ds) {
+      const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, o, 0, 0));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[ds][e], dself);
+      for (int e = 0; e < 8; ++e) dself = fmaf((float)qf[ds][e], (float)kv[e], dself);
+    }
+  }
   wait_vm_lgkm<0, 15>();
   __syncthreads();
   // Evidence of tile j (s_cur, per 32-key block) and packed bf16 weights of
@@ -406,8 +433,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (blk_active(md_cur, kb)) {
-        if (blk_diag(md_cur, kb)) weights_block<true>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
-        else weights_block<false>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
+        if (blk_diag(md_cur, kb)) {
+          dself = diag_entry(s_cur[kb], hf, lq);
+          weights_block<true>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
+        } else {
+          weights_block<false>(s_cur[kb], k2, m2, hf, lq, p_cur[kb], lsum);
+        }
       } else {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) p_cur[kb][ks] = u32x4{0u, 0u, 0u, 0u};
@@ -531,6 +562,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // The last iterations' direct loads (of tiles past the end) must land
   // before the work-group's LDS is released.
   wait_vm_lgkm<0, 15>();
+  if (nqt >= 0) load_q(nqt, nbh);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- epilogue -------------------------------------------------------------
   lsum = lane_pair_sum(lsum);
@@ -575,15 +608,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
 
   const int npair = (nq + 1) / 2;
   const int nwork = a.B * a.H * npair;
-  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
-    int bh, pr;
-    work_of(w, gridDim.x, npair, a.B * a.H, bh, pr);
-    // Heavier tile first; an odd tile count leaves the middle tile alone.
+  // Item w runs the heavier tile nq-1-pr, then pr (an odd tile count leaves
+  // the middle tile alone); each tile names the next one of the work-group.
+  int w = blockIdx.x;
+  if (w >= nwork) return;
+  int bh, pr;
+  work_of(w, gridDim.x, npair, a.B * a.H, bh, pr);
+  int qt = nq - 1 - pr;
+  load_q(qt, bh);
 #pragma nounroll
-    for (int k = 0; k < (pr == nq - 1 - pr ? 1 : 2); ++k) {
-      run_tile(k == 0 ? nq - 1 - pr : pr, bh);
-
+  while (true) {
+    int nqt = -1, nbh = bh, npr = pr, nw = w;
+    if (qt != pr) {
+      nqt = pr;
+    } else if (w + (int)gridDim.x < nwork) {
+      nw = w + gridDim.x;
+      work_of(nw, gridDim.x, npair, a.B * a.H, nbh, npr);
+      nqt = nq - 1 - npr;
     }
+    run_tile(qt, bh, nqt, nbh);
+    if (nqt < 0) break;
+    w = nw;
+    bh = nbh;
+    pr = npr;
+    qt = nqt;
   }
 }
 
