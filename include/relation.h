@@ -51,6 +51,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; the entry points
+ * declared here are its only exports. */
+#pragma GCC visibility push(default)
+
 #define REL_MAX_HEADS 256
 
 typedef enum {
@@ -298,6 +302,8 @@ rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len,
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* relation_status_str(rel_status s);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }
