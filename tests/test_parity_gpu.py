@@ -271,6 +271,34 @@ def test_decode_ragged_lengths(D, dt):
         assert torch.equal(y[0].cpu(), inp["v"][0])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_large_evidence(D, dt):
+    """U ~ 30 between the new query and every cached key (correlated rows):
+    the split-length partials carry large, different maxima and the merge
+    must rescale them exactly; lengths span one to several partial blocks.
+    The fp32 bar is scaled by max|U| / 4, as for the forward."""
+    B, H, Lc = 4, 2, 2100
+    cfg = W.DecodeConfig("d", B, H, D, 0, Lc, Lc, dtype=dt, tau=0.7)
+    inp = W.make_decode_inputs(cfg, 70 + D)
+    inp["lens"] = np.array([1, 300, 1029, Lc], dtype=np.int32)
+    rng = np.random.default_rng(D)
+    tdt = W.torch_dtype(dt)
+    base = np.float32(np.sqrt(30.0 / np.sqrt(D)))
+    g = lambda *shape: torch.from_numpy((base + 0.4 * rng.standard_normal(shape)).astype(np.float32)).to(tdt)
+    inp["p1"], inp["p2"], inp["cache_P2"] = g(B, H, D), g(B, H, D), g(B, H, Lc, D)
+    inp["cache_V"] = torch.from_numpy(rng.standard_normal((B, H, Lc, D)).astype(np.float32)).to(tdt)
+    y = _gpu_decode(inp, 0.5)
+    ref = _oracle_decode(inp, 0.5)
+    if dt == "f32":
+        U = np.einsum("bhd,bhld->bhl", f64(inp["p1"]), f64(inp["cache_P2"])) / np.sqrt(D)
+        tol = 1e-5 * max(1.0, float(np.abs(U).max()) / 4.0)
+        err = row_normwise_err(f64(y), ref)
+        assert err <= tol, f"D={D}: fp32 row-normwise error {err:.3e} > {tol:.3e}"
+    else:
+        assert_parity(f64(y), ref, tdt, f"D={D} {dt}")
+
+
 def test_decode_clamps_out_of_range_lengths():
     """len[b] outside [0, L_cap] is clamped: -5 reads nothing, L_cap + 10 reads
     the whole cache."""
