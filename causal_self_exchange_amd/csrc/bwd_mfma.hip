@@ -23,7 +23,7 @@
 //   dV^T[d][key] += dY^T[d][q] F[q][key] and dP2^T[d][key] += P1^T[d][q] W[q][key]
 //   on v_mfma_f32_16x16x32_bf16, both accumulators in the wave. LDS per query
 //   tile: P1 and dY in one row layout plus the tile's row statistics; a ring
-//   of 3 tiles, one barrier per tile.
+//   of 4 tiles, one barrier per pair of tiles.
 // The Self entries (diagonal) enter in the epilogues from the prep's
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
 // permuted as {16 qb0 + 4 j + r, 16 qb1 + 4 j + r} for lane group j, the B
 // operand F[q][key] (or W) is the lane's own 8 weights, and the A operand
 // dY^T[d][q] (or P1^T) is two transposing reads of the same row layout. So a
-// tile needs P1 and dY in one layout only, and a ring of 3 tiles (99 KB at
-// d_h = 128) needs one barrier per tile.
+// tile needs P1 and dY in one layout only, and a ring of 4 tiles (132 KB at
+// d_h = 128) needs one barrier per pair of tiles.
 // The row layout here packs its 8-row blocks 1024 bytes apart (the forward's
 // 1152-byte stride suits the 32x32x16 read pattern only). Measured on gfx950:
 // a 16-byte LDS read serves, in each pass, the lane groups {0-7, 24-31},
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
 // the 16x16x32 A-operand read puts both groups of every pass on the same
 // banks (two-way conflicts, half the throughput), with 1024 bytes they fall
 // in opposite halves. The transposing reads are conflict-free with either.
-constexpr int kKvSlots = 3;
+constexpr int kKvSlots = 4;
 
 template <int D>
 struct KvCfg : TileLayout<D> {
@@ -298,8 +298,8 @@ struct KvCfg : TileLayout<D> {
   static constexpr int kBlk = 1024;                    // block stride of this layout
   static constexpr int kTileBytes = L::kBlocks * kBlk;
   // Waves per work-group (16 keys each): d_h = 128 takes 12 (three per SIMD
-  // in one work-group per CU, as the 99 KB ring admits); d_h = 64 takes 8,
-  // and its 51 KB ring lets two work-groups share a CU.
+  // in one work-group per CU, as the 132 KB ring admits); d_h = 64 takes 8,
+  // and its 68 KB ring lets two work-groups share a CU.
   static constexpr int kWaves = D == 128 ? 12 : 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kKeys = 16 * kWaves;    // keys per work-group
@@ -307,11 +307,9 @@ struct KvCfg : TileLayout<D> {
   static constexpr int kStatOff = 2 * kTileBytes;
   static constexpr int kSlotBytes = kStatOff + kStatTile * 4;
   static constexpr int kLdsBytes = kKvSlots * kSlotBytes;
-  // Wave w moves blocks w, w + kWaves, ... of each tensor's tile; the waits
-  // count the fewest loads any wave issues per tile, which is conservative
-  // for the others (and for wave 0, which also moves the statistics).
+  // Wave w moves blocks w, w + kWaves, ... of each tensor's tile (wave 0
+  // also the statistics).
   static constexpr int kPer = (L::kBlocks + kWaves - 1) / kWaves;
-  static constexpr int kDmaTile = 2 * (L::kBlocks / kWaves);
   static constexpr int kKs = D / 32;           // evidence k-steps
   static constexpr int kDb = D / 16;           // 16-row blocks of the transports
   // Byte offset of (row q, 16-byte chunk c) in a tile (blocks as in the
@@ -420,22 +418,26 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs 
     accV[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     accP[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // The first two query tiles; tile t + 2 is loaded from the start of tile
-  // t, into the slot of tile t - 1. The full wait before the loop covers the
-  // key rows too: the compiler sees only the key-row loads (the direct loads
-  // are inline assembly), and once it knows they have completed it puts no
-  // wait of its own inside the loop, where any vmcnt wait would also stall on
-  // the tiles in flight.
+  // The first two query tiles. Tiles go by pairs (t0 + 2n, t0 + 2n + 1):
+  // at the start of a pair the waves wait for its loads and meet, then load
+  // the next pair into the slots of the previous one; so one barrier serves
+  // two tiles. The full wait before the loop covers the key rows too: the
+  // compiler sees only the key-row loads (the direct loads are inline
+  // assembly), and once it knows they have completed it puts no wait of its
+  // own inside the loop, where any vmcnt wait would also stall on the tiles
+  // in flight.
   if (t0 < nt) dma(t0);
   if (t0 + 1 < nt) dma(t0 + 1);
   wait_vm_lgkm<0, 15>();
 
   auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
-    if (t + 1 < nt) wait_vm_lgkm<C::kDmaTile, 15>();
-    else wait_vm_lgkm<0, 15>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + 2 < nt) dma(t + 2);
+    if (((t - t0) & 1) == 0) {
+      wait_vm_lgkm<0, 15>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 2 < nt) dma(t + 2);
+      if (t + 3 < nt) dma(t + 3);
+    }
     const unsigned so = (unsigned)(((t - t0) % kKvSlots) * C::kSlotBytes);
     unsigned oe1 = so + eb, oe2 = so + C::kTileBytes + eb;  // P1 / dY evidence reads
     unsigned ot1 = so + tb, ot2 = so + C::kTileBytes + tb;  // P1 / dY transposing reads
