@@ -272,23 +272,42 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
 // Phase 2: per state element (b*H + h, r, col): Cin_0 = 0,
 // Cin_{c+1} = e^{b_last,c}[r] Cin_c + dC_c; each chunk slot is overwritten
 // with its entering state, and the final state goes to a.final (if given).
+// A thread owns 4 consecutive elements of one row r (16-byte accesses; the
+// state buffers are 16-byte aligned) and loads the contributions and decays
+// of kScanAhead chunks before it uses them, so that many loads are in flight
+// per thread.
+constexpr int kScanAhead = 8;
+
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
+  constexpr int kQ = D * D / 4;                 // 4-element groups per state
   const long long idx = (long long)blockIdx.x * kScanThreads + threadIdx.x;
-  if (idx >= (long long)a.B * a.H * D * D) return;
-  const int e = (int)(idx % (D * D));
-  const long long bh = idx / (D * D);
+  if (idx >= (long long)a.B * a.H * kQ) return;
+  const int e = 4 * (int)(idx % kQ);
+  const long long bh = idx / kQ;
   const int r = e / D;
   const int nc = (a.T + kL - 1) / kL;
-  float* st = a.state + (size_t)bh * nc * D * D + e;
+  float4* st = reinterpret_cast<float4*>(a.state + (size_t)bh * nc * D * D + e);
   const float* g = a.decay + (size_t)bh * nc * D + r;
-  float C = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float dc = st[(size_t)c * D * D];
-    st[(size_t)c * D * D] = C;
-    C = fmaf(g[(size_t)c * D], C, dc);
+  float4 C = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto step = [&](float4& slot, float4 dc, float gc) __attribute__((always_inline)) {
+    slot = C;
+    C = make_float4(fmaf(gc, C.x, dc.x), fmaf(gc, C.y, dc.y), fmaf(gc, C.z, dc.z), fmaf(gc, C.w, dc.w));
+  };
+  int c = 0;
+  for (; c + kScanAhead <= nc; c += kScanAhead) {
+    float4 dc[kScanAhead];
+    float gc[kScanAhead];
+#pragma unroll
+    for (int k = 0; k < kScanAhead; ++k) {
+      dc[k] = st[(size_t)(c + k) * kQ];
+      gc[k] = g[(size_t)(c + k) * D];
+    }
+#pragma unroll
+    for (int k = 0; k < kScanAhead; ++k) step(st[(size_t)(c + k) * kQ], dc[k], gc[k]);
   }
-  if (a.final) a.final[(size_t)bh * D * D + e] = C;
+  for (; c < nc; ++c) step(st[(size_t)c * kQ], st[(size_t)c * kQ], g[(size_t)c * D]);
+  if (a.final) *reinterpret_cast<float4*>(a.final + (size_t)bh * D * D + e) = C;
 }
 
 // Phase 3: per (b*H + h, chunk): Y = I + at I + Qt Cin, with
@@ -481,7 +500,7 @@ template <typename Tin, int D>
 hipError_t launch_typed(const LinArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nc = (a.T + kL - 1) / kL;
   const long long wg = (long long)a.B * a.H * nc;
-  const long long scan_threads = (long long)a.B * a.H * D * D;
+  const long long scan_threads = (long long)a.B * a.H * D * D / 4;
   if (wg > 0x7fffffffLL || (scan_threads + kScanThreads - 1) / kScanThreads > 0x7fffffffLL) return hipErrorInvalidValue;
   // The output kernel is persistent: one work-group per compute unit (its LDS
   // admits one).
