@@ -36,6 +36,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, s), s
 
 
+def test_library_exports_nothing_else():
+    """Internal functions are built with hidden visibility: the dynamic text
+    symbols of the library are exactly the declared entry points."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not available")
+    R.lib()
+    out = subprocess.run([nm, "-D", "--defined-only", R.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    text = {f[2] for f in (line.split() for line in out.splitlines()) if len(f) == 3 and f[1] == "T"}
+    assert text == set(declared_symbols()), sorted(text ^ set(declared_symbols()))
+
+
 def test_status_strings():
     lib = R.lib()
     for code in range(12):
