@@ -43,6 +43,7 @@ constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
 constexpr int kDqRows = kDqWaves * 32;     // query rows per dq work-group
 constexpr int kDqSlots = 3;
+static_assert(kDqRows == kPrepRows, "a dq work-group's rows are one (dtau, dlambda) partial chunk");
 
 template <int D>
 struct DqCfg : TileLayout<D> {
@@ -159,9 +160,62 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
       yf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdY, o, 0, 0));
     }
   }
+  // Row statistics of this work-group's rows, from the rows of P1, P2, V, Y
+  // and dY (each lane takes the dot products over its half of the columns):
+  //   L2_i = (LSE_i + lambda log i) log2 e,  D_i = dY_i . Y_i,
+  //   F_ii = e^{S_i - LSE_i},  dU_ii / sqrt(d_h) = F_ii (dY_i . V_i - D_i) S_i (1 - S_i) / (tau sqrt(d_h)),
+  // stored per 64-row tile for the key/value kernel (launched after this
+  // one), and this 256-row chunk's (dtau, dlambda) partial.
   const bool valid = qrow < T;
-  const float L2 = valid ? a.stats[stat_at(bh, nt, qrow, 0)] : INFINITY;
-  const float negD = valid ? a.stats[stat_at(bh, nt, qrow, 1)] : 0.0f;
+  float L2 = INFINITY, negD = 0.0f, us = 0.0f, ptau = 0.0f, plam = 0.0f;
+  {
+    const auto rY = rsrc(static_cast<const __bf16*>(a.Y) + head, head_bytes);
+    const auto rV = rsrc(V, head_bytes);
+    const auto rP2 = rsrc(P2, head_bytes);
+    const int qoff = qrow * (DR * 2) + hf * 16;
+    float dyy = 0.0f, dyv = 0.0f, p12 = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < DR / 16; ++ds) {
+      const bf16x8 y = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rY, qoff + ds * 32, 0, 0));
+      const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, qoff + ds * 32, 0, 0));
+      const bf16x8 p = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP2, qoff + ds * 32, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dyy = fmaf((float)yf[ds][e], (float)y[e], dyy);
+        dyv = fmaf((float)yf[ds][e], (float)v[e], dyv);
+        p12 = fmaf((float)qf[ds][e], (float)p[e], p12);
+      }
+    }
+    dyy = lane_pair_sum(dyy);
+    dyv = lane_pair_sum(dyv);
+    p12 = lane_pair_sum(p12);
+    float st[4] = {INFINITY, 0.0f, 0.0f, 0.0f};
+    if (valid) {
+      const float lse = a.lse[(size_t)bh * T + qrow];
+      const float logi = logf((float)(qrow + 1));
+      const float inv_tau = hp.inv_tau[bh % a.H];
+      const float u = p12 * hp.scale;                  // U_ii
+      const float S = sigmoid_f32(u * inv_tau);
+      const float Fs = expf(S - lse);                  // F_ii
+      const float dR = Fs * (dyv - dyy);               // dR_ii
+      const float sp = S * (1.0f - S);
+      L2 = (lse + hp.lambda * logi) * kLog2e;
+      negD = -dyy;
+      us = dR * sp * inv_tau * hp.scale;
+      st[0] = L2;
+      st[1] = negD;
+      st[2] = Fs;
+      st[3] = us;
+      if (hf == 0) {
+        ptau = dR * sp * (-u * inv_tau * inv_tau);
+        plam = logi * dR;
+      }
+    }
+    if (hf == 0 && qrow < nt * kStatRows) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a.stats[stat_at(bh, nt, qrow, k)] = st[k];
+    }
+  }
   f32x16 negDv;                                       // G^T accumulators start at -D_q
 #pragma unroll
   for (int r = 0; r < 16; ++r) negDv[r] = negD;
@@ -242,10 +296,33 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   for (; t < nsteady; ++t) tile(t, Tag<true>{});
   for (; t < ntiles; ++t) tile(t, Tag<false>{});
 
+  // The chunk's (dtau, dlambda) partial: a fixed-order sum over the rows.
+  {
+    __shared__ float red[2][kDqWaves];
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) {
+      ptau += __shfl_xor(ptau, w, 64);
+      plam += __shfl_xor(plam, w, 64);
+    }
+    if (lane == 0) {
+      red[0][wave] = ptau;
+      red[1][wave] = plam;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f, l = 0.0f;
+      for (int w = 0; w < kDqWaves; ++w) {
+        t += red[0][w];
+        l += red[1][w];
+      }
+      a.part[((size_t)bh * nq + qt) * 2 + 0] = t;
+      a.part[((size_t)bh * nq + qt) * 2 + 1] = l;
+    }
+  }
+
   if (!valid) return;
-  // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h); the statistic holds
+  // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h); us holds
   // dU_ii / sqrt(d_h). Lane holds columns 32 db + 8 g4 + 4 hf + 0..3.
-  const float us = a.stats[stat_at(bh, nt, qrow, 3)];
   const size_t ro = (size_t)qrow * DR;
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) {
@@ -542,8 +619,9 @@ hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kDqRows - 1) / kDqRows;
   using Ckv = KvCfg<D>;
   const int nk = (a.T + Ckv::kKeys - 1) / Ckv::kKeys;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(Ckv::kThreads), 0, s, a, hp);
+  // dq first: it writes the row statistics that dkv reads.
   hipLaunchKernelGGL((bwd_dq_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(Ckv::kThreads), 0, s, a, hp);
   return hipGetLastError();
 }
 

@@ -335,9 +335,14 @@ rel_status relation_bwd(const void* P1, const void* P2, const void* V, const flo
   float* part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::bwd_stat_floats(BH, T)) * sizeof(float)));
   rel::BwdArgs a{P1, P2, V, Y, dY, LSE, dP1, dP2, dV, dtau, dlambda, stats, part, B, H, T, d_h};
   const bool bf16 = dt == REL_BF16;
-  hipError_t e = rel::launch_bwd_prep(a, hp, bf16, stream);
-  if (e == hipSuccess)
-    e = use_bwd_mfma(dt, d_h, T) ? rel::launch_bwd_mfma_bf16(a, hp, stream) : rel::launch_bwd_scan(a, hp, bf16, stream);
+  hipError_t e;
+  if (use_bwd_mfma(dt, d_h, T)) {
+    // The MFMA query kernel forms the row statistics itself.
+    e = rel::launch_bwd_mfma_bf16(a, hp, stream);
+  } else {
+    e = rel::launch_bwd_prep(a, hp, bf16, stream);
+    if (e == hipSuccess) e = rel::launch_bwd_scan(a, hp, bf16, stream);
+  }
   if (e == hipSuccess) e = rel::launch_bwd_reduce(a, stream);
   return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
