@@ -8,15 +8,17 @@
 // g = dY_i . V_j per tile and form, for j < i,
 //   F_ij = 2^(SiLU(u) log2 e - L2_i),  L2_i = (LSE_i + lambda log i) log2 e,
 //   W_ij = F_ij (g - D_i) SiLU'(u)      (= dU_ij; SiLU'(u) = s (1 + u (1 - s)))
-// with the row statistics L2_i and D_i = dY_i . Y_i from the prep kernel
-// (the G accumulators start at -D_i, so the MFMA yields g - D_i directly).
+// with the row statistics L2_i and D_i = dY_i . Y_i (the G accumulators start
+// at -D_i, so the MFMA yields g - D_i directly).
 //
 // dq (query gradient): 8 waves x 32 query rows, key tiles of 64 rows; per tile
 //   U^T[key][q] = P2 . P1^T and G^T[key][q] = V . dY^T (evidence; P1 and dY
 //   rows of the wave's queries in registers), then
 //   dP1^T[d][q] += P2^T[d][key] W^T[key][q] (transport).
 //   LDS per key tile: P2 in the row layout and the transposed layout, V in
-//   the row layout; a ring of 3 tiles, one barrier per tile.
+//   the row layout; a ring of 3 tiles, one barrier per tile. dq runs first:
+//   its prologue forms the row statistics of its rows (stored per 64-row
+//   tile) and its epilogue the chunk's (dtau, dlambda) partial.
 // dkv (key/value gradients): 16 keys per wave, query tiles of 64 rows; per
 //   16-query block U[q][key] = P1 . P2^T and G[q][key] = dY . V^T (P2 and V
 //   rows of the wave's keys in registers), F and W, then
@@ -24,7 +26,7 @@
 //   on v_mfma_f32_16x16x32_bf16, both accumulators in the wave. LDS per query
 //   tile: P1 and dY in one row layout plus the tile's row statistics; a ring
 //   of 4 tiles, one barrier per pair of tiles.
-// The Self entries (diagonal) enter in the epilogues from the prep's
+// The Self entries (diagonal) enter in the epilogues from the row
 // statistics: dP1_i += dU_ii p2_i / sqrt(d_h), dP2_j += dU_jj p1_j / sqrt(d_h),
 // dV_j += F_jj dY_j.
 #include <type_traits>
