@@ -147,7 +147,7 @@ def bench_backward(torch, R, W, steps, warmup):
     per, total, _ = time_launches(fn, steps, warmup, torch)
     ms = total / steps
     flops = 5.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.d_h
-    return {"workload": "backward: B=1 H=32 T=8192 d_h=128 bf16, dY ~ N(0,1), seed 42 (prep + dq + dkv + reduce)",
+    return {"workload": "backward: B=1 H=32 T=8192 d_h=128 bf16, dY ~ N(0,1), seed 42 (dq with the row statistics, dkv, reduce)",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "flops_counted": flops}
