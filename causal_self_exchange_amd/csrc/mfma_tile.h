@@ -130,9 +130,14 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
 // compiler does not guard every later LDS read with a wait for all
 // outstanding loads; kernels wait for them explicitly before the barrier
 // that publishes the tile.
+// The compiler's hazard checks do not look inside inline assembly: the
+// descriptor SGPRs may have just been written by a VALU instruction (e.g.
+// restored from spill lanes by v_readlane), and a VMEM instruction that
+// reads a VALU-written SGPR needs 5 wait states on this architecture (an
+// SALU write of M0 before an LDS-DMA needs 1); s_nop 4 provides them.
 __device__ __forceinline__ void dma16(const u32x4& r, const char* lds, int voffset) {
   const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ float lane_pair_max(float v) {
