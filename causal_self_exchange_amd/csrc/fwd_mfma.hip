@@ -20,9 +20,15 @@
 // They run as a software pipeline over blocks: one block step issues the
 // MFMAs of E(b+1) and T(b-1), alternating, while the VALU forms W(b) in two
 // stages (2^-a and the reciprocal of one score, then the weight of the
-// previous one); operand reads run two MFMAs ahead, also across the tile
-// barrier. Two block steps make one iteration over a 64-key tile; every
-// iteration ends with one barrier.
+// previous one); operand reads run two MFMAs ahead, also across tiles. Two
+// block steps make one iteration over a 64-key tile.
+//
+// The waves do not meet at a barrier per iteration: each one counts its
+// finished iterations in an LDS counter, and a wave waits only where it
+// refills the ring, between its two block steps, until every wave has
+// finished the previous iteration (so the slots it overwrites are no longer
+// read and the tiles it reads next have landed). The waves of a SIMD may thus
+// drift apart by up to an iteration and a half and keep both issuing.
 //
 // Two variants share the code:
 //   relation_fwd / relation_fwd_ex (kLse = false): P1 is scaled by
@@ -81,7 +87,8 @@ struct Cfg : TileLayout<D> {
   static constexpr int kKRing = kKSlots * L::kKBytes;
   static constexpr int kVRing = kVSlots * L::kVBytes;
   // + one block that absorbs direct loads of V tiles past the last one
-  // needed (so the ring keeps the work-group's own rows), + 8 wave flags.
+  // needed (so the ring keeps the work-group's own rows), + 8 wave flags and
+  // the iteration counter.
   static constexpr int kLdsBytes = kKRing + kVRing + L::kVBlock + 64;
   static constexpr int kDmaPerWave = L::kBlocks / kWaves;   // blocks per wave per tile and operand
   static constexpr int kSteps = 2 * L::kDs;                 // MFMA steps per block (evidence + transport)
@@ -135,6 +142,65 @@ __device__ __forceinline__ float diag_entry(const f32x16& s, int hf, int lq) {
   return ((lq >> 2) & 1) == hf ? v : 0.0f;
 }
 
+// Lane index read afresh (v_mbcnt) wherever it is used: the optimiser cannot
+// merge the reads, so no lane-derived value has to stay live (or be spilled)
+// across the key loop just to be used again after it.
+__device__ __forceinline__ int lane_now() {
+  unsigned l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return (int)l;
+}
+
+// LDS counter increment by lane 0 of the calling wave (exec narrowed to that
+// lane inside the statement, so no branch splits the caller's code). The
+// s_nop separates the VALU write of the data VGPR from the LDS instruction
+// that reads it, as the compiler does for its own code (its hazard checks do
+// not look inside inline assembly).
+__device__ __forceinline__ void lds_count_up(unsigned* p) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned*)p;
+  unsigned long long save;
+  unsigned one;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "v_mov_b32 %1, 1\n\t"
+      "s_nop 1\n\t"
+      "ds_add_u32 %2, %1\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(save), "=&v"(one)
+      : "v"(addr)
+      : "memory");
+}
+
+// Wait until the LDS counter *p has reached `want` (wrapping compare),
+// polling with a short sleep between reads. The loop is one assembly
+// statement: the compiler sees no basic-block boundary and moves no code into
+// or across it. Its hazard checks do not look inside the statement either:
+// v_readfirstlane reading a VGPR that the previous VALU instruction wrote
+// needs a wait state on this architecture (without it the read can return
+// the VGPR's older value), so the read is preceded by s_nop although here the
+// VGPR comes from an LDS load. (An SALU read of an SGPR that v_readfirstlane
+// wrote needs none.)
+__device__ __forceinline__ void lds_wait_count(const unsigned* p, unsigned want) {
+  const unsigned addr = (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned*)p;
+  unsigned v, d;
+  asm volatile(
+      "1:\n\t"
+      "ds_read_b32 %0, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 1\n\t"
+      "v_readfirstlane_b32 %1, %0\n\t"
+      "s_sub_u32 %1, %1, %3\n\t"
+      "s_cmp_lt_i32 %1, 0\n\t"
+      "s_cbranch_scc0 2f\n\t"
+      "s_sleep 1\n\t"
+      "s_branch 1b\n"
+      "2:"
+      : "=&v"(v), "=&s"(d)
+      : "v"(addr), "s"(want)
+      : "memory", "scc");
+}
+
 // Block roles of one step: weights off, full, or on the diagonal block.
 enum : int { kWOff = 0, kWFull = 1, kWDiag = 2 };
 template <bool kE, int kW, bool kT>
@@ -160,14 +226,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   char* const vbase = smem + C::kKRing;           // V ring
   char* const vsink = vbase + C::kVRing;
   int* const flags = reinterpret_cast<int*>(vsink + C::kVBlock);
+  // done_iters counts the iterations the waves have finished (one increment
+  // per wave and iteration, the pre-step of a tile included); `arrived` is its
+  // value once every wave has finished what this wave has. Neither is ever
+  // reset: they wrap, and only differences are compared.
+  unsigned* const done_iters = reinterpret_cast<unsigned*>(flags + kWaves);
+  unsigned arrived = 0;
 
   const int T = a.T;
   const int nq = (T + kBM - 1) / kBM;
   const int tid = threadIdx.x;
+  if (tid == 0) *done_iters = 0u;   // ordered before any use by the first tile's barrier
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int lq = lane & 31;                       // query (column) within the wave
-  const int hf = lane >> 5;                       // lane half
+  // Lane l holds query (column) lq = l % 32 of the wave's rows, lane half
+  // hf = l / 32; both are formed from lane_now() where they are used.
   const float k2 = hp.scale * kLog2e;             // raw dot -> log2-domain evidence
 
   // A operand of the row-sum MFMA (16x16x32, the weights as B operand): with
@@ -175,18 +247,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // sum over both lane halves of query l % 32, i.e. its own row sum.
   bf16x8 sel;
   {
+    const int lane = lane_now();
     const __bf16 v = (((lane >> 2) ^ (lane >> 4)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sel[e] = v;
   }
 
   // P1 rows of a query tile as the evidence MFMA's B operand: lane holds
-  // p1[qrow][16 ds + 8 hf + 0..7]. They are loaded one tile ahead, before the
-  // previous tile's epilogue, so their latency hides behind it.
+  // p1[qrow][16 ds + 8 hf + 0..7]. They are loaded at the end of the previous
+  // tile, so their latency overlaps that of the next tile's first key tiles
+  // (loading them earlier would hold them through the epilogue, where any
+  // wait on vector memory would also wait for them).
   bf16x8 qf[C::kDs];
   auto load_q = [&](int qt, int bh) __attribute__((always_inline)) {
     const auto rP1 = rsrc(static_cast<const __bf16*>(a.P1) + (size_t)bh * (size_t)T * DR, (long long)T * DR * 2);
-    const int qoff = (qt * kBM + wave * 32 + lq) * (DR * 2) + hf * 16;
+    const int lane = lane_now();
+    const int qoff = (qt * kBM + wave * 32 + (lane & 31)) * (DR * 2) + (lane >> 5) * 16;
 #pragma unroll
     for (int ds = 0; ds < C::kDs; ++ds) {
       // k-steps past DR / 16 cover padded columns: out-of-range offsets read 0.
@@ -196,8 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   };
 
   // One query tile (256 rows) of one head, start to finish; then, when nqt >=
-  // 0, the P1 rows of query tile nqt of head nbh are loaded before the
-  // epilogue.
+  // 0, the P1 rows of query tile nqt of head nbh are loaded.
   auto run_tile = [&](int qt, int bh, int nqt, int nbh) __attribute__((always_inline)) {
   const int h = bh % a.H;
   const size_t head = (size_t)bh * (size_t)T * DR;
@@ -208,7 +283,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const auto rY = rsrc(Y, head_bytes);
 
   const int q0 = qt * kBM;
-  const int qrow = q0 + wave * 32 + lq;           // may be >= T: loads give 0, stores drop
   // Iterations: 64-key tiles up to the tile's last row.
   const int kend = min(q0 + kBM, T) - 1;
   const int J = kend / kBN + 1;
@@ -222,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // go to the sink block, so the ring keeps the last real ones.
   const int hb = (int)head_bytes;
   int dma_koff[C::kDmaPerWave], dma_voff[C::kDmaPerWave];
+  const int lane = lane_now();
 #pragma unroll
   for (int u = 0; u < C::kDmaPerWave; ++u) {
     const int k = wave + kWaves * u;
@@ -283,7 +358,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     using K = decltype(kind);
     float tv[16];
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (K::W == kWDiag) dself = diag_entry(sW, hf, lq);
+    int lq = 0, hf = 0;
+    if constexpr (K::W == kWDiag) {
+      const int ln = lane_now();
+      lq = ln & 31;
+      hf = ln >> 5;
+      dself = diag_entry(sW, hf, lq);
+    }
     // Weight of score n in two stages: tv = 1 / (1 + 2^-a), then
     // w = 2^(a tv - m2), masked on the diagonal block, packed in pairs.
     auto front = [&](int n) {
@@ -340,16 +421,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   };
   using SFull = StepKind<true, kWFull, true>;
 
-  // Iteration end: wait for the previous iteration's direct loads (vector
-  // memory operations complete in order, so vmcnt <= this iteration's count
-  // suffices) and for every LDS read but the next iteration's first operands,
-  // then meet the other waves.
-  auto finish = [&]() __attribute__((always_inline)) {
+  // Ring hand-over without a barrier (done_iters / arrived above).
+  // An iteration ends once the wave's direct loads of the previous iteration
+  // have landed (vector memory operations complete in order, so vmcnt <= this
+  // iteration's count suffices) and all its LDS reads but the next
+  // iteration's first operands are done.
+  auto arrive = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     wait_vm_lgkm<kDmaIter, 3>();
-    __builtin_amdgcn_s_barrier();
+    lds_count_up(done_iters);
+    arrived += kWaves;
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Iteration j, between its block steps: once every wave has finished
+  // iteration j - 1 or the pre-step (so it read the slots of P2 tile j and V tile j - 1 for
+  // the last time, and its loads of P2 tile j + 3 and V tile j + 2 landed),
+  // load P2 tile j + 4 and V tile j + 3 into those slots. The slowest wave
+  // never waits here, so the wait always ends.
+  auto refill = [&](int jj) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    lds_wait_count(done_iters, arrived);
+    dma_k(jj + 4, jj & (kKSlots - 1));
+    dma_v(jj + 3);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -400,57 +496,71 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
         step(StepKind<false, kWDiag, false>{}, sB, sA, pB, pA, k0, 1, v0, 0, k1, 0, v0, 0);
       }
       // Iteration 0 loads P2 tile 4 into slot 0, which E(0) and the pre-step
-      // read: every wave must be done with it first (all LDS reads but the
-      // next three operands complete, then meet).
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      wait_vm_lgkm<63, 3>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
+      // read: the pre-step counts as an iteration.
+      arrive();
     }
 
     // Iteration j reads P2 tile j+1 and V tile j (and, in its last two
-    // steps, the first operands of P2 tile j+2 and V tile j+1); it issues the
-    // direct loads of P2 tile j+4 into the slot of tile j and of V tile j+3
-    // into the slot of tile j-1, both last read in iteration j-1. The barrier
-    // at its end publishes the tiles loaded in iteration j-1.
+    // steps, the first operands of P2 tile j+2 and V tile j+1); between its
+    // block steps it loads P2 tile j+4 into the slot of tile j and V tile j+3
+    // into the slot of tile j-1, both last read in iteration j-1.
     // A wave's steady iterations are those with 2j+3 <= dblk (every block
     // role full; E(dblk) is an ordinary evidence block).
     const int jsteady = dblk >= 3 ? min(J, (dblk - 3) / 2 + 1) : 0;
     int j = 0;
     for (; j < jsteady; ++j) {
-      dma_k(j + 4, j & (kKSlots - 1));
-      dma_v(j + 3);
       const char* ka = kslot(j + 1);
       const char* kn = kslot(j + 2);
       const VBase va = vslot(j);
       const VBase vn = vslot(j + 1);
       step(SFull{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
+      refill(j);
       step(SFull{}, sB, sA, pB, pA, ka, 1, va, 1, kn, 0, vn, 0);
-      finish();
+      arrive();
+    }
+    // The diagonal block relative to the next iteration: r = dblk - 2j is 1
+    // or 2 after the steady iterations (the diagonal block's tile dblk / 2 is
+    // at most J - 1), dblk itself when there were none, negative for a wave
+    // whose rows all lie past T. What is left is straight-line: at most two
+    // iterations with work, then iterations that only move tiles.
+    const int r = dblk - 2 * j;
+    if (r == 2) {
+      {
+        const char* ka = kslot(j + 1);
+        const VBase va = vslot(j);
+        step(SFull{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
+        refill(j);
+        step(StepKind<false, kWDiag, true>{}, sB, sA, pB, pA, ka, 1, va, 1, kslot(j + 2), 0, vslot(j + 1), 0);
+        arrive();
+        ++j;
+      }
+      {
+        const char* ka = kslot(j + 1);
+        const VBase va = vslot(j);
+        step(StepKind<false, kWOff, true>{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
+        refill(j);
+        arrive();
+        ++j;
+      }
+    } else if (r == 1) {
+      const char* ka = kslot(j + 1);
+      const VBase va = vslot(j);
+      step(StepKind<false, kWDiag, true>{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
+      refill(j);
+      step(StepKind<false, kWOff, true>{}, sB, sA, pB, pA, ka, 1, va, 1, kslot(j + 2), 0, vslot(j + 1), 0);
+      arrive();
+      ++j;
+    } else if (r == 0) {
+      const char* ka = kslot(j + 1);
+      const VBase va = vslot(j);
+      step(StepKind<false, kWOff, true>{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
+      refill(j);
+      arrive();
+      ++j;
     }
     for (; j < J; ++j) {
-      dma_k(j + 4, j & (kKSlots - 1));
-      dma_v(j + 3);
-      const char* ka = kslot(j + 1);
-      const char* kn = kslot(j + 2);
-      const VBase va = vslot(j);
-      const VBase vn = vslot(j + 1);
-      const int r = dblk - 2 * j;                // the diagonal block relative to this tile
-      if (r >= 3) {
-        step(SFull{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
-        step(SFull{}, sB, sA, pB, pA, ka, 1, va, 1, kn, 0, vn, 0);
-      } else if (r == 2) {
-        step(SFull{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
-        step(StepKind<false, kWDiag, true>{}, sB, sA, pB, pA, ka, 1, va, 1, kn, 0, vn, 0);
-      } else if (r == 1) {
-        step(StepKind<false, kWDiag, true>{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
-        step(StepKind<false, kWOff, true>{}, sB, sA, pB, pA, ka, 1, va, 1, kn, 0, vn, 0);
-      } else if (r == 0) {
-        step(StepKind<false, kWOff, true>{}, sA, sB, pA, pB, ka, 0, va, 0, ka, 1, va, 1);
-      }
-      finish();
+      refill(j);
+      arrive();
     }
     // The last iterations' direct loads (of tiles past the end) must land
     // before the ring is reused.
@@ -465,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
       for (int r = 0; r < 16; ++r) omax = fmaxf(omax, fabsf(o[db][r]));
     const bool ok = lrow <= kFinite && omax < INFINITY;
     const bool wave_bad = __any(!ok);
-    if (lane == 0) flags[wave] = wave_bad ? 1 : 0;
+    if (lane_now() == 0) flags[wave] = wave_bad ? 1 : 0;
     __syncthreads();
     int any_bad = 0;
 #pragma unroll
@@ -477,6 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     // Redo: an evidence-only pass over the history finds each row's maximum
     // a (the first row has none: its offset stays 0).
     float amax = -INFINITY;
+    const int lq = lane_now() & 31, hf = lane_now() >> 5;
     for (int t = 0; t < J; ++t) {
       dma_k(t, 0);
       wait_vm_lgkm<0, 15>();
@@ -498,6 +609,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   // V_i of this lane's row from the V ring (tile qrow / 64 is among the last
   // four loaded): columns 32 db + 8 g4 + 4 hf .. +3, i.e. half hf of chunk
   // 4 db + g4 of row qrow % 64 in the block layout.
+  const int lq = lane_now() & 31, hf = lane_now() >> 5;
+  const int qrow = q0 + wave * 32 + lq;           // may be >= T: the stores drop it
   bf16x4 vv[C::kDb][4];
   {
     const int r = qrow & (kBN - 1);
@@ -511,13 +624,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
         vv[db][g4] = *reinterpret_cast<const bf16x4*>(vrow + C::kVBlock * 8 * (c >> 3) + 16 * (8 * (r & 7) + ((c & 7) ^ sw)));
       }
   }
-  // Every wave's reads are done before the next tile's loads refill the ring.
-  wait_vm_lgkm<63, 0>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  if (nqt >= 0) load_q(nqt, nbh);
-  __builtin_amdgcn_sched_barrier(0);
 
   // ---- epilogue -------------------------------------------------------------
   const float lrow = kLse ? lane_pair_sum(lsum) : l16[0];
@@ -525,7 +631,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   const float S = sigmoid_f32(uii * inv_tau);
   const RowCombine c(S, m2 * kLn2, lrow, hp.lambda * logf((float)(qrow + 1)));
   if (kLse && hf == 0 && qrow < T) a.lse[(size_t)bh * T + qrow] = c.lse;
-  const int roff = qrow * (DR * 2) + hf * 8;
+  // The rows of Y pass through LDS, so that each store writes whole rows:
+  // the P2 ring is free once every wave has left the key loop, and each wave
+  // uses its own part of it (32 rows of 2 D + 16 bytes; the 16 bytes of
+  // padding spread a column's rows over the banks).
+  constexpr int kYStride = 2 * D + 16;
+  static_assert(kWaves * 32 * kYStride <= C::kKRing, "Y staging fits in the P2 ring");
+  char* const ystage = kbase + wave * 32 * kYStride;
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) {
 #pragma unroll
@@ -534,9 +646,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
       bf16x4 yy;
 #pragma unroll
       for (int e = 0; e < 4; ++e) yy[e] = (__bf16)(c.w_self * (float)vv[db][g4][e] + c.w_hist * o[db][4 * g4 + e]);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yy), rY, roff + (32 * db + 8 * g4) * 2, 0, 0);
+      *reinterpret_cast<bf16x4*>(ystage + lq * kYStride + 2 * (32 * db + 8 * g4 + 4 * hf)) = yy;
     }
   }
+  // A wave reads back only what its own lanes wrote (its LDS operations
+  // complete in order; the wave barrier only marks the dependence between
+  // lanes): 16-byte chunk ch of rows 64 / (D / 8) apart per store, so one
+  // store covers 64 / (D / 8) whole rows; chunks past DR are not stored, nor
+  // rows >= T (outside the descriptor's range).
+  __builtin_amdgcn_wave_barrier();
+  {
+    constexpr int kC = D / 8;
+    constexpr int kRows = 64 / kC;
+    const int ln = lane_now();
+    const int ch = ln % kC, rs = ln / kC;
+#pragma unroll
+    for (int i = 0; i < 32 / kRows; ++i) {
+      const int rr = i * kRows + rs;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ystage + rr * kYStride + 16 * ch);
+      const int off = ch < DR / 8 ? (q0 + wave * 32 + rr) * (DR * 2) + 16 * ch : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rY, off, 0, 0);
+    }
+  }
+  // Every wave is done with both rings (V_i, Y staging) before the next
+  // tile's loads refill them.
+  wait_vm_lgkm<63, 0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if (nqt >= 0) load_q(nqt, nbh);
   };
 
   const int npair = (nq + 1) / 2;
