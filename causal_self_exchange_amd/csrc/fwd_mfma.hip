@@ -271,6 +271,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     }
   };
 
+  // Scale the query rows by log2 e / sqrt(d_h) (bf16, round to nearest even).
+  auto prescale_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ds = 0; ds < C::kDs; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ds][e] = (__bf16)((float)qf[ds][e] * k2);
+  };
+
   // One query tile (256 rows) of one head, start to finish; then, when nqt >=
   // 0, the P1 rows of query tile nqt of head nbh are loaded.
   auto run_tile = [&](int qt, int bh, int nqt, int nbh) __attribute__((always_inline)) {
@@ -457,13 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     for (int t = 0; t < 3; ++t) dma_v(t);
     wait_vm_lgkm<0, 15>();
     __syncthreads();
-    if (!kLse && pass == 0) {
-      // Scale the query rows by log2 e / sqrt(d_h) (bf16, round to nearest even).
-#pragma unroll
-      for (int ds = 0; ds < C::kDs; ++ds)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ds][e] = (__bf16)((float)qf[ds][e] * k2);
-    }
+    if (!kLse && pass == 0) prescale_q();   // the redo scales its own reload
 #pragma unroll
     for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
@@ -585,7 +587,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     if (!any_bad || pass == 1) break;
 
     // Redo: an evidence-only pass over the history finds each row's maximum
-    // a (the first row has none: its offset stays 0).
+    // a (the first row has none: its offset stays 0). The P1 rows are loaded
+    // (and scaled) again here rather than kept live through the end of the
+    // scan, which would hold their registers in every tile.
+    load_q(qt, bh);
+    wait_vm_lgkm<0, 15>();
+    if (!kLse) prescale_q();
     float amax = -INFINITY;
     const int lq = lane_now() & 31, hf = lane_now() >> 5;
     for (int t = 0; t < J; ++t) {

@@ -185,15 +185,27 @@ def test_bwd_scan_kernels_bf16(D):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_fwd_lse_output_equals_plain_forward(dt):
-    """relation_fwd_lse returns the same Y as relation_fwd_ex, bit for bit."""
+def test_fwd_lse_output_matches_plain_forward(dt):
+    """relation_fwd_lse and relation_fwd_ex compute the same Y. In fp32 both
+    run the same arithmetic, bit for bit. In bf16 the training variant forms
+    the evidence in fp32 and sums the row from the fp32 weights (its log
+    normaliser feeds the backward), while the plain forward scales P1 by
+    log2 e / sqrt(d_h) in bf16 and sums the row from the bf16 weights; each
+    must meet the bf16 bar against the fp64 oracle, and so the two differ by
+    at most twice that bar."""
     cfg = W.FwdConfig("t", 2, 3, 333, 128, dt, tau=("uniform", 0.5, 2.0), lam=0.5)
     inp = W.make_fwd_inputs(cfg, 3)
     P1, P2, V = _dev(inp, ("P1", "P2", "V"))
     Y1 = R.fwd(P1, P2, V, inp["tau"], 0.5)
     Y2, _ = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
     torch.cuda.synchronize()
-    assert torch.equal(Y1, Y2)
+    if dt == "f32":
+        assert torch.equal(Y1, Y2)
+        return
+    ref = O.relation_fwd(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), inp["tau"], 0.5)
+    for Y in (Y1, Y2):
+        assert float(np.max(np.abs(f64(Y) - ref))) <= TOL["bf16"]
+    assert float((Y1.float() - Y2.float()).abs().max()) <= 2 * TOL["bf16"]
 
 
 def test_bwd_single_token_passes_dY_to_dV():
