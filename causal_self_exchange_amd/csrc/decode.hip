@@ -46,11 +46,24 @@ __device__ __forceinline__ Vec16<Tin> load16(const Tin* p) {
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// Lanes per cached row: 16-byte loads cover D / VEC lanes, rounded up to a
+// power of two for the shuffle reduction (for d_h = 48 and 80 the lanes past
+// the row load nothing and hold zeros); GROUPS rows per step of a work-group.
+template <typename Tin, int D>
+struct DecodeGeom {
+  static constexpr int VEC = 16 / (int)sizeof(Tin);
+  static constexpr int LIVE = D / VEC;
+  static constexpr int LPR = LIVE <= 4 ? 4 : (LIVE <= 8 ? 8 : (LIVE <= 16 ? 16 : 32));
+  static constexpr int GROUPS = kPartialThreads / LPR;
+  static_assert(D % VEC == 0 && LIVE <= 32, "row layout");
+};
+
 template <typename Tin, int D>
 __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeArgs a, HeadParams hp) {
-  constexpr int VEC = 16 / sizeof(Tin);
-  constexpr int LPR = D / VEC;                      // lanes per cached row
-  constexpr int GROUPS = kPartialThreads / LPR;     // rows in flight per step
+  using G = DecodeGeom<Tin, D>;
+  constexpr int VEC = G::VEC;
+  constexpr int LPR = G::LPR;                       // lanes per cached row
+  constexpr int GROUPS = G::GROUPS;                 // rows in flight per step
   __shared__ float s_m[GROUPS];
   __shared__ float s_l[GROUPS];
   __shared__ float s_z[GROUPS][D + 1];
@@ -63,16 +76,18 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
   const int tid = threadIdx.x;
   const int g = tid / LPR;
   const int sl = tid % LPR;
+  const bool live = sl < G::LIVE;                   // lanes past the row read its start, weighted 0
+  const int so = live ? sl * VEC : 0;
   const size_t bh = (size_t)b * a.H + h;
-  const Tin* p1 = static_cast<const Tin*>(a.p1) + bh * D + sl * VEC;
-  const Tin* cP2 = static_cast<const Tin*>(a.cP2) + bh * (size_t)a.L_cap * D + sl * VEC;
-  const Tin* cV = static_cast<const Tin*>(a.cV) + bh * (size_t)a.L_cap * D + sl * VEC;
+  const Tin* p1 = static_cast<const Tin*>(a.p1) + bh * D + so;
+  const Tin* cP2 = static_cast<const Tin*>(a.cP2) + bh * (size_t)a.L_cap * D + so;
+  const Tin* cV = static_cast<const Tin*>(a.cV) + bh * (size_t)a.L_cap * D + so;
 
   float q[VEC], z[VEC];
   {
     const Vec16<Tin> t = load16(p1);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) { q[e] = to_f32(t.v[e]); z[e] = 0.0f; }
+    for (int e = 0; e < VEC; ++e) { q[e] = live ? to_f32(t.v[e]) : 0.0f; z[e] = 0.0f; }
   }
   const float k2 = hp.scale * kLog2e;               // raw dot -> log2-domain evidence
   float m2 = 0.0f, l = 0.0f;                        // stabiliser (log2 domain), row sum
@@ -114,8 +129,10 @@ __global__ __launch_bounds__(kPartialThreads) void decode_partial_kernel(DecodeA
   const float m = m2 * kLn2;                        // natural-log stabiliser of this group
 
   if (sl == 0) { s_m[g] = m; s_l[g] = l; }
+  if (live) {
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) s_z[g][sl * VEC + e] = z[e];
+    for (int e = 0; e < VEC; ++e) s_z[g][sl * VEC + e] = z[e];
+  }
   __syncthreads();
 
   float* out = a.ws + (bh * a.n_chunks + chunk) * (size_t)(D + 2);
@@ -151,7 +168,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, HeadPara
     p2v[t] = k < D ? to_f32(p2[k]) : 0.0f;
     vv[t] = k < D ? to_f32(v[k]) : 0.0f;
   }
-  constexpr int GROUPS = kPartialThreads / (D / (16 / (int)sizeof(Tin)));   // rows per block
+  constexpr int GROUPS = DecodeGeom<Tin, D>::GROUPS;                         // rows per block
   const int L = clamp_len(a.len[b], a.L_cap);
   // Work-groups that found rows (and wrote a state).
   const int nch = min(a.n_chunks, (L + GROUPS - 1) / GROUPS);
@@ -230,7 +247,9 @@ hipError_t launch_decode_typed(const DecodeArgs& a, const HeadParams& hp, hipStr
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s) {
   switch (a.d_h) {
     case 32: return bf16 ? launch_decode_typed<__bf16, 32>(a, hp, s) : launch_decode_typed<float, 32>(a, hp, s);
+    case 48: return bf16 ? launch_decode_typed<__bf16, 48>(a, hp, s) : launch_decode_typed<float, 48>(a, hp, s);
     case 64: return bf16 ? launch_decode_typed<__bf16, 64>(a, hp, s) : launch_decode_typed<float, 64>(a, hp, s);
+    case 80: return bf16 ? launch_decode_typed<__bf16, 80>(a, hp, s) : launch_decode_typed<float, 80>(a, hp, s);
     case 128: return bf16 ? launch_decode_typed<__bf16, 128>(a, hp, s) : launch_decode_typed<float, 128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }

@@ -3,10 +3,12 @@
 // Every check runs before any HIP call, so an invalid call launches nothing.
 #include "relation.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "rel_internal.h"
 
@@ -58,13 +60,28 @@ rel_status pack_heads(HeadParams& hp, const float* tau, int H, int d_h, float la
   return REL_OK;
 }
 
+// Kernel selection (relation_select_kernels): process-wide, initialised once
+// from RELATION_FWD_KERNEL / RELATION_BWD_KERNEL.
+std::atomic<int> g_fwd_kernel{REL_KERNEL_AUTO}, g_bwd_kernel{REL_KERNEL_AUTO};
+std::once_flag g_kernel_env_once;
+
+void read_kernel_env() {
+  std::call_once(g_kernel_env_once, [] {
+    auto scan = [](const char* name) {
+      const char* v = std::getenv(name);
+      return v && std::strcmp(v, "scan") == 0;
+    };
+    if (scan("RELATION_FWD_KERNEL")) g_fwd_kernel.store(REL_KERNEL_SCAN, std::memory_order_relaxed);
+    if (scan("RELATION_BWD_KERNEL")) g_bwd_kernel.store(REL_KERNEL_SCAN, std::memory_order_relaxed);
+  });
+}
+
 // Which forward kernel runs: the MFMA kernel for bf16 where it exists, else
-// the row-scan kernel. RELATION_FWD_KERNEL=scan forces the row-scan kernel
-// (used to time and test it on its own).
+// the row-scan kernel (always, once REL_KERNEL_SCAN is selected).
 bool use_mfma(rel_dtype dt, int d_h, int T) {
   if (dt != REL_BF16 || !rel::fwd_mfma_supported(d_h, T)) return false;
-  const char* env = std::getenv("RELATION_FWD_KERNEL");
-  return !(env && std::strcmp(env, "scan") == 0);
+  read_kernel_env();
+  return g_fwd_kernel.load(std::memory_order_relaxed) != REL_KERNEL_SCAN;
 }
 
 // Forward with an optional row log-normaliser output (lse may be null).
@@ -96,11 +113,11 @@ rel_status fwd_impl(const void* P1, const void* P2, const void* V, const float* 
 }
 
 // Which backward runs: the MFMA kernels for bf16 where they exist, else the
-// row-scan kernels. RELATION_BWD_KERNEL=scan forces the row-scan kernels.
+// row-scan kernels (always, once REL_KERNEL_SCAN is selected).
 bool use_bwd_mfma(rel_dtype dt, int d_h, int T) {
   if (dt != REL_BF16 || !rel::bwd_mfma_supported(d_h, T)) return false;
-  const char* env = std::getenv("RELATION_BWD_KERNEL");
-  return !(env && std::strcmp(env, "scan") == 0);
+  read_kernel_env();
+  return g_bwd_kernel.load(std::memory_order_relaxed) != REL_KERNEL_SCAN;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -167,6 +184,7 @@ const char* relation_status_str(rel_status s) {
     case REL_E_WORKSPACE: return "workspace missing or too small";
     case REL_E_LAUNCH: return "kernel launch failed";
     case REL_E_PRESTEP: return "invalid rotary mode, base, pairing or Givens angle";
+    case REL_E_KERNEL: return "unknown kernel selection";
   }
   return "unknown status";
 }
@@ -231,14 +249,15 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I, con
     return REL_E_ALIAS;
   if (LSE) {
     const size_t lb = static_cast<size_t>(B) * H * T * sizeof(float);
+    if (!aligned4(LSE)) return REL_E_ALIGN;
     if (overlaps(LSE, lb, P1, tb) || overlaps(LSE, lb, P2, tb) || overlaps(LSE, lb, I, tb) ||
-        overlaps(LSE, lb, workspace, need))
+        overlaps(LSE, lb, Y, tb) || overlaps(LSE, lb, workspace, need) ||
+        (pos0 && overlaps(LSE, lb, pos0, static_cast<size_t>(B) * 4)))
       return REL_E_ALIAS;
   }
   HeadParams hp;
   st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
-  if (LSE && !aligned4(LSE)) return REL_E_ALIGN;
   if (rel::launch_prestep(a, pp, dt == REL_BF16, stream) != hipSuccess) return REL_E_LAUNCH;
   return fwd_impl(ws, ws + part, ws + 2 * part, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
 }
@@ -354,7 +373,7 @@ rel_status relation_fwd(const void* P1, const void* P2, const void* V, const flo
 
 size_t relation_decode_workspace_bytes(int B, int H, int L_cap, int d_h) {
   int64_t n = 0;
-  if (!count(n, {B, H, L_cap, d_h}) || !head_dim_ok(d_h)) return 0;
+  if (!count(n, {B, H, L_cap, d_h}) || !fwd_head_dim_ok(d_h)) return 0;
   const int64_t chunks = (L_cap + rel::kDecodeChunk - 1) / rel::kDecodeChunk;
   return static_cast<size_t>(B) * H * chunks * (d_h + 2) * sizeof(float);
 }
@@ -369,7 +388,7 @@ rel_status relation_decode(const void* p1, const void* p2, const void* v, const 
       B > 65535)
     return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
-  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!fwd_head_dim_ok(d_h)) return REL_E_HEADDIM;
   HeadParams hp;
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
@@ -406,7 +425,7 @@ rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len, co
       B > 65535)
     return REL_E_SHAPE;
   if (!dtype_ok(dt)) return REL_E_DTYPE;
-  if (!head_dim_ok(d_h)) return REL_E_HEADDIM;
+  if (!fwd_head_dim_ok(d_h)) return REL_E_HEADDIM;
   if (!aligned16(cache_P2) || !aligned16(cache_V) || !aligned16(p2) || !aligned16(v) ||
       (reinterpret_cast<uintptr_t>(len) & 3u))
     return REL_E_ALIGN;
@@ -424,3 +443,12 @@ rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len, co
 }
 
 }  // extern "C"
+
+rel_status relation_select_kernels(rel_kernel fwd, rel_kernel bwd) {
+  auto ok = [](int k) { return k == REL_KERNEL_AUTO || k == REL_KERNEL_SCAN; };
+  if (!ok(fwd) || !ok(bwd)) return REL_E_KERNEL;
+  read_kernel_env();   // so that a later first use does not override this selection
+  g_fwd_kernel.store(fwd, std::memory_order_relaxed);
+  g_bwd_kernel.store(bwd, std::memory_order_relaxed);
+  return REL_OK;
+}

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.relation_cache_append.restype = i
         L.relation_status_str.argtypes = [i]
         L.relation_status_str.restype = ctypes.c_char_p
+        L.relation_select_kernels.argtypes = [i, i]
+        L.relation_select_kernels.restype = i
         _lib = L
     return _lib
 
@@ -73,7 +75,29 @@ EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_
            "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
            "relation_fwd_model", "relation_linear_workspace_bytes", "relation_linear_fwd",
            "relation_decode_workspace_bytes", "relation_decode",
-           "relation_cache_append", "relation_status_str")
+           "relation_cache_append", "relation_status_str", "relation_select_kernels")
+
+KERNELS = {"auto": 0, "scan": 1}
+
+
+def select_kernels(fwd: str = "auto", bwd: str = "auto"):
+    """Process-wide choice of the bf16 forward / backward kernels: "auto"
+    (the MFMA kernels wherever they apply) or "scan" (the row-scan kernels)."""
+    _check("relation_select_kernels", lib().relation_select_kernels(KERNELS[fwd], KERNELS[bwd]))
+
+
+class kernels:
+    """Context manager: select kernels for the block, then back to "auto"."""
+
+    def __init__(self, fwd: str = "auto", bwd: str = "auto"):
+        self.sel = (fwd or "auto", bwd or "auto")
+
+    def __enter__(self):
+        select_kernels(*self.sel)
+        return self
+
+    def __exit__(self, *exc):
+        select_kernels("auto", "auto")
 
 ROPE = {"none": 0, "interleaved": 1, "half": 2}
 PAIRS = {"A": 0, "B": 1}
@@ -105,18 +129,63 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _require_cuda(*ts):
-    for t in ts:
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous device tensors")
+class _Args:
+    """Checks of caller-supplied tensors before anything reaches the library
+    (which sees bare pointers and sizes and cannot check them). Every tensor
+    is first checked for its shape and dtype (all of them, so a mismatch is
+    reported whatever device the tensors are on), then for being a contiguous
+    tensor on the device of the first one."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.ts = []
+
+    def __call__(self, name, t, shape=None, dtype=None, optional=False):
+        if t is None:
+            if optional:
+                return self
+            raise ValueError(f"{self.fn}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.fn}: {name} must be a torch.Tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{self.fn}: {name} has dtype {t.dtype}, expected {dtype}")
+        self.ts.append((name, t))
+        return self
+
+    def bytes(self, name, t, need: int):
+        """A workspace: uint8, at least `need` bytes."""
+        self(name, t, dtype=torch.uint8)
+        if t.dim() != 1 or t.numel() < need:
+            raise ValueError(f"{self.fn}: {name} holds {t.numel()} bytes, {need} needed")
+        return self
+
+    def done(self):
+        dev = None
+        for name, t in self.ts:
+            if not t.is_cuda:
+                raise ValueError(f"{self.fn}: {name} must be a device tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{self.fn}: {name} must be contiguous")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.fn}: {name} is on {t.device}, the inputs on {dev}")
+
+
+def _shape4(fn, P1):
+    if not isinstance(P1, torch.Tensor) or P1.dim() != 4:
+        raise ValueError(f"{fn}: P1 must be a [B, H, T, d_h] tensor")
+    return tuple(P1.shape)
 
 
 def fwd(P1, P2, V, tau, lam: float = 0.0, out=None, stream=None):
     """Y = relation forward of [B, H, T, d_h] device tensors; tau: float or [H]."""
-    _require_cuda(P1, P2, V)
-    B, H, T, D = P1.shape
-    if P2.shape != P1.shape or V.shape != P1.shape or P2.dtype != P1.dtype or V.dtype != P1.dtype:
-        raise ValueError("P1, P2, V must share shape and dtype")
+    shp = _shape4("fwd", P1)
+    B, H, T, D = shp
+    a = _Args("fwd")("P1", P1)("P2", P2, shp, P1.dtype)("V", V, shp, P1.dtype)
+    a("out", out, shp, P1.dtype, optional=True).done()
     if out is None:
         out = torch.empty_like(V)
     tau_keep, tau_p = _tau_arg(tau, H)
@@ -129,15 +198,14 @@ def fwd(P1, P2, V, tau, lam: float = 0.0, out=None, stream=None):
 
 def fwd_lse(P1, P2, V, tau, lam: float = 0.0, out=None, lse=None, stream=None):
     """Training forward: (Y, LSE) with LSE the fp32 [B, H, T] row log normaliser."""
-    _require_cuda(P1, P2, V)
-    B, H, T, D = P1.shape
-    if P2.shape != P1.shape or V.shape != P1.shape or P2.dtype != P1.dtype or V.dtype != P1.dtype:
-        raise ValueError("P1, P2, V must share shape and dtype")
+    shp = _shape4("fwd_lse", P1)
+    B, H, T, D = shp
+    a = _Args("fwd_lse")("P1", P1)("P2", P2, shp, P1.dtype)("V", V, shp, P1.dtype)
+    a("out", out, shp, P1.dtype, optional=True)("lse", lse, (B, H, T), torch.float32, optional=True).done()
     if out is None:
         out = torch.empty_like(V)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=P1.device)
-    _require_cuda(out, lse)
     tau_keep, tau_p = _tau_arg(tau, H)
     st = lib().relation_fwd_lse(_ptr(P1), _ptr(P2), _ptr(V), tau_p, float(lam), _ptr(out), _ptr(lse),
                                 B, H, T, D, _dtype_code(P1), _stream(stream))
@@ -153,20 +221,25 @@ def bwd_workspace_bytes(B: int, H: int, T: int, d_h: int) -> int:
 def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None):
     """Gradients (dP1, dP2, dV, dtau [H] fp32, dlambda [1] fp32) of sum(Y * dY),
     from the forward's inputs and its outputs Y, LSE (fwd_lse)."""
-    _require_cuda(P1, P2, V, Y, lse, dY)
-    B, H, T, D = P1.shape
-    for t in (P2, V, Y, dY):
-        if t.shape != P1.shape or t.dtype != P1.dtype:
-            raise ValueError("P1, P2, V, Y, dY must share shape and dtype")
-    if lse.shape != (B, H, T) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B, H, T]")
+    shp = _shape4("bwd", P1)
+    B, H, T, D = shp
+    dt = P1.dtype
+    a = _Args("bwd")("P1", P1)("P2", P2, shp, dt)("V", V, shp, dt)("Y", Y, shp, dt)("dY", dY, shp, dt)
+    a("lse", lse, (B, H, T), torch.float32)
+    if grads is not None:
+        if len(grads) != 5:
+            raise ValueError("bwd: grads must be (dP1, dP2, dV, dtau, dlam)")
+        a("dP1", grads[0], shp, dt)("dP2", grads[1], shp, dt)("dV", grads[2], shp, dt)
+        a("dtau", grads[3], (H,), torch.float32)("dlam", grads[4], (1,), torch.float32)
+    need = bwd_workspace_bytes(B, H, T, D)
+    if workspace is not None:
+        a.bytes("workspace", workspace, need)
+    a.done()
     if grads is None:
         grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
                  torch.empty(H, dtype=torch.float32, device=P1.device),
                  torch.empty(1, dtype=torch.float32, device=P1.device))
     dP1, dP2, dV, dtau, dlam = grads
-    _require_cuda(dP1, dP2, dV, dtau, dlam)
-    need = bwd_workspace_bytes(B, H, T, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
     tau_keep, tau_p = _tau_arg(tau, H)
@@ -187,13 +260,24 @@ def _theta_arg(theta, H: int):
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
 
 
+def _check_prestep(fn, P1, P2, I, pos0, out):
+    shp = _shape4(fn, P1)
+    a = _Args(fn)("P1", P1)("P2", P2, shp, P1.dtype)("I", I, shp, P1.dtype)
+    a("pos0", pos0, (shp[0],), torch.int32, optional=True)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError(f"{fn}: out must be (P1o, P2o, Io)")
+        a("out[0]", out[0], shp, P1.dtype)("out[1]", out[1], shp, P1.dtype)("out[2]", out[2], shp, P1.dtype)
+    a.done()
+    return shp
+
+
 def prestep(P1, P2, I, pos0=None, rope="interleaved", rope_base: float = 1e4, theta=None, pairing="A",
             out=None, stream=None):
     """RoPE on P1/P2 and Givens mixing of I ([B,H,T,d_h] device tensors); pos0:
     device int32[B] or None; theta: H/2 angles or None. out=(P1o, P2o, Io) may
     be the inputs themselves (in place)."""
-    _require_cuda(P1, P2, I)
-    B, H, T, D = P1.shape
+    B, H, T, D = _check_prestep("prestep", P1, P2, I, pos0, out)
     if out is None:
         out = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(I))
     th_keep, th_p = _theta_arg(theta, H)
@@ -209,8 +293,9 @@ def prestep_launcher(P1, P2, I, pos0, rope, rope_base, theta, pairing, out, stre
     """relation_prestep with its arguments marshalled once: returns a callable
     that launches it again on the same tensors (for timing loops, where a
     short kernel would otherwise wait on the per-call marshalling)."""
-    _require_cuda(P1, P2, I)
-    B, H, T, D = P1.shape
+    if out is None:
+        raise ValueError("prestep_launcher: out is required")
+    B, H, T, D = _check_prestep("prestep_launcher", P1, P2, I, pos0, out)
     th_keep, th_p = _theta_arg(theta, H)
     args = (_ptr(P1), _ptr(P2), _ptr(I), _ptr(pos0), ROPE[rope], float(rope_base), th_p, PAIRS[pairing],
             _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), B, H, T, D, _dtype_code(P1), _stream(stream))
@@ -227,11 +312,17 @@ def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", r
               theta=None, pairing="A", out=None, lse=None, workspace=None, stream=None):
     """The operator on raw projections: pre-steps, then the forward. Returns
     (Y, LSE or None, workspace holding the pre-stepped tensors)."""
-    _require_cuda(P1, P2, I)
-    B, H, T, D = P1.shape
+    shp = _shape4("fwd_model", P1)
+    B, H, T, D = shp
+    a = _Args("fwd_model")("P1", P1)("P2", P2, shp, P1.dtype)("I", I, shp, P1.dtype)
+    a("pos0", pos0, (B,), torch.int32, optional=True)("out", out, shp, P1.dtype, optional=True)
+    a("lse", lse, (B, H, T), torch.float32, optional=True)
+    need = int(lib().relation_fwd_model_workspace_bytes(B, H, T, D, _dtype_code(P1)))
+    if workspace is not None:
+        a.bytes("workspace", workspace, need)
+    a.done()
     if out is None:
         out = torch.empty_like(I)
-    need = int(lib().relation_fwd_model_workspace_bytes(B, H, T, D, _dtype_code(P1)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
     tau_keep, tau_p = _tau_arg(tau, H)
@@ -247,13 +338,17 @@ def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", r
 def linear_fwd(P1, P2, I, alpha, tau, out=None, state=None, workspace=None, stream=None):
     """Linear Relation forward; alpha fp32 [B,H,T,d_h]; state: optional fp32
     [B,H,d_h,d_h] output for C_T. Returns (Y, state)."""
-    _require_cuda(P1, P2, I, alpha)
-    B, H, T, D = P1.shape
-    if alpha.dtype != torch.float32 or alpha.shape != P1.shape:
-        raise ValueError("alpha must be float32 with the shape of P1")
+    shp = _shape4("linear_fwd", P1)
+    B, H, T, D = shp
+    a = _Args("linear_fwd")("P1", P1)("P2", P2, shp, P1.dtype)("I", I, shp, P1.dtype)
+    a("alpha", alpha, shp, torch.float32)("out", out, shp, P1.dtype, optional=True)
+    a("state", state, (B, H, D, D), torch.float32, optional=True)
+    need = int(lib().relation_linear_workspace_bytes(B, H, T, D))
+    if workspace is not None:
+        a.bytes("workspace", workspace, need)
+    a.done()
     if out is None:
         out = torch.empty_like(I)
-    need = int(lib().relation_linear_workspace_bytes(B, H, T, D))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=P1.device)
     tau_keep, tau_p = _tau_arg(tau, H)
@@ -273,11 +368,17 @@ def decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam: float = 0.0, out=None,
            workspace=None, stream=None):
     """One Relation Cache decode step; p1/p2/v [B,H,d_h], caches [B,H,L_cap,d_h],
     lens int32[B] on the device."""
-    _require_cuda(p1, p2, v, cache_P2, cache_V, lens)
+    if not isinstance(cache_P2, torch.Tensor) or cache_P2.dim() != 4:
+        raise ValueError("decode: cache_P2 must be a [B, H, L_cap, d_h] tensor")
     B, H, L_cap, D = cache_P2.shape
-    if lens.dtype != torch.int32:
-        raise TypeError("lens must be int32")
+    dt = cache_P2.dtype
+    a = _Args("decode")("cache_P2", cache_P2)("cache_V", cache_V, cache_P2.shape, dt)
+    a("p1", p1, (B, H, D), dt)("p2", p2, (B, H, D), dt)("v", v, (B, H, D), dt)("lens", lens, (B,), torch.int32)
+    a("out", out, (B, H, D), dt, optional=True)
     need = decode_workspace_bytes(B, H, L_cap, D)
+    if workspace is not None:
+        a.bytes("workspace", workspace, need)
+    a.done()
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=p1.device)
     if out is None:
@@ -293,8 +394,12 @@ def decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam: float = 0.0, out=None,
 
 def cache_append(cache_P2, cache_V, lens, p2, v, stream=None):
     """Append the token's p2, v [B,H,d_h] at row lens[b] and increment lens."""
-    _require_cuda(cache_P2, cache_V, lens, p2, v)
+    if not isinstance(cache_P2, torch.Tensor) or cache_P2.dim() != 4:
+        raise ValueError("cache_append: cache_P2 must be a [B, H, L_cap, d_h] tensor")
     B, H, L_cap, D = cache_P2.shape
+    dt = cache_P2.dtype
+    a = _Args("cache_append")("cache_P2", cache_P2)("cache_V", cache_V, cache_P2.shape, dt)
+    a("lens", lens, (B,), torch.int32)("p2", p2, (B, H, D), dt)("v", v, (B, H, D), dt).done()
     st = lib().relation_cache_append(_ptr(cache_P2), _ptr(cache_V), _ptr(lens), _ptr(p2), _ptr(v),
                                      B, H, L_cap, D, _dtype_code(p2), _stream(stream))
     _check("relation_cache_append", st)

@@ -36,9 +36,8 @@
  *     dlambda) 4-byte aligned; an output range may not overlap any input
  *     range or another output range.
  *   - Supported: d_h in {32, 64, 128} for every entry point, and also 48 and
- *     80 (the paper's model geometries) for relation_fwd, relation_fwd_ex,
- *     relation_fwd_lse, relation_bwd, relation_prestep and relation_fwd_model;
- *     1 <= H <= REL_MAX_HEADS; B <= 65535.
+ *     80 (the paper's model geometries) for every entry point but
+ *     relation_linear_fwd; 1 <= H <= REL_MAX_HEADS; B <= 65535.
  */
 #ifndef RELATION_H
 #define RELATION_H
@@ -69,7 +68,8 @@ typedef enum {
   REL_E_ALIAS = 8,     /* an output range overlaps an input or output range  */
   REL_E_WORKSPACE = 9, /* workspace missing or smaller than required         */
   REL_E_LAUNCH = 10,   /* a kernel launch failed                             */
-  REL_E_PRESTEP = 11   /* invalid rotary mode / base, pairing or Givens angle */
+  REL_E_PRESTEP = 11,  /* invalid rotary mode / base, pairing or Givens angle */
+  REL_E_KERNEL = 12    /* unknown kernel selection                           */
 } rel_status;
 
 typedef enum { REL_F32 = 0, REL_BF16 = 1 } rel_dtype;
@@ -302,6 +302,24 @@ rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len,
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* relation_status_str(rel_status s);
+
+/* Kernel family of the bf16 forward and backward. */
+typedef enum {
+  REL_KERNEL_AUTO = 0,  /* the MFMA kernels wherever they apply (default)  */
+  REL_KERNEL_SCAN = 1   /* the row-scan kernels (to run and test them alone) */
+} rel_kernel;
+
+/*
+ * relation_select_kernels - which kernels the bf16 forward family
+ * (relation_fwd, relation_fwd_ex, relation_fwd_lse, relation_fwd_model) and
+ * relation_bwd run. The selection is process-wide; calls made after this
+ * one returns use it. Before any call to it, the selection comes from the
+ * environment variables RELATION_FWD_KERNEL and RELATION_BWD_KERNEL (the
+ * value "scan" selects REL_KERNEL_SCAN), read once, the first time a
+ * selection is needed. No HIP call; REL_E_KERNEL for a value outside
+ * rel_kernel (and then nothing changes).
+ */
+rel_status relation_select_kernels(rel_kernel fwd, rel_kernel bwd);
 
 #pragma GCC visibility pop
 

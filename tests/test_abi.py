@@ -12,7 +12,7 @@ from causal_self_exchange_amd import relation as R
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_TAU, E_LAMBDA, E_ALIGN, E_ALIAS, E_WS, E_LAUNCH, E_PRESTEP = range(12)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_TAU, E_LAMBDA, E_ALIGN, E_ALIAS, E_WS, E_LAUNCH, E_PRESTEP, E_KERNEL = range(13)
 
 # Fake, never-dereferenced device addresses (16-byte aligned, far apart).
 A, B_, C, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -52,8 +52,8 @@ def test_library_exports_nothing_else():
 
 def test_status_strings():
     lib = R.lib()
-    for code in range(12):
-        assert lib.relation_status_str(code)
+    for code in range(13):
+        assert lib.relation_status_str(code) not in (b"", b"unknown status")
     assert lib.relation_status_str(99) == b"unknown status"
 
 
@@ -90,7 +90,10 @@ def test_decode_workspace_bytes():
     assert lib.relation_decode_workspace_bytes(2, 3, 1, 32) == 2 * 3 * 1 * 34 * 4
     assert lib.relation_decode_workspace_bytes(2, 3, 257, 64) == 2 * 3 * 2 * 66 * 4
     assert lib.relation_decode_workspace_bytes(0, 3, 10, 64) == 0
-    assert lib.relation_decode_workspace_bytes(1, 1, 10, 48) == 0
+    assert lib.relation_decode_workspace_bytes(1, 1, 10, 96) == 0
+    # the paper's head sizes 48 and 80 (states of d_h + 2 floats per chunk)
+    assert lib.relation_decode_workspace_bytes(1, 2, 300, 48) == 1 * 2 * 2 * 50 * 4
+    assert lib.relation_decode_workspace_bytes(1, 1, 256, 80) == 82 * 4
 
 
 LEN, WS, YD, CP, CV = 0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000
@@ -106,7 +109,7 @@ def dec(p1=A, p2=B_, v=C, cP2=CP, cV=CV, ln=LEN, tau=(1.0, 1.0), lam=0.0, y=YD,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(p1=None), E_NULL), (dict(cV=None), E_NULL), (dict(ln=None), E_NULL), (dict(y=None), E_NULL),
-    (dict(L=0), E_SHAPE), (dict(B=-1), E_SHAPE), (dict(dt=3), E_DTYPE), (dict(D=80), E_HEADDIM),
+    (dict(L=0), E_SHAPE), (dict(B=-1), E_SHAPE), (dict(dt=3), E_DTYPE), (dict(D=96), E_HEADDIM),
     (dict(tau=(0.0, 1.0)), E_TAU), (dict(lam=float("-inf")), E_LAMBDA),
     (dict(ws=None), E_WS), (dict(wsb=16), E_WS),
     (dict(cP2=CP + 4), E_ALIGN), (dict(ln=LEN + 2), E_ALIGN), (dict(ws=WS + 8), E_ALIGN),
@@ -127,6 +130,15 @@ def test_cache_append_rejects_invalid_arguments():
     assert f(CP, CV, LEN + 1, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIGN
     assert f(CP, CP + 256, LEN, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIAS
     assert f(CP, CV, CV + 64, A, C, 2, 2, 300, 128, R.REL_BF16, None) == E_ALIAS
+
+
+def test_select_kernels():
+    f = R.lib().relation_select_kernels
+    assert f(0, 0) == OK and f(1, 0) == OK and f(0, 1) == OK and f(1, 1) == OK
+    assert f(2, 0) == E_KERNEL and f(0, -1) == E_KERNEL
+    assert f(0, 0) == OK
+    with pytest.raises(KeyError):
+        R.select_kernels("fast")
 
 
 def test_binding_refuses_host_tensors():
@@ -223,6 +235,31 @@ def test_fwd_model_workspace_bytes():
     # the paper's head sizes 48 and 80 are accepted by the forward family
     assert lib.relation_fwd_model_workspace_bytes(1, 1, 3, 48, R.REL_F32) == 3 * 768
     assert lib.relation_fwd_model_workspace_bytes(2, 8, 1024, 80, R.REL_BF16) == 3 * 2 * 8 * 1024 * 80 * 2
+
+
+def fwd_model(P1=A, P2=B_, I=C, pos0=None, rope=1, base=1e4, theta=(0.3,), pairing=0, tau=(1.0, 1.0), lam=0.0,
+              Yp=Y, L=None, B=1, H=2, T=16, D=64, dt=R.REL_BF16, ws=WS, ws_bytes=None):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    keep2, thp = _tau(theta) if theta is not None else (None, None)
+    if ws_bytes is None:
+        ws_bytes = R.lib().relation_fwd_model_workspace_bytes(B, H, T, D, dt) if T > 0 else 0
+    return R.lib().relation_fwd_model(P1, P2, I, pos0, rope, base, thp, pairing, tp, lam, Yp, L, B, H, T, D, dt,
+                                      ws, ws_bytes, None)
+
+
+# Every check of relation_fwd_model, including those of the forward it runs
+# after the pre-steps (Y and LSE against the inputs, the workspace, each
+# other and pos0), happens before the pre-step kernel is enqueued.
+@pytest.mark.parametrize("kw,code", [
+    (dict(P1=None), E_NULL), (dict(Yp=None), E_NULL), (dict(tau=None), E_NULL), (dict(T=0), E_SHAPE),
+    (dict(D=96), E_HEADDIM), (dict(dt=5), E_DTYPE), (dict(ws=None), E_WS), (dict(ws_bytes=1024), E_WS),
+    (dict(rope=3), E_PRESTEP), (dict(theta=(float("inf"),)), E_PRESTEP), (dict(tau=(1.0, 0.0)), E_TAU),
+    (dict(lam=float("nan")), E_LAMBDA), (dict(Yp=Y + 2), E_ALIGN), (dict(L=LSE_ + 2), E_ALIGN),
+    (dict(Yp=A), E_ALIAS), (dict(Yp=WS + 64), E_ALIAS), (dict(L=A + 64), E_ALIAS), (dict(L=WS + 16), E_ALIAS),
+    (dict(L=Y + 4), E_ALIAS), (dict(L=Y - 4), E_ALIAS), (dict(L=LSE_, pos0=LSE_ + 8), E_ALIAS),
+])
+def test_fwd_model_rejects_invalid_arguments(kw, code):
+    assert fwd_model(**kw) == code
 
 
 def linear(P1=A, P2=B_, I=C, alpha=DY_, tau=(1.0, 1.0), Yp=Y, state=None, B=1, H=2, T=100, D=64,

@@ -15,8 +15,6 @@ Tolerances (the pages fix none for gradients; these follow the forward's bar):
     size of the quantities each share is computed from.
   LSE: absolute 1e-4 (fp32 exponent sums over up to T terms; |LSE| ~ log T).
 """
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -33,33 +31,13 @@ TOL = {"bf16": 2e-2, "f32": 1e-5}
 LSE_ATOL = 1e-4
 
 
-class _Env:
-    def __init__(self, **kv):
-        self.kv = kv
-
-    def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kv}
-        for k, v in self.kv.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-    def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
 def _dev(inp, keys=("P1", "P2", "V", "dY")):
     return [inp[k].to(DEV).contiguous() for k in keys]
 
 
 def _gpu_train(inp, lam, bwd_kernel=None):
     P1, P2, V, dY = _dev(inp)
-    with _Env(RELATION_BWD_KERNEL=bwd_kernel):
+    with R.kernels(bwd=bwd_kernel or "auto"):
         Y, L = R.fwd_lse(P1, P2, V, inp["tau"], lam)
         g = R.bwd(P1, P2, V, inp["tau"], lam, Y, L, dY)
     torch.cuda.synchronize()

@@ -5,6 +5,7 @@ Sizes: Tiny and Small are compared in full; Mid and Long (full size, the
 launch configuration the benchmark times) are compared on sampled rows of
 every head, each row computed by the oracle straight from the definition.
 """
+
 import os
 
 import numpy as np
@@ -59,20 +60,7 @@ def _oracle_sampled_compare(inp, Y, lam, seed, dtype, n=40):
 
 
 def _kernel_env(name):
-    class _Ctx:
-        def __enter__(self):
-            self.old = os.environ.get("RELATION_FWD_KERNEL")
-            if name is None:
-                os.environ.pop("RELATION_FWD_KERNEL", None)
-            else:
-                os.environ["RELATION_FWD_KERNEL"] = name
-
-        def __exit__(self, *a):
-            if self.old is None:
-                os.environ.pop("RELATION_FWD_KERNEL", None)
-            else:
-                os.environ["RELATION_FWD_KERNEL"] = self.old
-    return _Ctx()
+    return R.kernels(fwd=name or "auto")
 
 
 # ------------------------------------------------------------ configs -----
@@ -100,6 +88,64 @@ def test_long_config_sampled_parity(seed):
     inp = W.make_fwd_inputs(cfg, seed)
     Y = _gpu_fwd(inp)
     _oracle_sampled_compare(inp, Y, 0.0, seed, torch.bfloat16, n=24)
+
+
+def _oracle_heads(inp, heads, lam=0.0):
+    """The fp64 oracle on the listed (b, h) heads, one head per thread (numpy
+    releases the interpreter lock in its BLAS and elementwise loops; BLAS is
+    held to one thread per head)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    P1, P2, V = f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"])
+    tau = inp["tau"].astype(np.float64)
+
+    def one(bh):
+        b, h = bh
+        return O.relation_head(P1[b, h], P2[b, h], V[b, h], float(tau[h]), lam)
+
+    n = max(1, min(len(os.sched_getaffinity(0)), len(heads), 16))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(n) as ex:
+        return list(ex.map(one, heads))
+
+
+def test_mid_config_full_parity():
+    """Every element of every head of the mid workload (one seed)."""
+    cfg = W.CONFIGS["mid"]
+    inp = W.make_fwd_inputs(cfg, W.SEEDS[0])
+    Y = f64(_gpu_fwd(inp))
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    for (b, h), ref in zip(heads, _oracle_heads(inp, heads)):
+        assert_parity(Y[b, h], ref, torch.bfloat16, f"mid b={b} h={h}")
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_long_config_full_parity(group):
+    """Every element of every head of the long workload (one seed), in four
+    groups of eight heads (the launch is the whole workload each time)."""
+    cfg = W.CONFIGS["long"]
+    inp = W.make_fwd_inputs(cfg, W.SEEDS[0])
+    Y = f64(_gpu_fwd(inp))
+    heads = [(0, h) for h in range(8 * group, 8 * group + 8)]
+    for (b, h), ref in zip(heads, _oracle_heads(inp, heads)):
+        assert_parity(Y[b, h], ref, torch.bfloat16, f"long h={h}")
+
+
+def test_relation_fwd_entry_point_small():
+    """relation_fwd itself (not only relation_fwd_ex) on the small workload."""
+    import ctypes
+    cfg = W.CONFIGS["small"]
+    inp = W.make_fwd_inputs(cfg, W.SEEDS[0])
+    P1, P2, V = _dev(inp)
+    Y = torch.empty_like(V)
+    tau = np.ascontiguousarray(np.broadcast_to(np.asarray(inp["tau"], np.float32), (cfg.H,)))
+    st = R.lib().relation_fwd(P1.data_ptr(), P2.data_ptr(), V.data_ptr(),
+                              tau.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), Y.data_ptr(),
+                              cfg.B, cfg.H, cfg.T, cfg.d_h, R.REL_BF16, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert_parity(f64(Y), _oracle_full(inp, 0.0), torch.bfloat16, "relation_fwd small")
+    assert torch.equal(Y, _gpu_fwd(inp, 0.0))          # relation_fwd_ex with lambda = 0
 
 
 def test_scan_kernel_bf16_mid_sampled():
@@ -253,7 +299,7 @@ def test_decode_full_config_parity():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 48, 64, 80, 128])
 def test_decode_ragged_lengths(D, dt):
     cfg = W.DecodeConfig("d", 7, 3, D, 0, 600, 600, dtype=dt, tau=0.8)
     inp = W.make_decode_inputs(cfg, 3 + D)
@@ -272,7 +318,7 @@ def test_decode_ragged_lengths(D, dt):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 80, 128])
 def test_decode_large_evidence(D, dt):
     """U ~ 30 between the new query and every cached key (correlated rows):
     the split-length partials carry large, different maxima and the merge
@@ -311,12 +357,13 @@ def test_decode_clamps_out_of_range_lengths():
     assert_parity(f64(y), ref, torch.bfloat16, "clamped")
 
 
+@pytest.mark.parametrize("D", [48, 64, 80])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_autoregressive_decode_matches_forward(dt):
+def test_autoregressive_decode_matches_forward(dt, D):
     """Empty cache; for t = 0..T-1 decode token t then append it. Every decode
     output must equal row t of the forward on the whole sequence (exact cache,
     App. A.5), both checked against the oracle."""
-    B, H, T, D = 2, 2, 70, 64
+    B, H, T = 2, 2, 70
     cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0))
     inp = W.make_fwd_inputs(cfg, 5)
     P1, P2, V = _dev(inp)
