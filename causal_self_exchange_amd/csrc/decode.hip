@@ -18,6 +18,8 @@
 //     entry of the new token and the count term for position L + 1, and
 //     writes y.
 // relation_cache_append implements the cache update of App. A.5.3.
+#include <atomic>
+
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -253,6 +255,29 @@ hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, h
     case 128: return bf16 ? launch_decode_typed<__bf16, 128>(a, hp, s) : launch_decode_typed<float, 128>(a, hp, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Partial states of relation_decode_noalloc: a file-scope device array (each
+// GPU the library runs on holds its own copy until the process ends). In host
+// code its name is a stand-in, not a device address: the address comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);   // concurrent first calls store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "relation.h"
 #include <stdint.h>
 
 namespace rel {
@@ -110,6 +112,9 @@ inline int64_t lin_decay_floats(int64_t BH, int64_t T, int64_t D) { return BH * 
 // Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
 // states per (b, h), one per partial work-group.
 constexpr int kDecodeChunk = 256;
+// Size of the device array that holds relation_decode_noalloc's partial
+// states (B * H * ceil(L_cap / 256) * (d_h + 2) floats must fit).
+constexpr size_t kDecodeScratchBytes = REL_DECODE_SCRATCH_BYTES;
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
@@ -128,6 +133,8 @@ bool bwd_mfma_supported(int d_h, int T);
 hipError_t launch_prestep(const PrestepArgs& a, const PrestepParams& pp, bool bf16, hipStream_t s);
 hipError_t launch_linear(const LinArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
+// Device address of the decode scratch array on the current device.
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_cache_append(void* cP2, void* cV, int32_t* len, const void* p2, const void* v,
                                int B, int H, int L_cap, int d_h, bool bf16, hipStream_t s);
 

@@ -378,10 +378,14 @@ size_t relation_decode_workspace_bytes(int B, int H, int L_cap, int d_h) {
   return static_cast<size_t>(B) * H * chunks * (d_h + 2) * sizeof(float);
 }
 
-rel_status relation_decode(const void* p1, const void* p2, const void* v, const void* cache_P2,
-                           const void* cache_V, const int32_t* len, const float* tau_s, float lambda,
-                           void* y, int B, int H, int L_cap, int d_h, rel_dtype dt, void* workspace,
-                           size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// relation_decode with its workspace either passed in (scratch == false) or
+// the library's scratch array (scratch == true; then `workspace` is unused).
+rel_status decode_impl(const void* p1, const void* p2, const void* v, const void* cache_P2,
+                       const void* cache_V, const int32_t* len, const float* tau_s, float lambda, void* y,
+                       int B, int H, int L_cap, int d_h, rel_dtype dt, void* workspace, size_t ws_bytes,
+                       bool scratch, hipStream_t stream) {
   if (!p1 || !p2 || !v || !cache_P2 || !cache_V || !len || !tau_s || !y) return REL_E_NULL;
   int64_t ncache = 0, ntok = 0;
   if (!count(ncache, {B, H, L_cap, d_h}) || !count(ntok, {B, H, d_h}) || H > REL_MAX_HEADS ||
@@ -393,9 +397,15 @@ rel_status relation_decode(const void* p1, const void* p2, const void* v, const 
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
   const size_t need = relation_decode_workspace_bytes(B, H, L_cap, d_h);
-  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  if (scratch) {
+    // Every check above and below runs before the one HIP call that finds the
+    // scratch array's address.
+    if (need > rel::kDecodeScratchBytes) return REL_E_WORKSPACE;
+  } else if (!workspace || ws_bytes < need) {
+    return REL_E_WORKSPACE;
+  }
   if (!aligned16(p1) || !aligned16(p2) || !aligned16(v) || !aligned16(cache_P2) ||
-      !aligned16(cache_V) || !aligned16(y) || !aligned16(workspace) ||
+      !aligned16(cache_V) || !aligned16(y) || (!scratch && !aligned16(workspace)) ||
       (reinterpret_cast<uintptr_t>(len) & 3u))
     return REL_E_ALIGN;
   const size_t es = elem_size(dt);
@@ -403,17 +413,40 @@ rel_status relation_decode(const void* p1, const void* p2, const void* v, const 
   const size_t lb = static_cast<size_t>(B) * sizeof(int32_t);
   if (overlaps(y, tb, p1, tb) || overlaps(y, tb, p2, tb) || overlaps(y, tb, v, tb) ||
       overlaps(y, tb, cache_P2, cb) || overlaps(y, tb, cache_V, cb) || overlaps(y, tb, len, lb) ||
-      overlaps(y, tb, workspace, need))
+      (!scratch && overlaps(y, tb, workspace, need)))
     return REL_E_ALIAS;
-  if (overlaps(workspace, need, p1, tb) || overlaps(workspace, need, p2, tb) ||
-      overlaps(workspace, need, v, tb) || overlaps(workspace, need, cache_P2, cb) ||
-      overlaps(workspace, need, cache_V, cb) || overlaps(workspace, need, len, lb))
+  if (!scratch && (overlaps(workspace, need, p1, tb) || overlaps(workspace, need, p2, tb) ||
+                   overlaps(workspace, need, v, tb) || overlaps(workspace, need, cache_P2, cb) ||
+                   overlaps(workspace, need, cache_V, cb) || overlaps(workspace, need, len, lb)))
     return REL_E_ALIAS;
+  if (scratch) {
+    void* p = nullptr;
+    if (rel::decode_scratch(&p) != hipSuccess) return REL_E_LAUNCH;
+    workspace = p;
+  }
 
   rel::DecodeArgs a{p1, p2, v, cache_P2, cache_V, len, y, static_cast<float*>(workspace),
                     B, H, L_cap, d_h, static_cast<int>((L_cap + rel::kDecodeChunk - 1) / rel::kDecodeChunk)};
   const hipError_t e = rel::launch_decode(a, hp, dt == REL_BF16, stream);
   return e == hipSuccess ? REL_OK : REL_E_LAUNCH;
+}
+
+}  // namespace
+
+rel_status relation_decode(const void* p1, const void* p2, const void* v, const void* cache_P2,
+                           const void* cache_V, const int32_t* len, const float* tau_s, float lambda,
+                           void* y, int B, int H, int L_cap, int d_h, rel_dtype dt, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(p1, p2, v, cache_P2, cache_V, len, tau_s, lambda, y, B, H, L_cap, d_h, dt, workspace,
+                     ws_bytes, false, stream);
+}
+
+rel_status relation_decode_noalloc(const void* p1, const void* p2, const void* v, const void* cache_P2,
+                                   const void* cache_V, const int32_t* len, const float* tau_s, float lambda,
+                                   void* y, int B, int H, int L_cap, int d_h, rel_dtype dt,
+                                   hipStream_t stream) {
+  return decode_impl(p1, p2, v, cache_P2, cache_V, len, tau_s, lambda, y, B, H, L_cap, d_h, dt, nullptr, 0,
+                     true, stream);
 }
 
 rel_status relation_cache_append(void* cache_P2, void* cache_V, int32_t* len, const void* p2,

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.relation_decode_workspace_bytes.restype = sz
         L.relation_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp, sz, vp]
         L.relation_decode.restype = i
+        L.relation_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, fp, f, vp, i, i, i, i, i, vp]
+        L.relation_decode_noalloc.restype = i
         L.relation_cache_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.relation_cache_append.restype = i
         L.relation_status_str.argtypes = [i]
@@ -74,7 +76,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_workspace_bytes",
            "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
            "relation_fwd_model", "relation_linear_workspace_bytes", "relation_linear_fwd",
-           "relation_decode_workspace_bytes", "relation_decode",
+           "relation_decode_workspace_bytes", "relation_decode", "relation_decode_noalloc",
            "relation_cache_append", "relation_status_str", "relation_select_kernels")
 
 KERNELS = {"auto": 0, "scan": 1}
@@ -389,6 +391,28 @@ def decode(p1, p2, v, cache_P2, cache_V, lens, tau, lam: float = 0.0, out=None,
                                _dtype_code(p1), _ptr(workspace), workspace.numel(), _stream(stream))
     del tau_keep
     _check("relation_decode", st)
+    return out
+
+
+def decode_noalloc(p1, p2, v, cache_P2, cache_V, lens, tau, lam: float = 0.0, out=None, stream=None):
+    """relation_decode_noalloc: decode with the library's scratch array for the
+    partial states (no workspace; `out` must be given for a call that may not
+    allocate)."""
+    if not isinstance(cache_P2, torch.Tensor) or cache_P2.dim() != 4:
+        raise ValueError("decode_noalloc: cache_P2 must be a [B, H, L_cap, d_h] tensor")
+    B, H, L_cap, D = cache_P2.shape
+    dt = cache_P2.dtype
+    a = _Args("decode_noalloc")("cache_P2", cache_P2)("cache_V", cache_V, cache_P2.shape, dt)
+    a("p1", p1, (B, H, D), dt)("p2", p2, (B, H, D), dt)("v", v, (B, H, D), dt)("lens", lens, (B,), torch.int32)
+    a("out", out, (B, H, D), dt, optional=True).done()
+    if out is None:
+        out = torch.empty_like(v)
+    tau_keep, tau_p = _tau_arg(tau, H)
+    st = lib().relation_decode_noalloc(_ptr(p1), _ptr(p2), _ptr(v), _ptr(cache_P2), _ptr(cache_V), _ptr(lens),
+                                       tau_p, float(lam), _ptr(out), B, H, L_cap, D, _dtype_code(p1),
+                                       _stream(stream))
+    del tau_keep
+    _check("relation_decode_noalloc", st)
     return out
 
 

@@ -19,6 +19,7 @@ bool bwd_mfma_supported(int, int) { return false; }
 hipError_t launch_prestep(const PrestepArgs&, const PrestepParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_linear(const LinArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_decode(const DecodeArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t decode_scratch(void**) { return hipErrorLaunchFailure; }
 hipError_t launch_cache_append(void*, void*, int32_t*, const void*, const void*, int, int, int, int, bool,
                                hipStream_t) {
   return hipErrorLaunchFailure;

@@ -290,6 +290,28 @@ rel_status relation_decode(const void* p1, const void* p2, const void* v,
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * relation_decode_noalloc - relation_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same arguments without a workspace, the same
+ * kernels and the same result. The partial states live in a device array of
+ * the library, REL_DECODE_SCRATCH_BYTES (32 MiB) per GPU, held by each GPU the
+ * library runs on until the process ends; the call allocates and frees
+ * nothing. REL_E_WORKSPACE when relation_decode_workspace_bytes(B, H, L_cap,
+ * d_h) exceeds that size (then nothing is launched), REL_E_LAUNCH if the
+ * array's address cannot be found. Every call on one GPU uses the same array
+ * (each call writes every state it reads, so nothing carries over): calls
+ * that may run at the same time on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.
+ */
+#define REL_DECODE_SCRATCH_BYTES (32u << 20)
+rel_status relation_decode_noalloc(const void* p1, const void* p2, const void* v,
+                                   const void* cache_P2, const void* cache_V,
+                                   const int32_t* len, const float* tau_s,
+                                   float lambda, void* y, int B, int H,
+                                   int L_cap, int d_h, rel_dtype dt,
+                                   hipStream_t stream);
+
+/*
  * relation_cache_append - the cache update of App. A.5.3: write the token's
  * p2 and v ([B, H, d_h]) as row len[b] of cache_P2 / cache_V and increment
  * len[b]. A sequence whose len[b] is already >= L_cap (or < 0) is left

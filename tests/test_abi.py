@@ -120,6 +120,32 @@ def test_decode_rejects_invalid_arguments(kw, code):
     assert dec(**kw) == code
 
 
+def dec_noalloc(p1=A, p2=B_, v=C, cP2=CP, cV=CV, ln=LEN, tau=(1.0, 1.0), lam=0.0, y=YD,
+                B=2, H=2, L=300, D=128, dt=R.REL_BF16):
+    keep, tp = _tau(tau) if tau is not None else (None, None)
+    return R.lib().relation_decode_noalloc(p1, p2, v, cP2, cV, ln, tp, lam, y, B, H, L, D, dt, None)
+
+
+# Every rejection of relation_decode_noalloc, the size limit of its scratch
+# array included, comes before its one HIP call (the array's address).
+@pytest.mark.parametrize("kw,code", [
+    (dict(p1=None), E_NULL), (dict(ln=None), E_NULL), (dict(y=None), E_NULL), (dict(L=0), E_SHAPE),
+    (dict(dt=3), E_DTYPE), (dict(D=96), E_HEADDIM), (dict(tau=(0.0, 1.0)), E_TAU),
+    (dict(lam=float("nan")), E_LAMBDA), (dict(cP2=CP + 4), E_ALIGN), (dict(ln=LEN + 2), E_ALIGN),
+    (dict(y=A), E_ALIAS), (dict(y=CP + 1024), E_ALIAS), (dict(y=LEN), E_ALIAS),
+    # 64 x 64 heads, 8192 cached rows, d_h 128: 64 MiB of partial states > 32 MiB
+    (dict(B=64, H=64, L=8192, tau=[1.0] * 64), E_WS),
+])
+def test_decode_noalloc_rejects_invalid_arguments(kw, code):
+    assert dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_scratch_limit():
+    lib = R.lib()
+    assert lib.relation_decode_workspace_bytes(64, 32, 4096, 128) <= 32 << 20      # the decode workload fits
+    assert lib.relation_decode_workspace_bytes(64, 64, 8192, 128) > 32 << 20
+
+
 def test_cache_append_rejects_invalid_arguments():
     lib = R.lib()
     f = lib.relation_cache_append

@@ -109,6 +109,12 @@ CASES = {
     "decode out shape": (decode(out=z(B, H, D - 8)), ValueError, "out has shape"),
     "decode workspace": (decode(workspace=ws(4)), ValueError, "bytes"),
     "decode host": (decode(), ValueError, "device tensor"),
+    "decode_noalloc v dtype": (lambda: R.decode_noalloc(z(B, H, D), z(B, H, D), z(B, H, D, dtype=f32),
+                                                        z(B, H, L, D), z(B, H, L, D), z(B, dtype=torch.int32), 1.0),
+                               TypeError, "v has dtype"),
+    "decode_noalloc host": (lambda: R.decode_noalloc(z(B, H, D), z(B, H, D), z(B, H, D), z(B, H, L, D),
+                                                     z(B, H, L, D), z(B, dtype=torch.int32), 1.0),
+                            ValueError, "device tensor"),
     "append p2 dtype": (append(p2=z(B, H, D, dtype=f32)), TypeError, "p2 has dtype"),
     "append lens size": (append(lens=z(B + 1, dtype=torch.int32)), ValueError, "lens has shape"),
     "append v shape": (append(v=z(B, H, D, 2)), ValueError, "v has shape"),
