@@ -458,12 +458,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   };
 
   for (int pass = 0;; ++pass) {
-    // Prologue: P2 tiles 0..3 and V tiles 0..2 into their slots.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dma_k(t, t);
-#pragma unroll
-    for (int t = 0; t < 3; ++t) dma_v(t);
-    wait_vm_lgkm<0, 15>();
+    // Prologue: P2 tiles 0..3 and V tiles 0..2 into their slots, in the order
+    // they are read: P2 0, 1 and V 0 (the pre-step), P2 2 and V 1 (the end of
+    // iteration 0), P2 3 and V 2 (the end of iteration 1). Only the first
+    // group is waited for here; the pre-step's arrival certifies the second
+    // and iteration 0's the third (vector memory operations complete in
+    // order, and each arrival waits for all but its last kDmaIter).
+    dma_k(0, 0);
+    dma_k(1, 1);
+    dma_v(0);
+    dma_k(2, 2);
+    dma_v(1);
+    dma_k(3, 3);
+    dma_v(2);
+    wait_vm_lgkm<4 * C::kDmaPerWave, 15>();
     __syncthreads();
     if (!kLse && pass == 0) prescale_q();   // the redo scales its own reload
 #pragma unroll
