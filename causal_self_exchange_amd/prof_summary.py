@@ -6,6 +6,8 @@ trace_avg(csv, kernel_substr, last_n, within_first): mean duration (us) of the
 last `last_n` dispatches of one kernel from a `--kernel-trace` kernel_trace
 file (the timed launches of a run that first warms up), optionally within its
 first `within_first` dispatches.
+trace_series(csv, kernel_substr, first_n): durations (us) of the first
+`first_n` dispatches of one kernel, in dispatch order (a launch curve).
 counter_avg(csv, kernel_substr, counter): a counter's mean over dispatches of
 one kernel from a `--pmc` counter_collection file.
 traffic(...): HBM bytes per launch of a kernel from FETCH_SIZE / WRITE_SIZE
@@ -47,6 +49,16 @@ def trace_avg(path: str, kernel_substr: str, last_n: int, within_first: int | No
         raise ValueError(f"no dispatches of {kernel_substr} in {path}")
     return {"dispatches": len(rows), "last_n": len(durs), "avg_us": sum(durs) / len(durs),
             "min_us": min(durs), "max_us": max(durs)}
+
+
+def trace_series(path: str, kernel_substr: str, first_n: int) -> list[float]:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"]:
+                rows.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    return [round(d, 1) for _, d in rows[:first_n]]
 
 
 def counter_avg(path: str, kernel_substr: str, counter: str) -> float:
