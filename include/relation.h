@@ -26,8 +26,11 @@
  *   - lambda is the count-calibration coefficient; 0 gives the operator without
  *     count calibration.
  *   - The caller owns every buffer. The library allocates nothing and keeps
- *     no pointer after returning; its only global state is a per-device cache
- *     of the compute-unit count (written once, the same value by any caller).
+ *     no pointer after returning. Its global state: a per-device cache of the
+ *     compute-unit count (written once, the same value by any caller); the
+ *     kernel selection (relation_select_kernels, process-wide); and, for
+ *     relation_decode_noalloc only, a fixed device array per GPU (loaded with
+ *     the library's code object) and the cache of its per-device address.
  *   - All argument checks run on the host before any HIP call; on an error
  *     nothing is launched and no memory is touched.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
