@@ -15,7 +15,8 @@ import torch
 from causal_self_exchange_amd import relation as R
 from causal_self_exchange_amd import workloads as W
 from oracle import relation_oracle as O
-from tests._helpers import assert_parity, f64, row_normwise_err
+from tests import fp32_bars as FB
+from tests._helpers import assert_parity, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -196,12 +197,13 @@ def test_large_evidence_regime(D, kernel):
         ref = _oracle_full(inp, 0.5)
         if dt == torch.float32:
             # fp32 rounding of U_ij grows linearly with |U| and enters Y through
-            # the weights; the 1e-5 bar holds for |U| <~ 4, so scale it by
-            # max|U| / 4 here (max|U| ~ 45).
-            U = np.einsum("bhid,bhjd->bhij", f64(inp["P1"]), f64(inp["P2"])) / np.sqrt(D)
-            tol = 1e-5 * max(1.0, float(np.abs(U).max()) / 4.0)
-            err = row_normwise_err(f64(Y), ref)
-            assert err <= tol, f"D={D}: fp32 row-normwise error {err:.3e} > {tol:.3e}"
+            # the weights, so the fixed 1e-5 bar does not apply at |U| ~ 45:
+            # the first-order rounding-error bound of tests/fp32_bars.py does.
+            bar = FB.fwd_bar(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]),
+                             inp["tau"].astype(np.float64), 0.5)
+            ratio = FB.excess(f64(Y), ref, bar)
+            print(f"\nD={D} fp32 large evidence: error/bar {ratio:.2e}", flush=True)
+            assert ratio <= 1.0, f"D={D}: fp32 error exceeds its derived bar ({ratio:.2f}x)"
         else:
             assert_parity(f64(Y), ref, dt, f"D={D} {dt}")
 
@@ -323,7 +325,7 @@ def test_decode_large_evidence(D, dt):
     """U ~ 30 between the new query and every cached key (correlated rows):
     the split-length partials carry large, different maxima and the merge
     must rescale them exactly; lengths span one to several partial blocks.
-    The fp32 bar is scaled by max|U| / 4, as for the forward."""
+    fp32 is held to the derived rounding-error bound, as for the forward."""
     B, H, Lc = 4, 2, 2100
     cfg = W.DecodeConfig("d", B, H, D, 0, Lc, Lc, dtype=dt, tau=0.7)
     inp = W.make_decode_inputs(cfg, 70 + D)
@@ -337,10 +339,12 @@ def test_decode_large_evidence(D, dt):
     y = _gpu_decode(inp, 0.5)
     ref = _oracle_decode(inp, 0.5)
     if dt == "f32":
-        U = np.einsum("bhd,bhld->bhl", f64(inp["p1"]), f64(inp["cache_P2"])) / np.sqrt(D)
-        tol = 1e-5 * max(1.0, float(np.abs(U).max()) / 4.0)
-        err = row_normwise_err(f64(y), ref)
-        assert err <= tol, f"D={D}: fp32 row-normwise error {err:.3e} > {tol:.3e}"
+        tau = np.broadcast_to(np.asarray(inp["tau"], np.float64), (H,))
+        bar = FB.decode_bar(f64(inp["p1"]), f64(inp["p2"]), f64(inp["v"]), f64(inp["cache_P2"]),
+                            f64(inp["cache_V"]), inp["lens"], tau, 0.5)
+        ratio = FB.excess(f64(y), ref, bar)
+        print(f"\nD={D} fp32 decode large evidence: error/bar {ratio:.2e}", flush=True)
+        assert ratio <= 1.0, f"D={D}: fp32 error exceeds its derived bar ({ratio:.2f}x)"
     else:
         assert_parity(f64(y), ref, tdt, f"D={D} {dt}")
 
