@@ -146,7 +146,10 @@ def bench_backward(torch, R, W, steps, warmup):
     """relation_bwd on the T = 8192 workload with a seeded N(0, 1) upstream
     gradient; LSE and Y from relation_fwd_lse (outside the timed region).
     Throughput counts the 5 causal products of the gradient (recomputed U,
-    dY V^T, F^T dY, dU P2, dU^T P1): 5 B H T^2 d_h FLOPs, 2.5x the forward's."""
+    dY V^T, F^T dY, dU P2, dU^T P1): 5 B H T^2 d_h FLOPs, 2.5x the forward's.
+    The call gets the workspace with which dU is stored once; the path that
+    recomputes the evidence for dP1 instead (small workspace) is timed
+    beside it."""
     cfg = W.CONFIGS["long"]
     inp = W.make_bwd_inputs(cfg, 42)
     P1, P2, V, dY = (inp[k].cuda() for k in ("P1", "P2", "V", "dY"))
@@ -155,18 +158,25 @@ def bench_backward(torch, R, W, steps, warmup):
     grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
              torch.empty(cfg.H, dtype=torch.float32, device="cuda"),
              torch.empty(1, dtype=torch.float32, device="cuda"))
-    ws = torch.empty(R.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h), dtype=torch.uint8, device="cuda")
+    small = R.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h)
+    stored = R.bwd_stored_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.d_h)
+    ws = torch.empty(max(small, stored), dtype=torch.uint8, device="cuda")
 
-    def fn():
-        R.bwd(P1, P2, V, tau, 0.0, Y, L, dY, grads=grads, workspace=ws)
+    def timed(nbytes):
+        def fn():
+            R.bwd(P1, P2, V, tau, 0.0, Y, L, dY, grads=grads, workspace=ws[:nbytes])
+        _, total, _ = time_launches(fn, steps, warmup, torch)
+        return total / steps
 
-    per, total, _ = time_launches(fn, steps, warmup, torch)
-    ms = total / steps
+    ms = timed(max(small, stored))
+    ms_recompute = timed(small)
     flops = 5.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.d_h
-    return {"workload": "backward: B=1 H=32 T=8192 d_h=128 bf16, dY ~ N(0,1), seed 42 (dq with the row statistics, dkv, reduce)",
+    return {"workload": "backward: B=1 H=32 T=8192 d_h=128 bf16, dY ~ N(0,1), seed 42 "
+                        "(row statistics, dkv storing dU, dP1 from the stored dU, reduce)",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "flops_counted": flops}
+            "flops_counted": flops, "workspace_bytes": max(small, stored),
+            "recompute_path_ms_per_step": round(ms_recompute, 4), "recompute_path_workspace_bytes": small}
 
 
 def bench_prestep(torch, R, W, steps, warmup):
@@ -289,7 +299,8 @@ def bench_paper_geometry(torch, R, W, steps, warmup):
         Yl, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.5)
         grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),
                  torch.empty(H, device="cuda"), torch.empty(1, device="cuda"))
-        ws = torch.empty(R.bwd_workspace_bytes(B, H, T, d), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(R.bwd_workspace_bytes(B, H, T, d), R.bwd_stored_workspace_bytes(B, H, T, d)),
+                         dtype=torch.uint8, device="cuda")
 
         def fr_train():
             R.fwd_lse(P1, P2, V, inp["tau"], 0.5, out=Yl, lse=L)

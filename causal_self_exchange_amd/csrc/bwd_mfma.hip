@@ -341,6 +341,149 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadPa
   }
 }
 
+// ---- query gradient from the stored dU --------------------------------------
+//
+// dP1^T[d][q] += P2^T[d][key] dU^T[key][q] over the blocks the key/value
+// kernel stored: the dq kernel's transport (P2 in the transposed layout, one
+// barrier per 64-key tile), with its B operand read from the stored blocks
+// instead of formed from recomputed evidence. A stored block holds, in lane
+// L = 16 lj + k of the wave that formed it, the dU of key k for the queries
+// 16 h + 4 lj + 0..3 (h = 0, 1) as two 8-byte halves. A transposing LDS read
+// in which lane m of group g addresses key 8 half + 4 (g / 2) + m / 4 at the
+// queries 16 (g % 2) + 4 (m % 4) .. +3 gives lane 16 (g % 2) + m the dU of its
+// query for four consecutive keys: the operand order of the transport (keys
+// 16 ks + 4 (l / 32) + 0..3 and 16 ks + 8 + 4 (l / 32) + 0..3 of a 32-key
+// block). Each wave stages its own blocks next to the shared P2 tile.
+constexpr int kDuWaveTile = 4 * kDuBlockBytes;     // one wave's blocks of a 64-key tile
+
+template <int D>
+struct DquCfg : TileLayout<D> {
+  using L = TileLayout<D>;
+  static constexpr int kSlotBytes = L::kVBytes + kDqWaves * kDuWaveTile;
+  static constexpr int kLdsBytes = kDqSlots * kSlotBytes;
+  static constexpr int kPer = L::kBlocks / kDqWaves;   // P2 blocks per wave and tile
+  static constexpr int kDmaTile = kPer + 4;            // direct loads per wave and tile
+};
+
+template <int D, int DR = D>
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dqu_kernel(BwdArgs a, HeadParams hp) {
+  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  using C = DquCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
+
+  const int T = a.T;
+  const int nq = (T + kDqRows - 1) / kDqRows;
+  const int BH = a.B * a.H;
+  const int qt = nq - 1 - (int)blockIdx.x / BH;       // longest histories first
+  const int bh = (int)blockIdx.x % BH;
+  const int nt = (T + kStatRows - 1) / kStatRows;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+
+  const size_t head = (size_t)bh * (size_t)T * DR;
+  const long long head_bytes = (long long)T * DR * 2;
+  const __bf16* P2 = static_cast<const __bf16*>(a.P2) + head;
+  __bf16* dP1 = static_cast<__bf16*>(a.dP1) + head;
+
+  const int q0 = qt * kDqRows;
+  const int qrow = q0 + wave * 32 + lq;               // may be >= T: stores drop
+  const int own = q0 / 32 + wave;                     // the wave's 32-query block
+  const int kend = min(q0 + kDqRows, T) - 1;
+  const int ntiles = (kend + kTileRows - 1) / kTileRows;
+  const int nsteady = min(ntiles, q0 / kTileRows);
+
+  const int hb = (int)head_bytes;
+  int src_tr[C::kPer];
+#pragma unroll
+  for (int u = 0; u < C::kPer; ++u) src_tr[u] = C::template tr_src_real<DR>(wave + kDqWaves * u, lane);
+  // This wave's stored blocks (own, kb), kb = 0 .. 2 own + 1, lie one after
+  // another; blocks past the last one read as zeros (and are never used).
+  const int du_bytes = (int)bwd_du_head_bytes(T);
+  const u32x4 rdu = rsrc_words(static_cast<const char*>(a.du) + (size_t)bh * (size_t)du_bytes, du_bytes);
+  const long long du_src = (long long)own * (own + 1) * kDuBlockBytes + 16 * lane;
+  const int kb_last = 2 * own + 1;
+  auto dma = [&](int t) {
+    const int left = hb - t * kTileRows * DR * 2;
+    const auto rk = rsrc_words(P2 + (size_t)t * kTileRows * DR, left);
+    char* slot = smem + (t % kDqSlots) * C::kSlotBytes;
+#pragma unroll
+    for (int u = 0; u < C::kPer; ++u) dma16(rk, slot + (wave + kDqWaves * u) * C::kVBlock, src_tr[u]);
+    char* mine = slot + C::kVBytes + wave * kDuWaveTile;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int kb = 4 * t + b;
+      const long long o = du_src + (long long)kb * kDuBlockBytes;
+      dma16_nt(rdu, mine + b * kDuBlockBytes, kb <= kb_last && o < du_bytes ? (int)o : kOutOfRange);
+    }
+  };
+  const int tr_even = C::tr_base(lane, false), tr_odd = C::tr_base(lane, true);
+  const int tg = lane >> 4, tm = lane & 15;
+  const int du_lane = (16 * (tm & 3) + 4 * (tg >> 1) + (tm >> 2)) * 16 + 8 * (tg & 1);
+
+  f32x16 acc[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  auto tile = [&](int t, auto steady) __attribute__((always_inline)) {
+    if (t + 1 < ntiles) wait_vm_lgkm<C::kDmaTile, 15>();
+    else wait_vm_lgkm<0, 15>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Slot (t + 2) % 3 was last read in iteration t - 1.
+    if (t + 2 < ntiles) dma(t + 2);
+    const unsigned so = (unsigned)((t % kDqSlots) * C::kSlotBytes);
+    unsigned oe = so + tr_even, oo = so + tr_odd;
+    unsigned od = so + C::kVBytes + wave * kDuWaveTile + du_lane;
+    asm volatile("" : "+v"(oe), "+v"(oo), "+v"(od));
+    const VBase p2t{smem + oe, smem + oo};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (!decltype(steady)::value) {
+        if (mode_keys_below(2 * t + kb, own) == 0) continue;
+      }
+      u32x4 pw[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* p = smem + od + (2 * kb + ks) * kDuBlockBytes;
+        const bf16x4 lo = lds_tr_read(p), hi = lds_tr_read(p + 128);
+        pw[ks] = __builtin_bit_cast(u32x4, bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+      transport_block<D>(p2t, kb, pw, acc);
+    }
+  };
+
+  if (ntiles > 0) dma(0);
+  if (ntiles > 1) dma(1);
+  int t = 0;
+  for (; t < nsteady; ++t) tile(t, Tag<true>{});
+  for (; t < ntiles; ++t) tile(t, Tag<false>{});
+
+  if (qrow >= T) return;
+  // dP1_i = (sum_j dU_ij p2_j + dU_ii p2_i) / sqrt(d_h), dU_ii / sqrt(d_h)
+  // from the row statistics. Lane holds columns 32 db + 8 g4 + 4 hf + 0..3.
+  const float c = hp.scale;
+  const float us = a.stats[stat_at(bh, nt, qrow, 3)];
+  const size_t ro = (size_t)qrow * DR;
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      if (32 * db + 8 * g4 >= DR) continue;          // padded columns
+      const int col = 32 * db + 8 * g4 + 4 * hf;
+      float p[4];
+      load4(P2 + ro + col, p);
+      const int r = 4 * g4;
+      store4(dP1 + ro + col, fmaf(acc[db][r + 0], c, us * p[0]), fmaf(acc[db][r + 1], c, us * p[1]),
+             fmaf(acc[db][r + 2], c, us * p[2]), fmaf(acc[db][r + 3], c, us * p[3]));
+    }
+  }
+}
+
 // ---- key/value gradients ----------------------------------------------------
 //
 // v_mfma_f32_16x16x32_bf16 operand layouts (lane l, element e, register r):
@@ -416,7 +559,9 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* a, const char* b) {
   return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
-template <int D, int DR = D>
+// kDU: also store the packed dU of every processed (32-query, 16-key) pair
+// as block (qp, kb) of the stored-dU triangle, for bwd_dqu_kernel.
+template <int D, int DR = D, bool kDU = false>
 __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
   static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
   using C = KvCfg<D>;
@@ -490,6 +635,14 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs 
   };
   const int eb = C::e_base(lane);
   const int tb = C::t_base(lane);
+
+  // Stored dU: one 1 KB block per wave and pair of 16-query blocks (lane
+  // l's 16 bytes), written as soon as it is formed with the non-temporal
+  // hint (it is read once, by the query kernel, and should not push the
+  // shared P1 / dY tiles out of the L2).
+  const int nqp = (T + 31) / 32;
+  const auto rdu = rsrc(kDU ? static_cast<char*>(a.du) + (size_t)bh * (size_t)bwd_du_head_bytes(T) : nullptr,
+                        kDU ? bwd_du_head_bytes(T) : 0);
 
   f32x4 accV[C::kDb], accP[C::kDb];
 #pragma unroll
@@ -572,6 +725,12 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs 
         pw[2 * h + 0] = pack_bf16(w[0], w[1]);
         pw[2 * h + 1] = pack_bf16(w[2], w[3]);
       }
+      if constexpr (kDU) {
+        const int qp = 2 * t + p;
+        if (qp < nqp)
+          __builtin_amdgcn_raw_buffer_store_b128(pw, rdu, (qp * (qp + 1) + kblk) * kDuBlockBytes + 16 * lane, 0,
+                                                 kCachePolicyNT);
+      }
       const bf16x8 bF = __builtin_bit_cast(bf16x8, pf), bW = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < C::kDb; ++db) {
@@ -621,6 +780,15 @@ hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const int nq = (a.T + kDqRows - 1) / kDqRows;
   using Ckv = KvCfg<D>;
   const int nk = (a.T + Ckv::kKeys - 1) / Ckv::kKeys;
+  if (a.du != nullptr) {
+    // Stored dU: the row statistics first, then dkv (which also stores dU),
+    // then dP1 as a product over the stored blocks.
+    hipError_t e = launch_bwd_prep(a, hp, true, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, DR, true>), dim3(nk * BH), dim3(Ckv::kThreads), 0, s, a, hp);
+    hipLaunchKernelGGL((bwd_dqu_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
+    return hipGetLastError();
+  }
   // dq first: it writes the row statistics that dkv reads.
   hipLaunchKernelGGL((bwd_dq_kernel<D, DR>), dim3(nq * BH), dim3(kDqThreads), 0, s, a, hp);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, DR>), dim3(nk * BH), dim3(Ckv::kThreads), 0, s, a, hp);
@@ -633,6 +801,10 @@ bool bwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including
   // the rows past T of the last tile.
   return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
+}
+
+bool bwd_du_supported(int d_h, int T) {
+  return bwd_mfma_supported(d_h, T) && bwd_du_head_bytes(T) < 0x7fff0000LL;
 }
 
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {

@@ -140,6 +140,15 @@ __device__ __forceinline__ void dma16(const u32x4& r, const char* lds, int voffs
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
 }
 
+// dma16 with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ void dma16_nt(const u32x4& r, const char* lds, int voffset) {
+  const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voffset), "s"(r), "{m0}"(m0) : "memory");
+}
+
+// Cache-policy operand of the buffer store builtins: non-temporal (gfx950).
+constexpr int kCachePolicyNT = 2;
+
 __device__ __forceinline__ float lane_pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

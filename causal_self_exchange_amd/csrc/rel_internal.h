@@ -65,11 +65,23 @@ struct BwdArgs {
   float* dlambda;       // [1]
   float* stats;         // [B*H][ceil(T/64)][4][64]
   float* part;          // [B*H][ceil(T/256)][2]
+  void* du;             // stored dU blocks (bf16 MFMA backward only), or null to recompute
   int B, H, T, d_h;
 };
 
 inline int64_t bwd_stat_floats(int64_t BH, int64_t T) { return BH * ((T + kStatRows - 1) / kStatRows) * kStatTile; }
 inline int64_t bwd_part_floats(int64_t BH, int64_t T) { return BH * ((T + kPrepRows - 1) / kPrepRows) * 2; }
+
+// Stored dU of the bf16 MFMA backward: per head, blocks of 32 queries x 16
+// keys (1 KB of bf16) for every 32-query block qp and 16-key block kb with
+// kb <= 2 qp + 1 (the lower triangle, strictly-causal entries; zeros above the
+// diagonal), block (qp, kb) at index qp (qp + 1) + kb.
+constexpr int kDuBlockBytes = 1024;
+__host__ __device__ inline int64_t bwd_du_head_blocks(int64_t T) {
+  const int64_t nqp = (T + 31) / 32;
+  return nqp * (nqp + 1);
+}
+__host__ __device__ inline int64_t bwd_du_head_bytes(int64_t T) { return bwd_du_head_blocks(T) * kDuBlockBytes; }
 
 // Model-side pre-steps: rotary encoding of P1 / P2 and Givens mixing of the
 // information heads (one HBM pass; outputs may be the inputs).
@@ -130,6 +142,9 @@ hipError_t launch_bwd_scan(const BwdArgs& a, const HeadParams& hp, bool bf16, hi
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(int d_h, int T);
+// Whether the bf16 MFMA backward can store dU for this length (one head's
+// blocks addressed with 31-bit byte offsets).
+bool bwd_du_supported(int d_h, int T);
 hipError_t launch_prestep(const PrestepArgs& a, const PrestepParams& pp, bool bf16, hipStream_t s);
 hipError_t launch_linear(const LinArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);

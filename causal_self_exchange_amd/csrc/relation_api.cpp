@@ -315,6 +315,15 @@ size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h) {
          align256(static_cast<size_t>(rel::bwd_part_floats(BH, T)) * sizeof(float));
 }
 
+size_t relation_bwd_stored_workspace_bytes(int B, int H, int T, int d_h) {
+  const size_t base = relation_bwd_workspace_bytes(B, H, T, d_h);
+  if (base == 0 || !rel::bwd_du_supported(d_h, T)) return 0;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const int64_t hb = rel::bwd_du_head_bytes(T);
+  if (BH > (INT64_MAX / 2) / hb) return 0;
+  return base + align256(static_cast<size_t>(BH * hb));
+}
+
 rel_status relation_bwd(const void* P1, const void* P2, const void* V, const float* tau_s,
                         float lambda, const void* Y, const float* LSE, const void* dY, void* dP1,
                         void* dP2, void* dV, float* dtau, float* dlambda, int B, int H, int T,
@@ -329,8 +338,13 @@ rel_status relation_bwd(const void* P1, const void* P2, const void* V, const flo
   HeadParams hp;
   const rel_status st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
-  const size_t need = relation_bwd_workspace_bytes(B, H, T, d_h);
-  if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  const size_t base = relation_bwd_workspace_bytes(B, H, T, d_h);
+  if (!workspace || ws_bytes < base) return REL_E_WORKSPACE;
+  // The bf16 MFMA backward stores dU when the workspace holds it.
+  const size_t stored = relation_bwd_stored_workspace_bytes(B, H, T, d_h);
+  const bool mfma = use_bwd_mfma(dt, d_h, T);
+  const bool store_du = mfma && stored != 0 && ws_bytes >= stored;
+  const size_t need = store_du ? stored : base;
   if (!aligned16(P1) || !aligned16(P2) || !aligned16(V) || !aligned16(Y) || !aligned16(dY) ||
       !aligned16(dP1) || !aligned16(dP2) || !aligned16(dV) || !aligned16(workspace) || !aligned4(LSE) ||
       !aligned4(dtau) || !aligned4(dlambda))
@@ -352,11 +366,13 @@ rel_status relation_bwd(const void* P1, const void* P2, const void* V, const flo
   char* ws = static_cast<char*>(workspace);
   float* stats = reinterpret_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::bwd_stat_floats(BH, T)) * sizeof(float)));
-  rel::BwdArgs a{P1, P2, V, Y, dY, LSE, dP1, dP2, dV, dtau, dlambda, stats, part, B, H, T, d_h};
+  void* du = store_du ? static_cast<void*>(ws + base) : nullptr;
+  rel::BwdArgs a{P1, P2, V, Y, dY, LSE, dP1, dP2, dV, dtau, dlambda, stats, part, du, B, H, T, d_h};
   const bool bf16 = dt == REL_BF16;
   hipError_t e;
-  if (use_bwd_mfma(dt, d_h, T)) {
-    // The MFMA query kernel forms the row statistics itself.
+  if (mfma) {
+    // Recomputing: the MFMA query kernel forms the row statistics itself.
+    // Storing dU: the prep kernel forms them first.
     e = rel::launch_bwd_mfma_bf16(a, hp, stream);
   } else {
     e = rel::launch_bwd_prep(a, hp, bf16, stream);

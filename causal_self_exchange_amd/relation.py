@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.relation_fwd_lse.restype = i
         L.relation_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.relation_bwd_workspace_bytes.restype = sz
+        L.relation_bwd_stored_workspace_bytes.argtypes = [i, i, i, i]
+        L.relation_bwd_stored_workspace_bytes.restype = sz
         L.relation_bwd.argtypes = [vp, vp, vp, fp, f, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         L.relation_bwd.restype = i
         L.relation_prestep.argtypes = [vp, vp, vp, vp, i, f, fp, i, vp, vp, vp, i, i, i, i, i, vp]
@@ -74,7 +76,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("relation_fwd", "relation_fwd_ex", "relation_fwd_lse", "relation_bwd_workspace_bytes",
-           "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
+           "relation_bwd_stored_workspace_bytes", "relation_bwd", "relation_prestep", "relation_fwd_model_workspace_bytes",
            "relation_fwd_model", "relation_linear_workspace_bytes", "relation_linear_fwd",
            "relation_decode_workspace_bytes", "relation_decode", "relation_decode_noalloc",
            "relation_cache_append", "relation_status_str", "relation_select_kernels")
@@ -220,9 +222,17 @@ def bwd_workspace_bytes(B: int, H: int, T: int, d_h: int) -> int:
     return int(lib().relation_bwd_workspace_bytes(B, H, T, d_h))
 
 
-def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None):
+def bwd_stored_workspace_bytes(B: int, H: int, T: int, d_h: int) -> int:
+    return int(lib().relation_bwd_stored_workspace_bytes(B, H, T, d_h))
+
+
+def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None, store_du=None):
     """Gradients (dP1, dP2, dV, dtau [H] fp32, dlambda [1] fp32) of sum(Y * dY),
-    from the forward's inputs and its outputs Y, LSE (fwd_lse)."""
+    from the forward's inputs and its outputs Y, LSE (fwd_lse).
+
+    store_du (when no workspace is given): True or None allocates the workspace
+    with which the bf16 MFMA path stores dU (where that path exists), False
+    the smaller one with which it recomputes the evidence for dP1."""
     shp = _shape4("bwd", P1)
     B, H, T, D = shp
     dt = P1.dtype
@@ -236,6 +246,8 @@ def bwd(P1, P2, V, tau, lam, Y, lse, dY, grads=None, workspace=None, stream=None
     need = bwd_workspace_bytes(B, H, T, D)
     if workspace is not None:
         a.bytes("workspace", workspace, need)
+    elif store_du is not False and dt == torch.bfloat16:
+        need = max(need, bwd_stored_workspace_bytes(B, H, T, D))
     a.done()
     if grads is None:
         grads = (torch.empty_like(P1), torch.empty_like(P2), torch.empty_like(V),

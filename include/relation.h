@@ -140,6 +140,18 @@ rel_status relation_fwd_lse(const void* P1, const void* P2, const void* V,
 size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h);
 
 /*
+ * relation_bwd_stored_workspace_bytes - bytes of device workspace with which
+ * relation_bwd (dtype REL_BF16, d_h in {48, 64, 80, 128}) stores dU once
+ * instead of recomputing the evidence for dP1: the statistics and partials
+ * of relation_bwd_workspace_bytes plus dU in bf16 for every strictly causal
+ * (query, key) pair, in blocks of 32 queries x 16 keys (about B H T^2 bytes;
+ * 2.1 GB for B = 1, H = 32, T = 8192). 0 on invalid sizes, or where that path
+ * is not available (a head's dU blocks must stay below 2^31 bytes, i.e.
+ * T <= 46,304).
+ */
+size_t relation_bwd_stored_workspace_bytes(int B, int H, int T, int d_h);
+
+/*
  * relation_bwd - gradients of the forward (Eq. (1)-(3) with the count term of
  * Eq. (2)) for an upstream gradient dY = dL/dY:
  *   dP1, dP2, dV : dL/dP1, dL/dP2, dL/dV, device [B, H, T, d_h], dtype dt
@@ -157,7 +169,13 @@ size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h);
  *   Y, LSE       : in, the forward's outputs from relation_fwd_lse with the
  *                  same inputs
  *   dY           : in, device [B, H, T, d_h], dtype dt
- *   workspace    : device scratch of >= relation_bwd_workspace_bytes bytes
+ *   workspace    : device scratch of >= relation_bwd_workspace_bytes bytes;
+ *                  with >= relation_bwd_stored_workspace_bytes bytes (when
+ *                  that is not 0) the bf16 MFMA path stores dU in it: the
+ *                  key/value pass writes each dU block once and the query
+ *                  pass forms dP1 = dU P2 from the stored blocks, instead of
+ *                  recomputing U, dY V^T and the weights (same roundings: dU
+ *                  is a bf16 MFMA operand on both paths)
  * Every output is overwritten (not accumulated into). The result is
  * deterministic: no atomics, scalar sums in a fixed order (fp64 across rows
  * chunks, heads and batch).

@@ -208,6 +208,25 @@ def test_bwd_workspace_bytes():
     assert lib.relation_bwd_workspace_bytes(4, 8, 1024, 48) == want(4, 8, 1024)
 
 
+def test_bwd_stored_workspace_bytes():
+    """The statistics and partials, then per head nqp (nqp + 1) blocks of
+    1 KB (nqp = ceil(T / 32)), 256-aligned; 0 where the path does not exist."""
+    lib = R.lib()
+    def want(B, H, T, D):
+        nqp = (T + 31) // 32
+        du = B * H * nqp * (nqp + 1) * 1024
+        return lib.relation_bwd_workspace_bytes(B, H, T, D) + ((du + 255) // 256) * 256
+    for B, H, T, D in ((1, 32, 8192, 128), (2, 3, 1, 64), (4, 16, 2049, 64), (1, 2, 300, 48), (1, 1, 77, 80)):
+        assert lib.relation_bwd_stored_workspace_bytes(B, H, T, D) == want(B, H, T, D)
+    assert lib.relation_bwd_stored_workspace_bytes(1, 32, 8192, 128) == 2_155_872_256 + \
+        lib.relation_bwd_workspace_bytes(1, 32, 8192, 128)
+    assert lib.relation_bwd_stored_workspace_bytes(1, 1, 10, 32) == 0        # no MFMA backward at d_h = 32
+    assert lib.relation_bwd_stored_workspace_bytes(1, 1, 10, 96) == 0
+    assert lib.relation_bwd_stored_workspace_bytes(0, 1, 10, 64) == 0
+    assert lib.relation_bwd_stored_workspace_bytes(1, 1, 46304, 64) > 0     # largest length with 31-bit offsets
+    assert lib.relation_bwd_stored_workspace_bytes(1, 1, 46305, 64) == 0
+
+
 def bwd(P1=A, P2=B_, V=C, tau=(1.0, 1.0), lam=0.0, Yp=Y, L=LSE_, dY=DY_, dP1=G1, dP2=G2, dV=G3,
         dtau=DT, dlam=DL, B=1, H=2, T=16, D=64, dt=R.REL_BF16, ws=WS, ws_bytes=None):
     keep, tp = _tau(tau) if tau is not None else (None, None)

@@ -36,11 +36,11 @@ def _dev(inp, keys=("P1", "P2", "V", "dY")):
     return [inp[k].to(DEV).contiguous() for k in keys]
 
 
-def _gpu_train(inp, lam, bwd_kernel=None):
+def _gpu_train(inp, lam, bwd_kernel=None, store_du=None):
     P1, P2, V, dY = _dev(inp)
     with R.kernels(bwd=bwd_kernel or "auto"):
         Y, L = R.fwd_lse(P1, P2, V, inp["tau"], lam)
-        g = R.bwd(P1, P2, V, inp["tau"], lam, Y, L, dY)
+        g = R.bwd(P1, P2, V, inp["tau"], lam, Y, L, dY, store_du=store_du)
     torch.cuda.synchronize()
     return Y, L, g
 
@@ -143,6 +143,39 @@ def test_bwd_ragged_shapes(shape, lam):
     inp = W.make_bwd_inputs(cfg, 11 + T)
     Y, L, g = _gpu_train(inp, lam)
     _check(inp, lam, dt, Y, L, g, f"{shape} lam={lam}")
+
+
+MFMA_SHAPES = [s for s in SHAPES if s[4] == "bf16" and s[3] in (48, 64, 80, 128)]
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_recompute_path(shape):
+    """The bf16 MFMA backward with the small workspace: the query pass
+    recomputes the evidence and weights instead of reading the stored dU."""
+    B, H, T, D, dt = shape
+    cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_bwd_inputs(cfg, 11 + T)
+    Y, L, g = _gpu_train(inp, 0.5, store_du=False)
+    _check(inp, 0.5, dt, Y, L, g, f"recompute {shape}")
+
+
+def test_bwd_stored_path_uses_the_stored_workspace():
+    """With the larger workspace the stored-dU path runs and writes dU
+    blocks there (the recompute path leaves the workspace past the
+    statistics untouched)."""
+    cfg = W.FwdConfig("t", 1, 2, 200, 64, "bf16", tau=("uniform", 0.5, 2.0))
+    inp = W.make_bwd_inputs(cfg, 3)
+    P1, P2, V, dY = _dev(inp)
+    Y, L = R.fwd_lse(P1, P2, V, inp["tau"], 0.0)
+    small = R.bwd_workspace_bytes(1, 2, 200, 64)
+    big = R.bwd_stored_workspace_bytes(1, 2, 200, 64)
+    assert big > small
+    for ws_bytes, touched in ((big, True), (small, False)):
+        ws = torch.full((big,), 0x7F, dtype=torch.uint8, device=DEV)
+        R.bwd(P1, P2, V, inp["tau"], 0.0, Y, L, dY, workspace=ws[:ws_bytes])
+        torch.cuda.synchronize()
+        tail = ws[-(big - small) // 2:]
+        assert bool((tail != 0x7F).any()) == touched
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
