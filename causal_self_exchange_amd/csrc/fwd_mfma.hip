@@ -214,8 +214,11 @@ struct StepKind {
 // the rows' real head size in memory (48 runs on the 64 layout and 80 on the
 // 128 layout, the chunks past DR held at zero, so evidence and transport are
 // exact and the padded output rows are not stored).
-template <int D, int DR, bool kLse>
-__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadParams hp) {
+// kRope: P1 is rotated (rotary position encoding, interleaved or half-split
+// pairs) after each query tile's rows are loaded, as the pre-step would have
+// rotated it (same angles, fp32 rotation, one bf16 rounding).
+template <int D, int DR, bool kLse, bool kRope>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, const HeadParams& hp, const RopeParams& rp) {
   static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
   using C = Cfg<D>;
   constexpr int kNS = C::kSteps;
@@ -268,6 +271,48 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
       // k-steps past DR / 16 cover padded columns: out-of-range offsets read 0.
       const int o = ds < DR / 16 ? qoff + ds * 32 : kOutOfRange;
       qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rP1, o, 0, 0));
+    }
+  };
+
+  // Rotate the loaded query rows of tile qt of head bh (kRope). The lane
+  // holds row q0 + 32 wave + lane % 32 at columns 16 ds + 8 (lane / 32) + e:
+  // interleaved pair k = (2k, 2k+1) lies in one 8-element chunk; half-split
+  // pair k = (k, k + DR/2) lies in chunks ds and ds + DR/32 of the same lane.
+  auto rope_q = [&](int qt, int bh) __attribute__((always_inline)) {
+    if constexpr (kRope) {
+      const int lane = lane_now();
+      const int hf = lane >> 5;
+      const int row = qt * kBM + wave * 32 + (lane & 31);
+      const long long p0 = rp.pos0 ? (long long)rp.pos0[bh / a.H] : 0;
+      const double pos = (double)(p0 + row);
+      // (x, y) -> (x cos - y sin, x sin + y cos), in fp32, rounded to bf16
+      auto turn = [&](float u, float v, int k, __bf16* out) __attribute__((always_inline)) {
+        float sn, cs;
+        sincos_of(pos * rp.inv_freq[k], &sn, &cs);
+        out[0] = (__bf16)fmaf(u, cs, -v * sn);
+        out[1] = (__bf16)fmaf(u, sn, v * cs);
+      };
+      if (rp.rope == 1) {
+#pragma unroll
+        for (int ds = 0; ds < DR / 16; ++ds)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            __bf16 r[2];
+            turn((float)qf[ds][2 * e], (float)qf[ds][2 * e + 1], 8 * ds + 4 * hf + e, r);
+            qf[ds][2 * e] = r[0];
+            qf[ds][2 * e + 1] = r[1];
+          }
+      } else if constexpr (DR % 32 == 0) {
+#pragma unroll
+        for (int ds = 0; ds < DR / 32; ++ds)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            __bf16 r[2];
+            turn((float)qf[ds][e], (float)qf[ds + DR / 32][e], 16 * ds + 8 * hf + e, r);
+            qf[ds][e] = r[0];
+            qf[ds + DR / 32][e] = r[1];
+          }
+      }
     }
   };
 
@@ -473,7 +518,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     dma_v(2);
     wait_vm_lgkm<4 * C::kDmaPerWave, 15>();
     __syncthreads();
-    if (!kLse && pass == 0) prescale_q();   // the redo scales its own reload
+    if (pass == 0) {                        // the redo transforms its own reload
+      rope_q(qt, bh);
+      if (!kLse) prescale_q();
+    }
 #pragma unroll
     for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
@@ -600,6 +648,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
     // scan, which would hold their registers in every tile.
     load_q(qt, bh);
     wait_vm_lgkm<0, 15>();
+    rope_q(qt, bh);
     if (!kLse) prescale_q();
     float amax = -INFINITY;
     const int lq = lane_now() & 31, hf = lane_now() >> 5;
@@ -721,8 +770,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadPa
   }
 }
 
+template <int D, int DR, bool kLse>
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, HeadParams hp) {
+  const RopeParams none{};
+  fwd_body<D, DR, kLse, false>(a, hp, none);
+}
+
+template <int D, int DR, bool kLse>
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_rope_kernel(FwdArgs a, HeadParams hp, RopeParams rp) {
+  fwd_body<D, DR, kLse, true>(a, hp, rp);
+}
+
 template <int D, int DR>
-hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
+hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s, const RopeParams* rp) {
   const int nq = (a.T + kBM - 1) / kBM;
   const long long nwork = (long long)((nq + 1) / 2) * a.B * a.H;
   if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -731,7 +791,13 @@ hipError_t launch_typed(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
   const hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
   const long long grid = nwork < n_cu ? nwork : n_cu;
-  if (a.lse != nullptr) {
+  if (rp != nullptr) {
+    if (a.lse != nullptr) {
+      hipLaunchKernelGGL((fwd_mfma_rope_kernel<D, DR, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp, *rp);
+    } else {
+      hipLaunchKernelGGL((fwd_mfma_rope_kernel<D, DR, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp, *rp);
+    }
+  } else if (a.lse != nullptr) {
     hipLaunchKernelGGL((fwd_mfma_kernel<D, DR, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
   } else {
     hipLaunchKernelGGL((fwd_mfma_kernel<D, DR, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, hp);
@@ -765,12 +831,17 @@ bool fwd_mfma_supported(int d_h, int T) {
   return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kBM) * d_h * 2 < 0x7fffffffLL;
 }
 
-hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s) {
+bool fwd_mfma_rope_fusable(int d_h, int rope) {
+  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && (rope == 1 || (rope == 2 && d_h % 32 == 0));
+}
+
+hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s, const RopeParams* rp) {
+  if (rp != nullptr && !fwd_mfma_rope_fusable(a.d_h, rp->rope)) return hipErrorInvalidValue;
   switch (a.d_h) {
-    case 48: return launch_typed<64, 48>(a, hp, s);
-    case 64: return launch_typed<64, 64>(a, hp, s);
-    case 80: return launch_typed<128, 80>(a, hp, s);
-    case 128: return launch_typed<128, 128>(a, hp, s);
+    case 48: return launch_typed<64, 48>(a, hp, s, rp);
+    case 64: return launch_typed<64, 64>(a, hp, s, rp);
+    case 80: return launch_typed<128, 80>(a, hp, s, rp);
+    case 128: return launch_typed<128, 128>(a, hp, s, rp);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,26 +54,6 @@ __device__ __forceinline__ void store8(Tin* p, const float (&x)[8]) {
   }
 }
 
-// sin and cos of an angle held in fp64: reduced by pi/2 in fp64 (the
-// remainder r, |r| <= pi/4, is exact to far below fp32 resolution for the
-// angles a position count produces), then the single-precision minimax
-// polynomials for sin and cos on [-pi/4, pi/4] published with S. Moshier's
-// Cephes library (sinf / cosf), and the quadrant's swap and signs. Accurate
-// to a few fp32 ulps, with none of a general sincosf's large-argument path.
-__device__ __forceinline__ void sincos_of(double ang, float* s, float* c) {
-  const double k = rint(ang * 0.63661977236758134);           // 2 / pi
-  const float r = (float)fma(-k, 1.5707963267948966, ang);     // ang - k pi / 2
-  const int q = (int)(long long)k & 3;                          // quadrant (two's complement mod 4)
-  const float z = r * r;
-  const float sr = fmaf(r * z, fmaf(z, fmaf(z, -1.9515295891e-4f, 8.3321608736e-3f), -1.6666654611e-1f), r);
-  const float cr = fmaf(z * z, fmaf(z, fmaf(z, 2.443315711809948e-5f, -1.388731625493765e-3f), 4.166664568298827e-2f),
-                        fmaf(-0.5f, z, 1.0f));
-  const float sv = (q & 1) ? cr : sr;                          // sin(r + q pi/2), cos(r + q pi/2)
-  const float cv = (q & 1) ? sr : cr;
-  *s = (q & 2) ? -sv : sv;
-  *c = ((q + 1) & 2) ? -cv : cv;
-}
-
 // Rotate 8 pairs (a[e], b[e]) by angles with cosines c[e], sines s[e].
 __device__ __forceinline__ void rotate(float (&a)[8], float (&b)[8], const float (&c)[8], const float (&s)[8]) {
 #pragma unroll
@@ -109,8 +89,10 @@ __global__ __launch_bounds__(kThreads) void prestep_kernel(PrestepArgs a, Preste
   if (copy_coords) {
     const Tin* P1 = static_cast<const Tin*>(a.P1) + ro;
     const Tin* P2 = static_cast<const Tin*>(a.P2) + ro;
-    load8(P1 + oa, c1[0]);
-    load8(P1 + ob, c1[1]);
+    if (!a.skip_p1) {
+      load8(P1 + oa, c1[0]);
+      load8(P1 + ob, c1[1]);
+    }
     load8(P2 + oa, c2[0]);
     load8(P2 + ob, c2[1]);
   }
@@ -140,6 +122,7 @@ __global__ __launch_bounds__(kThreads) void prestep_kernel(PrestepArgs a, Preste
     for (int e = 0; e < 8; ++e) sincos_of((double)pos * pp.inv_freq[8 * g + e], &sn[e], &c[e]);
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
+      if (w == 0 && a.skip_p1) continue;
       float(&x)[2][8] = w ? c2 : c1;
       if (a.rope == 1) {
         // pairs (x0,x1) (x2,x3) ... of the 16 consecutive elements
@@ -163,8 +146,10 @@ __global__ __launch_bounds__(kThreads) void prestep_kernel(PrestepArgs a, Preste
   if (copy_coords) {
     Tin* P1o = static_cast<Tin*>(a.P1o) + ro;
     Tin* P2o = static_cast<Tin*>(a.P2o) + ro;
-    store8(P1o + oa, c1[0]);
-    store8(P1o + ob, c1[1]);
+    if (!a.skip_p1) {
+      store8(P1o + oa, c1[0]);
+      store8(P1o + ob, c1[1]);
+    }
     store8(P2o + oa, c2[0]);
     store8(P2o + ob, c2[1]);
   }

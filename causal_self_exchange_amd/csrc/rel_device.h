@@ -46,4 +46,24 @@ struct RowCombine {
   }
 };
 
+// sin and cos of an angle held in fp64: reduced by pi/2 in fp64 (the
+// remainder r, |r| <= pi/4, is exact to far below fp32 resolution for the
+// angles a position count produces), then the single-precision minimax
+// polynomials for sin and cos on [-pi/4, pi/4] published with S. Moshier's
+// Cephes library (sinf / cosf), and the quadrant's swap and signs. Accurate
+// to a few fp32 ulps, with none of a general sincosf's large-argument path.
+__device__ __forceinline__ void sincos_of(double ang, float* s, float* c) {
+  const double k = rint(ang * 0.63661977236758134);           // 2 / pi
+  const float r = (float)fma(-k, 1.5707963267948966, ang);     // ang - k pi / 2
+  const int q = (int)(long long)k & 3;                          // quadrant (two's complement mod 4)
+  const float z = r * r;
+  const float sr = fmaf(r * z, fmaf(z, fmaf(z, -1.9515295891e-4f, 8.3321608736e-3f), -1.6666654611e-1f), r);
+  const float cr = fmaf(z * z, fmaf(z, fmaf(z, 2.443315711809948e-5f, -1.388731625493765e-3f), 4.166664568298827e-2f),
+                        fmaf(-0.5f, z, 1.0f));
+  const float sv = (q & 1) ? cr : sr;                          // sin(r + q pi/2), cos(r + q pi/2)
+  const float cv = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -sv : sv;
+  *c = ((q + 1) & 2) ? -cv : cv;
+}
+
 }  // namespace rel

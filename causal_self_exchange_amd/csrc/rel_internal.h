@@ -97,6 +97,7 @@ struct PrestepArgs {
   int rope;             // 0 none, 1 interleaved pairs, 2 half split
   int pairing;          // 0: (1,2),(3,4),...; 1: (2,3),...,(H,1) (one-based heads)
   int mix;              // 1: Givens mixing of I, 0: copy
+  int skip_p1;          // 1: P1 is neither read nor written (the forward rotates it)
 };
 
 struct PrestepParams {
@@ -133,8 +134,21 @@ hipError_t launch_fwd_scan(const FwdArgs& a, const HeadParams& hp, bool bf16, hi
 // Compute units of the current device (queried once per device, then cached:
 // the library's only global state).
 hipError_t device_cu_count(int* n_cu);
-hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s);
+// Rotary encoding of P1 applied by the MFMA forward as it loads a query tile
+// (relation_fwd_model): the pre-step's rotation of each row, with the same
+// angles and roundings, so the result equals pre-step then forward.
+struct RopeParams {
+  const int32_t* pos0;  // optional device int32[B]: position of row 0 per sequence
+  int rope;             // 1 interleaved pairs, 2 half split
+  double inv_freq[64];  // base^(-2k/d_h), k < d_h / 2
+};
+hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s,
+                                const RopeParams* rope = nullptr);
 bool fwd_mfma_supported(int d_h, int T);
+// Whether the MFMA forward can rotate P1 itself: interleaved pairs at any
+// head size, half-split pairs where both halves of a pair sit in one lane
+// (d_h a multiple of 32).
+bool fwd_mfma_rope_fusable(int d_h, int rope);
 // Backward: prep (row statistics, dtau / dlambda partials) then the query and
 // key/value gradient kernels, then the fixed-order reduce.
 hipError_t launch_bwd_prep(const BwdArgs& a, const HeadParams& hp, bool bf16, hipStream_t s);

@@ -233,6 +233,7 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I, con
     return dtype_ok(dt) ? REL_E_HEADDIM : REL_E_DTYPE;
   }
   if (!workspace || ws_bytes < need) return REL_E_WORKSPACE;
+  if (H > REL_MAX_HEADS || B > 65535) return REL_E_SHAPE;
   const size_t part = need / 3;
   char* ws = static_cast<char*>(workspace);
   rel::PrestepArgs a;
@@ -258,8 +259,19 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I, con
   HeadParams hp;
   st = pack_heads(hp, tau_s, H, d_h, lambda);
   if (st != REL_OK) return st;
+  // The bf16 MFMA forward rotates P1 itself as it loads each query tile: the
+  // pre-step then rotates P2 and mixes I only, and P1 is read once.
+  const bool fuse = rope != REL_ROPE_NONE && use_mfma(dt, d_h, T) &&
+                    rel::fwd_mfma_rope_fusable(d_h, static_cast<int>(rope));
+  if (fuse) a.skip_p1 = 1;
   if (rel::launch_prestep(a, pp, dt == REL_BF16, stream) != hipSuccess) return REL_E_LAUNCH;
-  return fwd_impl(ws, ws + part, ws + 2 * part, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
+  if (!fuse) return fwd_impl(ws, ws + part, ws + 2 * part, tau_s, lambda, Y, LSE, B, H, T, d_h, dt, stream);
+  rel::RopeParams rp;
+  rp.pos0 = pos0;
+  rp.rope = static_cast<int>(rope);
+  for (int k = 0; k < 64; ++k) rp.inv_freq[k] = pp.inv_freq[k];
+  const rel::FwdArgs fa{P1, ws + part, ws + 2 * part, Y, B, H, T, d_h, LSE};
+  return rel::launch_fwd_mfma_bf16(fa, hp, stream, &rp) == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
 
 size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h) {

@@ -325,7 +325,9 @@ def prestep_launcher(P1, P2, I, pos0, rope, rope_base, theta, pairing, out, stre
 def fwd_model(P1, P2, I, tau, lam: float = 0.0, pos0=None, rope="interleaved", rope_base: float = 1e4,
               theta=None, pairing="A", out=None, lse=None, workspace=None, stream=None):
     """The operator on raw projections: pre-steps, then the forward. Returns
-    (Y, LSE or None, workspace holding the pre-stepped tensors)."""
+    (Y, LSE or None, workspace): the workspace holds the pre-stepped P2 and I
+    (second and third slots) and, unless the bf16 MFMA forward rotated P1
+    itself, the rotated P1 (first slot)."""
     shp = _shape4("fwd_model", P1)
     B, H, T, D = shp
     a = _Args("fwd_model")("P1", P1)("P2", P2, shp, P1.dtype)("I", I, shp, P1.dtype)

@@ -9,7 +9,8 @@ namespace rel {
 
 hipError_t launch_fwd_scan(const FwdArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t device_cu_count(int* n_cu) { *n_cu = 1; return hipSuccess; }
-hipError_t launch_fwd_mfma_bf16(const FwdArgs&, const HeadParams&, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t launch_fwd_mfma_bf16(const FwdArgs&, const HeadParams&, hipStream_t, const RopeParams*) { return hipErrorLaunchFailure; }
+bool fwd_mfma_rope_fusable(int, int) { return false; }
 bool fwd_mfma_supported(int, int) { return false; }
 hipError_t launch_bwd_prep(const BwdArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_bwd_scan(const BwdArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }

@@ -234,9 +234,14 @@ size_t relation_fwd_model_workspace_bytes(int B, int H, int T, int d_h,
  * computes it: relation_prestep into the workspace, then relation_fwd_lse
  * (LSE may be NULL) on the rotated P1 / P2 and the mixed information I~.
  * Arguments as for those two calls; Y and LSE may not overlap the inputs or
- * the workspace. After the call the workspace holds the pre-stepped tensors
- * (rotated P1, rotated P2, mixed I, each 256-byte aligned, in that order),
- * which a backward on the rotated coordinates can reuse.
+ * the workspace. The workspace has three 256-byte aligned slots (rotated P1,
+ * rotated P2, mixed I, in that order); after the call the last two hold the
+ * pre-stepped P2 and I. Where the bf16 MFMA forward rotates P1 itself as it
+ * loads each query tile (REL_BF16, d_h in {48, 64, 80, 128}, interleaved
+ * pairs, or half-split pairs with d_h a multiple of 32) the first slot is
+ * not written, and the result equals pre-step then forward bit for bit;
+ * otherwise the first slot holds the rotated P1. A backward on the rotated
+ * coordinates takes rotated P1 from relation_prestep.
  */
 rel_status relation_fwd_model(const void* P1, const void* P2, const void* I,
                               const int32_t* pos0, rel_rope rope,

@@ -108,27 +108,45 @@ def test_prestep_without_angles_copies_information_and_allows_odd_heads():
     assert torch.equal(o3, I)
 
 
+def _fused(D, dt, mode):
+    """Whether the bf16 MFMA forward rotates P1 itself (relation_fwd_model):
+    interleaved pairs at every head size, half-split pairs when d_h % 32 == 0."""
+    return dt == "bf16" and D in (48, 64, 80, 128) and (mode == "interleaved" or D % 32 == 0)
+
+
+@pytest.mark.parametrize("with_lse", [True, False])
 @pytest.mark.parametrize("mode,pairing", [("interleaved", "A"), ("half", "B")])
-@pytest.mark.parametrize("case", [(2, 4, 300, 64, "bf16"), (1, 8, 513, 128, "bf16"), (1, 2, 128, 32, "f32")],
+@pytest.mark.parametrize("case", [(2, 4, 300, 64, "bf16"), (1, 8, 513, 128, "bf16"), (1, 2, 128, 32, "f32"),
+                                  (1, 4, 200, 80, "bf16"), (2, 2, 150, 48, "bf16")],
                          ids=lambda c: "x".join(map(str, c)))
-def test_model_forward_matches_oracle(case, mode, pairing):
+def test_model_forward_matches_oracle(case, mode, pairing, with_lse):
     B, H, T, D, dt = case
     inp, theta, pos0 = _inputs(B, H, T, D, dt, 8 + T)
     P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
     p0 = torch.from_numpy(pos0).to(DEV)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV) if with_lse else None
     Y, L, ws = R.fwd_model(P1, P2, I, inp["tau"], 0.5, p0, mode, 1e4, theta, pairing, lse=lse)
     torch.cuda.synchronize()
     ref = PO.relation_fwd_model(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), inp["tau"].astype(np.float64),
                                 0.5, pos0, 1e4, mode, theta.astype(np.float64), pairing)
     assert_parity(f64(Y), ref, W.torch_dtype(dt), f"{case} {mode}")
-    # The workspace holds the pre-stepped tensors the forward consumed.
+    # The workspace holds the pre-stepped P2 and I the forward consumed, and
+    # P1 too unless the forward rotated it itself as it loaded each query
+    # tile. Either way the result is the forward on the pre-stepped tensors,
+    # bit for bit (same angles, same fp32 rotation, same bf16 rounding).
     n = B * H * T * D
     es = 2 if dt == "bf16" else 4
     part = ((n * es + 255) // 256) * 256
     tdt = W.torch_dtype(dt)
     pre = [ws[k * part: k * part + n * es].view(tdt).view(B, H, T, D) for k in range(3)]
     want = R.prestep(P1, P2, I, p0, mode, 1e4, theta, pairing)
+    if with_lse:
+        Y2, L2 = R.fwd_lse(want[0], want[1], want[2], inp["tau"], 0.5)
+    else:
+        Y2, L2 = R.fwd(want[0], want[1], want[2], inp["tau"], 0.5), None
     torch.cuda.synchronize()
-    for x, y in zip(pre, want):
-        assert torch.equal(x, y)
+    for k in ((1, 2) if _fused(D, dt, mode) else (0, 1, 2)):
+        assert torch.equal(pre[k], want[k])
+    assert torch.equal(Y, Y2)
+    if with_lse:
+        assert torch.equal(L, L2)
