@@ -120,7 +120,7 @@ using Tag = std::integral_constant<bool, B>;
 // not stored).
 template <int D, int DR = D>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, HeadParams hp) {
-  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  static_assert(DR % 16 == 0 && DR <= D && DR >= 32, "real head size within the layout");
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
@@ -367,7 +367,7 @@ struct DquCfg : TileLayout<D> {
 
 template <int D, int DR = D>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dqu_kernel(BwdArgs a, HeadParams hp) {
-  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  static_assert(DR % 16 == 0 && DR <= D && DR >= 32, "real head size within the layout");
   using C = DquCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
@@ -563,7 +563,7 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* a, const char* b) {
 // as block (qp, kb) of the stored-dU triangle, for bwd_dqu_kernel.
 template <int D, int DR = D, bool kDU = false>
 __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkv_kernel(BwdArgs a, HeadParams hp) {
-  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  static_assert(DR % 16 == 0 && DR <= D && DR >= 32, "real head size within the layout");
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
 
@@ -800,7 +800,7 @@ hipError_t launch_typed(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
 bool bwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including
   // the rows past T of the last tile.
-  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
+  return (d_h == 32 || d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kDqRows) * d_h * 2 < 0x7fffffffLL;
 }
 
 bool bwd_du_supported(int d_h, int T) {
@@ -809,6 +809,7 @@ bool bwd_du_supported(int d_h, int T) {
 
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, const HeadParams& hp, hipStream_t s) {
   switch (a.d_h) {
+    case 32: return launch_typed<64, 32>(a, hp, s);
     case 48: return launch_typed<64, 48>(a, hp, s);
     case 64: return launch_typed<64>(a, hp, s);
     case 80: return launch_typed<128, 80>(a, hp, s);

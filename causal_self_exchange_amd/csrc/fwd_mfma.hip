@@ -219,7 +219,7 @@ struct StepKind {
 // rotated it (same angles, fp32 rotation, one bf16 rounding).
 template <int D, int DR, bool kLse, bool kRope>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, const HeadParams& hp, const RopeParams& rp) {
-  static_assert(DR % 16 == 0 && DR <= D && DR > D / 2, "real head size within the layout");
+  static_assert(DR % 16 == 0 && DR <= D && DR >= 32, "real head size within the layout");
   using C = Cfg<D>;
   constexpr int kNS = C::kSteps;
   constexpr int kSc = C::kScores;
@@ -828,16 +828,17 @@ hipError_t device_cu_count(int* n_cu) {
 bool fwd_mfma_supported(int d_h, int T) {
   // Buffer descriptors address one head with 31-bit byte offsets, including
   // the rows past T of the last query tile.
-  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kBM) * d_h * 2 < 0x7fffffffLL;
+  return (d_h == 32 || d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && ((long long)T + kBM) * d_h * 2 < 0x7fffffffLL;
 }
 
 bool fwd_mfma_rope_fusable(int d_h, int rope) {
-  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && (rope == 1 || (rope == 2 && d_h % 32 == 0));
+  return (d_h == 32 || d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && (rope == 1 || (rope == 2 && d_h % 32 == 0));
 }
 
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a, const HeadParams& hp, hipStream_t s, const RopeParams* rp) {
   if (rp != nullptr && !fwd_mfma_rope_fusable(a.d_h, rp->rope)) return hipErrorInvalidValue;
   switch (a.d_h) {
+    case 32: return launch_typed<64, 32>(a, hp, s, rp);
     case 48: return launch_typed<64, 48>(a, hp, s, rp);
     case 64: return launch_typed<64, 64>(a, hp, s, rp);
     case 80: return launch_typed<128, 80>(a, hp, s, rp);

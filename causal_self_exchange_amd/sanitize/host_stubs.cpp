@@ -18,7 +18,7 @@ hipError_t launch_bwd_mfma_bf16(const BwdArgs&, const HeadParams&, hipStream_t) 
 hipError_t launch_bwd_reduce(const BwdArgs&, hipStream_t) { return hipErrorLaunchFailure; }
 bool bwd_mfma_supported(int, int) { return false; }
 bool bwd_du_supported(int d_h, int T) {
-  return (d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && bwd_du_head_bytes(T) < 0x7fff0000LL;
+  return (d_h == 32 || d_h == 48 || d_h == 64 || d_h == 80 || d_h == 128) && bwd_du_head_bytes(T) < 0x7fff0000LL;
 }
 hipError_t launch_prestep(const PrestepArgs&, const PrestepParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_linear(const LinArgs&, const HeadParams&, bool, hipStream_t) { return hipErrorLaunchFailure; }

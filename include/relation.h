@@ -141,7 +141,7 @@ size_t relation_bwd_workspace_bytes(int B, int H, int T, int d_h);
 
 /*
  * relation_bwd_stored_workspace_bytes - bytes of device workspace with which
- * relation_bwd (dtype REL_BF16, d_h in {48, 64, 80, 128}) stores dU once
+ * relation_bwd (dtype REL_BF16, d_h in {32, 48, 64, 80, 128}) stores dU once
  * instead of recomputing the evidence for dP1: the statistics and partials
  * of relation_bwd_workspace_bytes plus dU in bf16 for every strictly causal
  * (query, key) pair, in blocks of 32 queries x 16 keys (about B H T^2 bytes;
@@ -179,7 +179,7 @@ size_t relation_bwd_stored_workspace_bytes(int B, int H, int T, int d_h);
  * Every output is overwritten (not accumulated into). The result is
  * deterministic: no atomics, scalar sums in a fixed order (fp64 across rows
  * chunks, heads and batch).
- * Numerics: REL_BF16 with d_h in {48, 64, 80, 128} recomputes both evidence
+ * Numerics: REL_BF16 with d_h in {32, 48, 64, 80, 128} recomputes both evidence
  * products on bf16 MFMA and rounds F and dU to bf16 as operands of the
  * gradient products (fp32 accumulation); other cases compute in fp32
  * throughout.
@@ -237,7 +237,7 @@ size_t relation_fwd_model_workspace_bytes(int B, int H, int T, int d_h,
  * the workspace. The workspace has three 256-byte aligned slots (rotated P1,
  * rotated P2, mixed I, in that order); after the call the last two hold the
  * pre-stepped P2 and I. Where the bf16 MFMA forward rotates P1 itself as it
- * loads each query tile (REL_BF16, d_h in {48, 64, 80, 128}, interleaved
+ * loads each query tile (REL_BF16, d_h in {32, 48, 64, 80, 128}, interleaved
  * pairs, or half-split pairs with d_h a multiple of 32) the first slot is
  * not written, and the result equals pre-step then forward bit for bit;
  * otherwise the first slot holds the rotated P1. A backward on the rotated

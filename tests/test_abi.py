@@ -216,11 +216,11 @@ def test_bwd_stored_workspace_bytes():
         nqp = (T + 31) // 32
         du = B * H * nqp * (nqp + 1) * 1024
         return lib.relation_bwd_workspace_bytes(B, H, T, D) + ((du + 255) // 256) * 256
-    for B, H, T, D in ((1, 32, 8192, 128), (2, 3, 1, 64), (4, 16, 2049, 64), (1, 2, 300, 48), (1, 1, 77, 80)):
+    for B, H, T, D in ((1, 32, 8192, 128), (2, 3, 1, 64), (4, 16, 2049, 64), (1, 2, 300, 48), (1, 1, 77, 80),
+                       (2, 2, 100, 32)):
         assert lib.relation_bwd_stored_workspace_bytes(B, H, T, D) == want(B, H, T, D)
     assert lib.relation_bwd_stored_workspace_bytes(1, 32, 8192, 128) == 2_155_872_256 + \
         lib.relation_bwd_workspace_bytes(1, 32, 8192, 128)
-    assert lib.relation_bwd_stored_workspace_bytes(1, 1, 10, 32) == 0        # no MFMA backward at d_h = 32
     assert lib.relation_bwd_stored_workspace_bytes(1, 1, 10, 96) == 0
     assert lib.relation_bwd_stored_workspace_bytes(0, 1, 10, 64) == 0
     assert lib.relation_bwd_stored_workspace_bytes(1, 1, 46304, 64) > 0     # largest length with 31-bit offsets

@@ -124,11 +124,11 @@ def _check_bars(ref, L, g, what, bars):
 
 
 SHAPES = [
-    # B, H, T, d_h, dtype  (bf16 d_h 64/128: MFMA kernels; the rest: row-scan kernels)
+    # B, H, T, d_h, dtype  (bf16: MFMA kernels; fp32: row-scan kernels)
     (1, 1, 1, 64, "bf16"), (1, 2, 2, 128, "bf16"), (1, 1, 65, 128, "bf16"), (2, 3, 100, 64, "bf16"),
     (1, 2, 129, 128, "bf16"), (3, 1, 191, 64, "bf16"), (1, 2, 300, 128, "bf16"), (1, 1, 513, 128, "bf16"),
     (2, 2, 100, 32, "bf16"), (1, 2, 77, 32, "f32"), (1, 1, 64, 64, "f32"), (1, 1, 150, 128, "f32"),
-    (1, 1, 1, 32, "f32"),
+    (1, 1, 1, 32, "f32"), (1, 3, 333, 32, "bf16"), (1, 1, 1, 32, "bf16"),
     # the paper's head sizes: MFMA kernels on the 64 / 128 layouts (bf16), row-scan kernels (fp32)
     (2, 4, 300, 48, "bf16"), (1, 2, 257, 80, "bf16"), (1, 1, 1, 48, "bf16"), (1, 2, 130, 48, "f32"),
     (1, 1, 99, 80, "f32"),
@@ -145,7 +145,7 @@ def test_bwd_ragged_shapes(shape, lam):
     _check(inp, lam, dt, Y, L, g, f"{shape} lam={lam}")
 
 
-MFMA_SHAPES = [s for s in SHAPES if s[4] == "bf16" and s[3] in (48, 64, 80, 128)]
+MFMA_SHAPES = [s for s in SHAPES if s[4] == "bf16" and s[3] in (32, 48, 64, 80, 128)]
 
 
 @pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -165,6 +165,7 @@ SHAPES = [
     (2, 3, 100, 64, "bf16"), (1, 2, 129, 128, "bf16"), (1, 1, 1000, 128, "bf16"),
     (2, 2, 257, 32, "bf16"), (1, 2, 333, 128, "f32"), (1, 1, 64, 64, "f32"),
     (3, 1, 191, 64, "bf16"), (1, 1, 513, 128, "bf16"), (1, 2, 77, 32, "f32"),
+    (1, 3, 700, 32, "bf16"), (1, 1, 1, 32, "bf16"),
 ]
 
 
@@ -391,11 +392,11 @@ def test_autoregressive_decode_matches_forward(dt, D):
     assert lens.cpu().tolist() == [T] * B
 
 
-# ------------------------------------------ the paper's head sizes 48, 80 ----
+# ---------------------------- padded head sizes: the paper's 48, 80, and 32 ----
 
 PAPER_SHAPES = [
     (2, 8, 300, 48, "bf16"), (1, 8, 513, 80, "bf16"), (1, 2, 129, 48, "f32"), (1, 2, 100, 80, "f32"),
-    (1, 1, 1, 48, "bf16"), (1, 3, 257, 80, "bf16"),
+    (1, 1, 1, 48, "bf16"), (1, 3, 257, 80, "bf16"), (2, 2, 520, 32, "bf16"),
 ]
 
 
@@ -403,9 +404,9 @@ PAPER_SHAPES = [
 @pytest.mark.parametrize("lam", [0.0, 0.5])
 @pytest.mark.parametrize("shape", PAPER_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_paper_head_sizes(shape, lam, kernel):
-    """d_h = 48 and 80 ([paper] Table 6 geometries): bf16 runs the MFMA kernel
-    on the 64 / 128 tile layouts with zero-filled padding chunks; the
-    row-scan kernel is checked too. LSE from the training forward as well."""
+    """d_h = 48 and 80 ([paper] Table 6 geometries) and 32: bf16 runs the
+    MFMA kernel on the 64 / 128 tile layouts with zero-filled padding chunks;
+    the row-scan kernel is checked too. LSE from the training forward as well."""
     B, H, T, D, dt = shape
     cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0), lam=lam)
     inp = W.make_fwd_inputs(cfg, 31 + T)

@@ -111,13 +111,13 @@ def test_prestep_without_angles_copies_information_and_allows_odd_heads():
 def _fused(D, dt, mode):
     """Whether the bf16 MFMA forward rotates P1 itself (relation_fwd_model):
     interleaved pairs at every head size, half-split pairs when d_h % 32 == 0."""
-    return dt == "bf16" and D in (48, 64, 80, 128) and (mode == "interleaved" or D % 32 == 0)
+    return dt == "bf16" and D in (32, 48, 64, 80, 128) and (mode == "interleaved" or D % 32 == 0)
 
 
 @pytest.mark.parametrize("with_lse", [True, False])
 @pytest.mark.parametrize("mode,pairing", [("interleaved", "A"), ("half", "B")])
 @pytest.mark.parametrize("case", [(2, 4, 300, 64, "bf16"), (1, 8, 513, 128, "bf16"), (1, 2, 128, 32, "f32"),
-                                  (1, 4, 200, 80, "bf16"), (2, 2, 150, 48, "bf16")],
+                                  (1, 4, 200, 80, "bf16"), (2, 2, 150, 48, "bf16"), (1, 4, 270, 32, "bf16")],
                          ids=lambda c: "x".join(map(str, c)))
 def test_model_forward_matches_oracle(case, mode, pairing, with_lse):
     B, H, T, D, dt = case
