@@ -13,7 +13,10 @@
 // Every exponent above is <= 0, so any retention in (0, 1] is safe.
 // Three kernels: chunk (the bracketed sum and e^{b_last} per chunk), scan
 // (the elementwise recurrence over chunks, one thread per state element),
-// output (Y per chunk). Arithmetic is fp32 throughout.
+// output (Y per chunk). Arithmetic is fp32 throughout; with bf16 inputs the
+// two large products (the chunk contributions K^T I and the output's at I and
+// Qt Cin) run on bf16 MFMA with every fp32 operand split into a bf16 pair
+// (I itself is exact in bf16), which carries it to about 2^-17 relative.
 #include "rel_internal.h"
 #include "rel_device.h"
 
@@ -34,6 +37,36 @@ constexpr float kFactorBound = 40.0f;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+// x = hi + lo + O(2^-17 |x|): hi is x rounded to bf16 (nearest even), lo the
+// exact fp32 remainder x - hi rounded to bf16. A product of two split operands
+// is taken as hi hi + hi lo + lo hi (the dropped lo lo is below 2^-16 of it),
+// on bf16 MFMA with fp32 accumulation.
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8v& hi, bf16x8v& lo) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    hi[u] = (__bf16)x[u];
+    lo[u] = (__bf16)(x[u] - (float)hi[u]);
+  }
+}
+
+// bf16 operand tiles in LDS: row `row` of 8-element (16-byte) chunks, the
+// chunk index XOR-swizzled with a function of the row so that the MFMA
+// operand reads (32 rows, one chunk each) spread over the banks. Rows of 8
+// chunks (64 elements) and of 16 chunks (128 elements).
+__device__ __forceinline__ int sw8(int row, int c) { return row * 128 + 16 * (c ^ ((row >> 1) & 7)); }
+__device__ __forceinline__ int sw16(int row, int c) { return row * 256 + 16 * (c ^ (row & 15)); }
+// Rows of D elements (D / 8 chunks).
+template <int D>
+__device__ __forceinline__ int swd(int row, int c) {
+  if constexpr (D == 128) return sw16(row, c);
+  else if constexpr (D == 64) return sw8(row, c);
+  else return row * 64 + 16 * (c ^ ((row >> 2) & 3));
+}
+__device__ __forceinline__ bf16x8v lds_bf16x8(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8v*>(base + off);
+}
 
 template <typename Tin>
 __device__ __forceinline__ float ld_val(const Tin* p, size_t i) { return to_f32(p[i]); }
@@ -84,6 +117,20 @@ struct Staged {
         if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u];
         else dst[t * ld + r0 + u] = x[u];
       }
+    }
+  }
+  // bf16 rows (exact) into a channel-major bf16 tile: element (t, r) at
+  // sw8(r, t / 8) + 2 (t % 8), i.e. the tokens of a channel contiguous.
+  __device__ __forceinline__ void store_bf16_cm(char* dst, int tid) const {
+    static_assert(sizeof(Tin) == 2 && kL == 64, "bf16 rows of a 64-token chunk");
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = tid + i * NT, e = idx * kVec;
+      if (idx >= kTot) break;
+      const int t = e / D, r0 = e % D;
+      const bf16x8v b = __builtin_bit_cast(bf16x8v, v[i]);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) *reinterpret_cast<__bf16*>(dst + sw8(r0 + u, t >> 3) + 2 * (t & 7)) = b[u];
     }
   }
 };
@@ -185,12 +232,13 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
 
 // Phase 1: per (b*H + h, chunk): dC = sum_j S_j (k_j o e^{b_last - b_j}) I_j^T
 // and g = e^{b_last}, into the state slot of the chunk. dC = Kt^T I is a
-// d_h x d_h x 64 product on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 out): a
-// wave owns column block n and all row blocks (independent accumulators that
-// share the I operand, which comes straight from global memory into
-// registers). P1 is only needed for the row statistics, which come from the
-// staged registers; LDS holds Kt and the decay prefix, 66 KB at d_h = 128, so
-// two work-groups fit per CU.
+// d_h x d_h x 64 product: on v_mfma_f32_32x32x2_f32 for fp32 inputs, on
+// v_mfma_f32_32x32x16_bf16 over Kt's split bf16 pair for bf16 inputs. A wave
+// owns column block n and all row blocks (independent accumulators that share
+// the I operand, which comes straight from global memory into registers). P1
+// is only needed for the row statistics, which come from the staged
+// registers; LDS holds Kt (then its split tiles) and the decay prefix, 66 KB
+// at d_h = 128, so two work-groups fit per CU.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kChunkThreads;
@@ -209,20 +257,34 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   constexpr int kT = D / 32;
   constexpr int kNPerWave = (kT + 3) / 4;            // column blocks per wave (ceil)
+  constexpr bool kSplit = sizeof(Tin) == 2;          // bf16 MFMA on split operands
 
-  // I operands (B[j][col] = I_j[col], j = 2 ks + lh) of this wave's column
-  // blocks: issued first, consumed last. Rows past the chunk's end read the
-  // last row (an address inside the tensor) and are zeroed afterwards, so
-  // no load sits behind a per-lane branch.
-  float bf[kNPerWave][kL / 2];
+  // I operands of this wave's column blocks, issued first and consumed last:
+  // fp32, B[j][col] = I_j[col] with j = 2 ks + lh; bf16, 8 rows j = 16 kk +
+  // 8 lh + e per k-step. Rows past the chunk's end read the last row (an
+  // address inside the tensor) and are zeroed afterwards, so no load sits
+  // behind a per-lane branch.
+  float bf[kSplit ? 1 : kNPerWave][kSplit ? 1 : kL / 2];
+  bf16x8v bi[kSplit ? kNPerWave : 1][kL / 16];
 #pragma unroll
   for (int q = 0; q < kNPerWave; ++q) {
     const int n = wave + 4 * q;
     if (n >= kT) break;
+    if constexpr (kSplit) {
 #pragma unroll
-    for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
+      for (int kk = 0; kk < kL / 16; ++kk)
 #pragma unroll
-    for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
+        for (int e = 0; e < 8; ++e) bi[q][kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
+#pragma unroll
+      for (int kk = 0; kk < kL / 16; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bi[q][kk][e] = 16 * kk + 8 * lh + e < rows ? bi[q][kk][e] : (__bf16)0.0f;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
+#pragma unroll
+      for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
+    }
   }
   {
     Staged<NT, Tin, D> g1, g2;
@@ -237,9 +299,39 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   __syncthreads();
   decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
   __syncthreads();
-  for (int e = threadIdx.x; e < kL * D; e += NT) {
-    const int t = e / D, r = e % D;
-    kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+  // Kt_j = S_j k_j o e^{b_last - b_j} (rows past the chunk's end: 0). The
+  // bf16 path splits it into two channel-major bf16 tiles (channel r, tokens
+  // contiguous) that take kt's place once every thread has read its values.
+  char* const kh = reinterpret_cast<char*>(&kt[0][0]);
+  char* const kl = kh + D * 128;
+  if constexpr (kSplit) {
+    constexpr int kG = (kL * D / 8 + NT - 1) / NT;   // 8-token groups per thread
+    float x[kG][8];
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
+      if (idx >= kL * D / 8) break;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = 8 * cc + u;
+        x[k][u] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
+      if (idx >= kL * D / 8) break;
+      bf16x8v hi, lo;
+      split_bf16(x[k], hi, lo);
+      *reinterpret_cast<bf16x8v*>(kh + sw8(r, cc)) = hi;
+      *reinterpret_cast<bf16x8v*>(kl + sw8(r, cc)) = lo;
+    }
+  } else {
+    for (int e = threadIdx.x; e < kL * D; e += NT) {
+      const int t = e / D, r = e % D;
+      kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+    }
   }
   __syncthreads();
   float* dC = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
@@ -250,16 +342,36 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
     f32x16 acc[kT];
 #pragma unroll
     for (int m = 0; m < kT; ++m) acc[m] = f32x16{};
-    struct Op { float a[kT]; };
-    pipelined<kL / 2, 4, Op>(
-        [&](int ks, Op& o) {
+    if constexpr (kSplit) {
+      // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per k-step.
+      struct Op { bf16x8v h[kT], l[kT]; };
+      pipelined<kL / 16, 2, Op>(
+          [&](int kk, Op& o) {
 #pragma unroll
-          for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
-        },
-        [&](int ks, const Op& o) {
+            for (int m = 0; m < kT; ++m) {
+              o.h[m] = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
+              o.l[m] = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
+            }
+          },
+          [&](int kk, const Op& o) {
 #pragma unroll
-          for (int m = 0; m < kT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[m], 0, 0, 0);
-        });
+            for (int m = 0; m < kT; ++m) {
+              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h[m], bi[q][kk], acc[m], 0, 0, 0);
+              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l[m], bi[q][kk], acc[m], 0, 0, 0);
+            }
+          });
+    } else {
+      struct Op { float a[kT]; };
+      pipelined<kL / 2, 4, Op>(
+          [&](int ks, Op& o) {
+#pragma unroll
+            for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
+          },
+          [&](int ks, const Op& o) {
+#pragma unroll
+            for (int m = 0; m < kT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[m], 0, 0, 0);
+          });
+    }
 #pragma unroll
     for (int m = 0; m < kT; ++m)
 #pragma unroll
@@ -319,10 +431,13 @@ __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
 // diagonal R is the block's middle row, which keeps every exponent within
 // +-40 unless the retention falls by more than e^-40 within 8 tokens on some
 // channel; such a block takes the exact per-element exponentials instead.
-// The output is one v_mfma_f32_32x32x2_f32 accumulation over j (at I) and r
-// (Qt Cin) per 32 x 32 tile, one tile per wave, with its column of Cin in
-// registers. LDS arrays are stored channel-major ([r][t], rows padded to 65
-// floats) so that the operand reads and transposing writes are conflict-free.
+// The output is one accumulation over j (at I) and r (Qt Cin) per 32 x 32
+// tile, one tile per wave, with its column of Cin in registers: on
+// v_mfma_f32_32x32x2_f32 for fp32 inputs; for bf16 inputs on
+// v_mfma_f32_32x32x16_bf16 with at, Qt and Cin split into bf16 pairs (I is
+// exact), from XOR-swizzled bf16 tiles. The fp32 LDS arrays are stored
+// channel-major ([r][t], rows padded to 65 floats) so that the operand reads
+// and transposing writes are conflict-free.
 // Persistent: a work-group takes chunks blockIdx.x + k gridDim.x, and the
 // next chunk's rows are loaded into registers while the current one is
 // computed (its Cin column, needed last, is loaded at the iteration's start).
@@ -344,6 +459,27 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t] (the prefix's scratch before)
   __shared__ float s[kL], n1[kL], n2[kL];
   static_assert(kL * kP >= NT, "prefix scratch fits in atT");
+  // bf16 inputs: I is kept as a channel-major bf16 tile in it's place, at as
+  // split bf16 tiles (token-major) in atT's, and Qt as split bf16 tiles
+  // (token-major) in kT's once the sub-block tasks are done with it.
+  constexpr bool kSplit = sizeof(Tin) == 2;
+  char* const itb = reinterpret_cast<char*>(&it[0][0]);
+  char* const ath = reinterpret_cast<char*>(&atT[0][0]);
+  char* const atl = ath + kL * 128;
+  char* const qth = reinterpret_cast<char*>(&kT[0][0]);
+  char* const qtl = qth + kL * 2 * D;
+  static_assert(2 * kL * 128 <= (int)sizeof(atT) && 4 * kL * D <= (int)sizeof(kT), "split tiles fit");
+  // at[t][j] into its tile(s).
+  auto put_at = [&](int t, int j, float v) __attribute__((always_inline)) {
+    if constexpr (kSplit) {
+      const __bf16 hi = (__bf16)v;
+      const int off = sw8(t, j >> 3) + 2 * (j & 7);
+      *reinterpret_cast<__bf16*>(ath + off) = hi;
+      *reinterpret_cast<__bf16*>(atl + off) = (__bf16)(v - (float)hi);
+    } else {
+      atT[j][t] = v;
+    }
+  };
   const int nc = (a.T + kL - 1) / kL;
   const int total = a.B * a.H * nc;
   constexpr int kTN = D / 32;
@@ -382,13 +518,18 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     staged_row_stats(nx.p1, nx.p2, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
     nx.p1.template store<true>(&qT[0][0], kP, tid);
     nx.p2.template store<true>(&kT[0][0], kP, tid);
-    nx.in.template store<false>(&it[0][0], D, tid);
+    if constexpr (kSplit) nx.in.store_bf16_cm(itb, tid);
+    else nx.in.template store<false>(&it[0][0], D, tid);
     nx.al.template store<true>(&bT[0][0], kP, tid);
     float cf[D / 2];
     if (has_tile) {
       const float* cin = a.state + (size_t)g * D * D;
+      // fp32: B[r][col] with r = 2 ks + lh; bf16: rows r = 16 kk + 8 lh + e at cf[8 kk + e].
 #pragma unroll
-      for (int ks = 0; ks < D / 2; ++ks) cf[ks] = cin[(size_t)(2 * ks + lh) * D + 32 * n_out + l32];
+      for (int ks = 0; ks < D / 2; ++ks) {
+        const int r = kSplit ? 16 * (ks / 8) + 8 * lh + ks % 8 : 2 * ks + lh;
+        cf[ks] = cin[(size_t)r * D + 32 * n_out + l32];
+      }
     }
     if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
     __syncthreads();
@@ -443,8 +584,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
           // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16; on the
           // diagonal only j < t is history.
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            atT[16 * jb + l16][16 * tb + 4 * lq + i] = (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f;
+          for (int i = 0; i < 4; ++i) put_at(16 * tb + 4 * lq + i, 16 * jb + l16, (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f);
         } else {
           for (int e = lane; e < 256; e += 64) {
             const int tl = e >> 4, jl = e & 15;
@@ -453,7 +593,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
             if (jl < tl) {
               for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
             }
-            atT[j][t] = acc;
+            put_at(t, j, acc);
           }
         }
       }
@@ -463,13 +603,27 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
       constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
       constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
       const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
-      atT[16 * kUpJ[p] + jl][16 * kUpT[p] + tl] = 0.0f;
+      put_at(16 * kUpT[p] + tl, 16 * kUpJ[p] + jl, 0.0f);
     }
     __syncthreads();
-    // Qt = S q o e^{b} in place (every exponent <= 0).
-    for (int e = tid; e < kL * D; e += NT) {
-      const int r = e / kL, t = e % kL;
-      qT[r][t] *= __expf(bT[r][t]);
+    // Qt = S q o e^{b} (every exponent <= 0): in place, or split into
+    // token-major bf16 tiles (kT is no longer read).
+    if constexpr (kSplit) {
+      for (int e = tid; e < kL * D / 8; e += NT) {
+        const int t = e % kL, cc = e / kL;
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = qT[8 * cc + u][t] * __expf(bT[8 * cc + u][t]);
+        bf16x8v hi, lo;
+        split_bf16(x, hi, lo);
+        *reinterpret_cast<bf16x8v*>(qth + swd<D>(t, cc)) = hi;
+        *reinterpret_cast<bf16x8v*>(qtl + swd<D>(t, cc)) = lo;
+      }
+    } else {
+      for (int e = tid; e < kL * D; e += NT) {
+        const int r = e / kL, t = e % kL;
+        qT[r][t] *= __expf(bT[r][t]);
+      }
     }
     __syncthreads();
 
@@ -477,19 +631,54 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     if (has_tile) {
       const int col = 32 * n_out + l32, t = 32 * m_out + l32;
       f32x16 acc = {};
-      struct Op2 { float a, b; };
-      pipelined<kL / 2, 8, Op2>(
-          [&](int ks, Op2& o) {
-            o.a = atT[2 * ks + lh][t];
-            o.b = it[2 * ks + lh][col];
-          },
-          [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
-      pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
-                                 [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
+      if constexpr (kSplit) {
+        // at I: A = at (hi, lo), B = I (exact); Qt Cin: A = Qt (hi, lo), B = Cin
+        // (hi, lo, split here); 16 tokens or channels per k-step.
+        struct OpA { bf16x8v h, l, b; };
+        pipelined<kL / 16, 2, OpA>(
+            [&](int kk, OpA& o) {
+              o.h = lds_bf16x8(ath, sw8(t, 2 * kk + lh));
+              o.l = lds_bf16x8(atl, sw8(t, 2 * kk + lh));
+              o.b = lds_bf16x8(itb, sw8(col, 2 * kk + lh));
+            },
+            [&](int kk, const OpA& o) {
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, o.b, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, o.b, acc, 0, 0, 0);
+            });
+        struct OpQ { bf16x8v h, l; };
+        pipelined<D / 16, 2, OpQ>(
+            [&](int kk, OpQ& o) {
+              o.h = lds_bf16x8(qth, swd<D>(t, 2 * kk + lh));
+              o.l = lds_bf16x8(qtl, swd<D>(t, 2 * kk + lh));
+            },
+            [&](int kk, const OpQ& o) {
+              float x[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = cf[8 * kk + e];
+              bf16x8v ch, cl;
+              split_bf16(x, ch, cl);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, ch, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, cl, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, ch, acc, 0, 0, 0);
+            });
+      } else {
+        struct Op2 { float a, b; };
+        pipelined<kL / 2, 8, Op2>(
+            [&](int ks, Op2& o) {
+              o.a = atT[2 * ks + lh][t];
+              o.b = it[2 * ks + lh][col];
+            },
+            [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
+        pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
+                                   [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tr = 32 * m_out + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(it[tr][col] + acc[r]);
+        float iv;
+        if constexpr (kSplit) iv = (float)*reinterpret_cast<const __bf16*>(itb + sw8(col, tr >> 3) + 2 * (tr & 7));
+        else iv = it[tr][col];
+        if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(iv + acc[r]);
       }
     }
     __syncthreads();

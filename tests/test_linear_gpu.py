@@ -2,9 +2,11 @@
 the C ABI) against the fp64 recurrence of the oracle on the same seeded
 inputs.
 
-Tolerances: the kernels compute in fp32 from the stored inputs, so the final
-state C_T (fp32 output) meets max |C - C*| <= 1e-5 * max(1, max |C*|) for
-either input dtype. Y: fp32 per row ||Y_t - Y*_t||_inf <= 1e-5 * ||Y*_t||_inf
+Tolerances: the final state C_T (fp32 output) meets max |C - C*| <= 1e-5 *
+max(1, max |C*|) for either input dtype. fp32 inputs run on fp32 MFMA; bf16
+inputs take the chunk products on bf16 MFMA with the fp32 factor split into
+a bf16 pair (at most 2^-18 relative per product, I being exact), which puts
+the state error at 2-3e-6 on these shapes against 2-4e-7 for fp32. Y: fp32 per row ||Y_t - Y*_t||_inf <= 1e-5 * ||Y*_t||_inf
 (the forward's bar); bf16 per row ||Y_t - Y*_t||_inf <= 2e-2 * max(1,
 ||Y*_t||_inf) (the forward's absolute bar, relative once the history makes a
 row exceed 1: Y_t = I_t + E_t is not bounded by the inputs here, and bf16
@@ -47,11 +49,12 @@ def _check(inp, Y, st, dt, what):
     else:
         err = float(np.max(num / np.maximum(1.0, mx)))
         assert err <= 2e-2, (what, err)
+    serr = float("nan")
     if st is not None:
         c = f64(st)
         serr = float(np.max(np.abs(c - C)) / max(1.0, float(np.max(np.abs(C)))))
         assert serr <= 1e-5, (what, "state", serr)
-    print(f"\n{what}: Y err {err:.2e}", flush=True)
+    print(f"\n{what}: Y err {err:.2e}, state err {serr:.2e}", flush=True)
 
 
 SHAPES = [
