@@ -288,6 +288,33 @@ def relation_head_bwd_sampled(p1, p2, v, tau, lam, dy, rows, cols, block=256):
     return dict(dP1=dP1, dV=dV, dP2=dP2, dtau=dtau, lse=lse, Y=Y, F_self=F_self, S=S, U_self=diag_u)
 
 
+def relation_head_dp1_rows(p1, p2, v, tau, lam, dy, rows):
+    """dP1 at query rows `rows` of one head, each row on its own: row i's
+    relation logits, flow F_i, output Y_i and D_i = dY_i . Y_i need only
+    p1[i], p2[:i+1], v[:i+1] and dy[i], so each row costs O(i d_h) at any T.
+    The chain rule is the one of ``relation_head_bwd`` restricted to row i:
+    dR_ij = F_ij (dY_i . V_j - D_i), dU_ij = dR_ij SiLU'(U_ij) below the
+    diagonal and dR_ii S_i (1 - S_i) / tau on it, dP1_i = sum_j dU_ij p2_j / sqrt(d_h)."""
+    p1, p2, v, dy = (np.asarray(x, dtype=np.float64) for x in (p1, p2, v, dy))
+    d_h = p1.shape[-1]
+    c = 1.0 / math.sqrt(d_h)
+    tau = float(tau)
+    out = np.empty((len(rows), d_h))
+    for n, i in enumerate(rows):
+        u = (p2[: i + 1] @ p1[i]) * c
+        s = sigmoid(np.array([u[i] / tau]))[0]
+        R = silu(u) - lam * math.log(i + 1)
+        R[i] = s
+        W = np.exp(R - R.max())
+        F = W / W.sum()
+        y = F @ v[: i + 1]
+        dR = F * (v[: i + 1] @ dy[i] - float(dy[i] @ y))
+        dU = dR * silu_grad(u)
+        dU[i] = dR[i] * s * (1.0 - s) / tau
+        out[n] = (dU @ p2[: i + 1]) * c
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Cross-check routes (pins for the definition above; never used by the kernels)
 # ---------------------------------------------------------------------------

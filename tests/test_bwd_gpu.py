@@ -178,6 +178,34 @@ def test_bwd_stored_path_uses_the_stored_workspace():
         assert bool((tail != 0x7F).any()) == touched
 
 
+def test_bwd_stored_path_at_its_longest_length():
+    """T = 46,304, the longest sequence the stored-dU path takes: one head's
+    dU blocks end just below 2^31 bytes, so the last query blocks use the
+    largest offsets a 32-bit buffer offset holds. Two heads, d_h = 64, bf16,
+    lambda = 0.5: dP1 on sampled rows (the last ones included) against the
+    oracle row by row, and all three gradient tensors against the recompute
+    path, which shares the key/value pass but forms dP1 without stored dU."""
+    B, H, T, D = 1, 2, 46304, 64
+    assert R.bwd_stored_workspace_bytes(B, H, T, D) > 0
+    cfg = W.FwdConfig("t", B, H, T, D, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_bwd_inputs(cfg, 46)
+    _, _, g = _gpu_train(inp, 0.5, store_du=True)
+    _, _, g2 = _gpu_train(inp, 0.5, store_du=False)
+    rng = np.random.default_rng(46)
+    rows = sorted(set([0, 1, 31, 32, 4095, T - 65, T - 64, T - 33, T - 32, T - 2, T - 1] +
+                      [int(x) for x in rng.integers(0, T, 8)]))
+    for h in range(H):
+        p1, p2, v, dy = (f64(inp[k])[0, h] for k in ("P1", "P2", "V", "dY"))
+        ref = O.relation_head_dp1_rows(p1, p2, v, float(inp["tau"][h]), 0.5, dy, rows)
+        err = row_err(f64(g[0])[0, h, rows], ref)
+        print(f"\nT={T} h={h}: dP1 sampled rows {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], (h, err)
+    for name, a, b in zip(("dP1", "dP2", "dV"), g[:3], g2[:3]):
+        e = row_err(f64(a), f64(b))
+        print(f"stored vs recompute {name}: {e:.2e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_bwd_config_full(name):
     """Tiny (fp32, row-scan kernels) and Small (bf16, MFMA kernels) in full."""

@@ -206,3 +206,16 @@ def test_sampled_gradients_equal_the_materialised_ones(lam):
     assert math.isclose(got["dtau"], full[3], rel_tol=1e-10, abs_tol=1e-12)
     np.testing.assert_allclose(got["lse"], O.row_lse(p1, p2, 0.8, lam), rtol=1e-12)
     np.testing.assert_allclose(got["Y"], O.relation_head(p1, p2, v, 0.8, lam), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+def test_dp1_rows_equal_the_materialised_ones(lam):
+    """The row-only dP1 route (for lengths where no T x T matrix or full
+    forward pass is affordable) agrees with the materialised backward on
+    every row, the first (Self only) and the last included."""
+    rng = np.random.default_rng(15)
+    T, d = 29, 6
+    p1, p2, v, dy = _head(rng, T, d, scale=1.3)
+    full = O.relation_head_bwd(p1, p2, v, 0.7, lam, dy)
+    got = O.relation_head_dp1_rows(p1, p2, v, 0.7, lam, dy, list(range(T)))
+    np.testing.assert_allclose(got, full[0], rtol=1e-10, atol=1e-12)
