@@ -238,7 +238,8 @@ def bench_linear(torch, R, W, steps, warmup):
     state_bytes = float(cfg.B * cfg.H * ((cfg.T + L - 1) // L)) * d * d * 4 * 4   # chunk states: write, scan r/w, read
     return {"workload": "linear relation: B=1 H=32 T=8192 d_h=128 bf16, seeded retention, 64-token chunks",
             "us_per_call": round(ms * 1e3, 2), "tokens/s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
-            "TFLOP/s_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
+            "TFLOP/s_counted": round(flops / (ms * 1e-3) / 1e12, 2),
+            "arithmetic": "fp32 accumulation; chunk products on bf16 MFMA over split bf16 operand pairs",
             "GB/s_io_plus_states": round((io_bytes + state_bytes) / (ms * 1e-3) / 1e9, 1),
             "flops_counted": flops, "io_bytes": io_bytes, "state_bytes": state_bytes}
 
