@@ -542,29 +542,62 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     __syncthreads();
 
-    // Sub-block tasks: 6 pairs below the diagonal, then the 4 diagonal blocks.
+    // Sub-block tasks on the 8 waves. The pairs below the diagonal (tb, jb),
+    // tb > jb, factor through R = 16 jb + 15: waves 0 and 1 take two pairs
+    // that share jb, (1,0) + (2,0) and (2,1) + (3,1), with one key-side
+    // operand and two accumulators; waves 2-5 take the diagonal blocks; waves
+    // 6 and 7 the pairs (3,0) and (3,2).
+    static_assert(kW == 8, "the task assignment is for 8 waves");
     {
-      constexpr int kPairT[6] = {1, 2, 3, 2, 3, 3};
-      constexpr int kPairJ[6] = {0, 0, 0, 1, 1, 2};
       const int l16 = lane & 15, lq = lane >> 4;
-      for (int p = wave; p < 10; p += kW) {
-        const bool diag = p >= 6;
-        const int tb = diag ? p - 6 : kPairT[p];
-        const int jb = diag ? p - 6 : kPairJ[p];
-        const int R = diag ? 16 * tb + 7 : 16 * jb + 15;
-        bool factor = true;
-        if (diag) {
-          // b is non-increasing in t, so the extreme exponents are those of
-          // the block's first and last rows.
-          int ok = 1;
-          for (int r = lane; r < D; r += 64) {
-            const float br = bT[r][R];
-            ok &= (bT[r][16 * tb] - br <= kFactorBound) & (br - bT[r][16 * tb + 15] <= kFactorBound);
-          }
-          factor = __all(ok);
+      auto pairs = [&](auto nt, int tb0, int tb1, int jb) __attribute__((always_inline)) {
+        constexpr int N = decltype(nt)::value;
+        const int R = 16 * jb + 15, j = 16 * jb + l16;
+        const int tq[2] = {16 * tb0 + l16, 16 * tb1 + l16};
+        f32x4 acc[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[n] = f32x4{};
+        struct OpP { float ref, k, bk, q[N], bq[N]; };
+        pipelined<D / 4, 8 / N, OpP>(
+            [&](int ks, OpP& o) {
+              const int r = 4 * ks + lq;
+              o.ref = bT[r][R];
+              o.k = kT[r][j];
+              o.bk = bT[r][j];
+#pragma unroll
+              for (int n = 0; n < N; ++n) {
+                o.q[n] = qT[r][tq[n]];
+                o.bq[n] = bT[r][tq[n]];
+              }
+            },
+            [&](int ks, const OpP& o) {
+              const float bv = o.k * __expf(o.ref - o.bk);
+#pragma unroll
+              for (int n = 0; n < N; ++n)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.q[n] * __expf(o.bq[n] - o.ref), bv, acc[n], 0, 0, 0);
+            });
+        // acc[n][i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16.
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) put_at(16 * (n ? tb1 : tb0) + 4 * lq + i, 16 * jb + l16, acc[n][i]);
+      };
+      if (wave < 2) {
+        pairs(std::integral_constant<int, 2>{}, wave + 1, wave + 2, wave);
+      } else if (wave >= 6) {
+        pairs(std::integral_constant<int, 1>{}, 3, 3, wave == 6 ? 0 : 2);
+      } else {
+        const int tb = wave - 2;
+        const int R = 16 * tb + 7;
+        // b is non-increasing in t, so the extreme exponents are those of
+        // the block's first and last rows.
+        int ok = 1;
+        for (int r = lane; r < D; r += 64) {
+          const float br = bT[r][R];
+          ok &= (bT[r][16 * tb] - br <= kFactorBound) & (br - bT[r][16 * tb + 15] <= kFactorBound);
         }
-        if (factor) {
-          const int t = 16 * tb + l16, j = 16 * jb + l16;
+        if (__all(ok)) {
+          const int t = 16 * tb + l16, j = 16 * tb + l16;
           f32x4 acc = {};
           struct OpAt { float ref, q, bq, k, bk; };
           pipelined<D / 4, 8, OpAt>(
@@ -581,10 +614,10 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 const float bv = o.k * __expf(o.ref - o.bk);
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
               });
-          // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16; on the
-          // diagonal only j < t is history.
+          // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 tb + l16; only
+          // j < t is history.
 #pragma unroll
-          for (int i = 0; i < 4; ++i) put_at(16 * tb + 4 * lq + i, 16 * jb + l16, (!diag || l16 < 4 * lq + i) ? acc[i] : 0.0f);
+          for (int i = 0; i < 4; ++i) put_at(16 * tb + 4 * lq + i, 16 * tb + l16, l16 < 4 * lq + i ? acc[i] : 0.0f);
         } else {
           for (int e = lane; e < 256; e += 64) {
             const int tl = e >> 4, jl = e & 15;
