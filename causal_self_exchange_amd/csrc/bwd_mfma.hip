@@ -115,7 +115,7 @@ template <bool B>
 using Tag = std::integral_constant<bool, B>;
 
 // D: head size of the tile layout (64 or 128); DR: the rows' real head size
-// (48 and 80 run on the 64 / 128 layouts with zero-filled pad chunks, as in
+// (32 and 48 run on the 64 layout, 80 on the 128 one, with zero-filled pad chunks, as in
 // the forward: exact evidence, zero pad rows of the transports, pad columns
 // not stored).
 template <int D, int DR = D>

@@ -211,9 +211,9 @@ struct StepKind {
 };
 
 // D: head size of the LDS tile layout and the MFMA schedule (64 or 128); DR:
-// the rows' real head size in memory (48 runs on the 64 layout and 80 on the
-// 128 layout, the chunks past DR held at zero, so evidence and transport are
-// exact and the padded output rows are not stored).
+// the rows' real head size in memory (32 and 48 run on the 64 layout and 80
+// on the 128 layout, the chunks past DR held at zero, so evidence and
+// transport are exact and the padded output rows are not stored).
 // kRope: P1 is rotated (rotary position encoding, interleaved or half-split
 // pairs) after each query tile's rows are loaded, as the pre-step would have
 // rotated it (same angles, fp32 rotation, one bf16 rounding).
