@@ -206,6 +206,28 @@ def test_bwd_stored_path_at_its_longest_length():
         assert e <= TOL["bf16"], (name, e)
 
 
+def test_bwd_head_size_32_long_sequence():
+    """d_h = 32 on the padded 64-wide MFMA layout at T = 16,384 (two heads,
+    stored-dU path): dP1 on sampled rows against the oracle row by row, and
+    all gradients against the recompute path."""
+    B, H, T, D = 1, 2, 16384, 32
+    cfg = W.FwdConfig("t", B, H, T, D, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_bwd_inputs(cfg, 33)
+    _, _, g = _gpu_train(inp, 0.5, store_du=True)
+    _, _, g2 = _gpu_train(inp, 0.5, store_du=False)
+    rng = np.random.default_rng(33)
+    rows = sorted(set([0, 1, 31, 32, 4095, T - 33, T - 32, T - 2, T - 1] + [int(x) for x in rng.integers(0, T, 8)]))
+    for h in range(H):
+        p1, p2, v, dy = (f64(inp[k])[0, h] for k in ("P1", "P2", "V", "dY"))
+        ref = O.relation_head_dp1_rows(p1, p2, v, float(inp["tau"][h]), 0.5, dy, rows)
+        err = row_err(f64(g[0])[0, h, rows], ref)
+        print(f"\nd_h=32 T={T} h={h}: dP1 sampled rows {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], (h, err)
+    for name, a, b in zip(("dP1", "dP2", "dV"), g[:3], g2[:3]):
+        e = row_err(f64(a), f64(b))
+        assert e <= TOL["bf16"], (name, e)
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_bwd_config_full(name):
     """Tiny (fp32, row-scan kernels) and Small (bf16, MFMA kernels) in full."""

@@ -420,6 +420,16 @@ def test_paper_head_sizes(shape, lam, kernel):
     assert float(np.max(np.abs(f64(L) - want))) <= 1e-4
 
 
+
+def test_head_size_32_long_sequence_sampled():
+    """d_h = 32 on the padded 64-wide MFMA layout at a long sequence (T =
+    16,384, two heads, lambda = 0.5): sampled rows of every head, the last
+    ones included, against the oracle row by row."""
+    cfg = W.FwdConfig("t", 1, 2, 16384, 32, "bf16", tau=("uniform", 0.5, 2.0), lam=0.5)
+    inp = W.make_fwd_inputs(cfg, 32)
+    Y = _gpu_fwd(inp, 0.5)
+    _oracle_sampled_compare(inp, Y, 0.5, 32, torch.bfloat16, n=24)
+
 def test_paper_head_size_guard_columns_untouched():
     """Padded columns are never stored: a Y buffer with guard rows after the
     last head keeps its sentinel values."""
