@@ -459,9 +459,10 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t] (the prefix's scratch before)
   __shared__ float s[kL], n1[kL], n2[kL];
   static_assert(kL * kP >= NT, "prefix scratch fits in atT");
-  // bf16 inputs: I is kept as a channel-major bf16 tile in it's place, at as
-  // split bf16 tiles (token-major) in atT's, and Qt as split bf16 tiles
-  // (token-major) in kT's once the sub-block tasks are done with it.
+  // bf16 inputs: I is kept as a channel-major bf16 tile in the memory of
+  // `it`, at as split bf16 tiles (token-major) in that of atT, and Qt as split
+  // bf16 tiles (token-major) in that of kT once the sub-block tasks are done
+  // with it.
   constexpr bool kSplit = sizeof(Tin) == 2;
   char* const itb = reinterpret_cast<char*>(&it[0][0]);
   char* const ath = reinterpret_cast<char*>(&atT[0][0]);
