@@ -228,6 +228,25 @@ def test_bwd_head_size_32_long_sequence():
         assert e <= TOL["bf16"], (name, e)
 
 
+@pytest.mark.parametrize("lam", [-2.0, 4.0])
+@pytest.mark.parametrize("shape", [(1, 2, 1500, 128, "bf16"), (1, 2, 700, 64, "f32")], ids=lambda s: "x".join(map(str, s)))
+def test_bwd_count_calibration_range(shape, lam):
+    """lambda far from its initial 0.5, both signs: -lambda log i then
+    outweighs the evidence (4.0) or lifts Exchange above Self (-2.0) over
+    most of the sequence. Y, LSE and every gradient against the oracle."""
+    B, H, T, D, dt = shape
+    cfg = W.FwdConfig("t", B, H, T, D, dt, tau=("uniform", 0.5, 2.0), lam=lam)
+    inp = W.make_bwd_inputs(cfg, 17 + T)
+    Y, L, g = _gpu_train(inp, lam)
+    ref = O.relation_fwd(*(f64(inp[k]) for k in ("P1", "P2", "V")), inp["tau"].astype(np.float64), lam)
+    if dt == "bf16":
+        assert float(np.max(np.abs(f64(Y) - ref))) <= 2e-2
+    else:
+        num = np.max(np.abs(f64(Y) - ref), axis=-1)
+        assert float(np.max(num / np.max(np.abs(ref), axis=-1))) <= 1e-5
+    _check(inp, lam, dt, Y, L, g, f"{shape} lam={lam}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "small"])
 def test_bwd_config_full(name):
     """Tiny (fp32, row-scan kernels) and Small (bf16, MFMA kernels) in full."""
