@@ -209,6 +209,39 @@ def test_large_evidence_regime(D, kernel):
             assert_parity(f64(Y), ref, dt, f"D={D} {dt}")
 
 
+
+@pytest.mark.parametrize("with_lse", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_overflowing_evidence_takes_the_redo_pass(D, with_lse):
+    """U ~ 100 on the rows of one 256-row query tile: with the fixed offset
+    m = 0 their weights would reach 2^144, past the 2^100 row-sum bound, so
+    the work-group redoes that tile with each row's evidence maximum as the
+    offset; the other tiles (|U| ~ 1.5) stay on the fixed-offset path. bf16
+    MFMA kernel; Y (and LSE) against the oracle everywhere."""
+    T, H = 700, 2
+    rng = np.random.default_rng(100 + D)
+    base = np.float32(np.sqrt(100.0 / np.sqrt(D)))
+    P2 = (base + 0.4 * rng.standard_normal((1, H, T, D))).astype(np.float32)
+    P1 = (0.5 * rng.standard_normal((1, H, T, D))).astype(np.float32)
+    P1[:, :, 256:512] = base + 0.4 * rng.standard_normal((1, H, 256, D))
+    V = (0.5 * rng.standard_normal((1, H, T, D))).astype(np.float32)
+    inp = dict(P1=torch.from_numpy(P1).to(torch.bfloat16), P2=torch.from_numpy(P2).to(torch.bfloat16),
+               V=torch.from_numpy(V).to(torch.bfloat16), tau=np.array([1.0, 0.7], np.float32))
+    ref = _oracle_full(inp, 0.5)
+    U = O.evidence(f64(inp["P1"])[0, 0], f64(inp["P2"])[0, 0])
+    assert float(np.max(U[300])) > 90.0 and float(np.max(np.abs(U[100, :100]))) < 10.0
+    P1d, P2d, Vd = _dev(inp)
+    if with_lse:
+        Y, L = R.fwd_lse(P1d, P2d, Vd, inp["tau"], 0.5)
+        torch.cuda.synchronize()
+        want = np.stack([O.row_lse(f64(inp["P1"])[0, h], f64(inp["P2"])[0, h], float(inp["tau"][h]), 0.5)
+                         for h in range(H)])
+        assert float(np.max(np.abs(f64(L)[0] - want))) <= 1e-4
+    else:
+        Y = R.fwd(P1d, P2d, Vd, inp["tau"], 0.5)
+        torch.cuda.synchronize()
+    assert_parity(f64(Y), ref, torch.bfloat16, f"redo D={D} lse={with_lse}")
+
 def test_zero_evidence_rows():
     """P2 = 0: S = 1/2, E = 0; the oracle's closed form holds on the GPU too."""
     for dt in (torch.float32, torch.bfloat16):

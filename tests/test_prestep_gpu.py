@@ -150,3 +150,45 @@ def test_model_forward_matches_oracle(case, mode, pairing, with_lse):
     assert torch.equal(Y, Y2)
     if with_lse:
         assert torch.equal(L, L2)
+
+
+@pytest.mark.parametrize("with_lse", [True, False])
+@pytest.mark.parametrize("mode", ["interleaved", "half"])
+def test_model_forward_redo_with_rotation_fused(mode, with_lse):
+    """The fused-rotation forward on rows whose rotated evidence reaches
+    U ~ 100 (one 256-row query tile): raw P1 and P2 are the target rows
+    rotated back by their positions, so the pre-step restores them. The
+    work-group redoes that tile, reloading and rotating its P1 rows again;
+    the result must match the oracle and, bit for bit, the forward on the
+    pre-stepped tensors."""
+    B, H, T, D = 1, 2, 600, 128
+    rng = np.random.default_rng(7)
+    base = np.sqrt(100.0 / np.sqrt(D))
+    pos = np.arange(T)
+    w2 = base + 0.4 * rng.standard_normal((B, H, T, D))
+    w1 = 0.5 * rng.standard_normal((B, H, T, D))
+    w1[:, :, 256:512] = base + 0.4 * rng.standard_normal((B, H, 256, D))
+    raw1 = PO.rope(w1, -pos, 1e4, mode)
+    raw2 = PO.rope(w2, -pos, 1e4, mode)
+    Vr = 0.5 * rng.standard_normal((B, H, T, D))
+    inp = {"P1": torch.from_numpy(raw1).to(torch.bfloat16), "P2": torch.from_numpy(raw2).to(torch.bfloat16),
+           "V": torch.from_numpy(Vr).to(torch.bfloat16), "tau": np.array([1.0, 0.8], np.float32)}
+    theta = np.array([0.3], np.float32)
+    pos0 = np.zeros(B, np.int32)
+    a, b, _ = PO.prestep(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), pos0, 1e4, mode, theta.astype(np.float64), "A")
+    assert float(np.max(a[0, 0, 300] @ b[0, 0, :301].T)) / np.sqrt(D) > 90.0
+    P1, P2, I = (inp[k].to(DEV) for k in ("P1", "P2", "V"))
+    p0 = torch.from_numpy(pos0).to(DEV)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV) if with_lse else None
+    Y, L, ws = R.fwd_model(P1, P2, I, inp["tau"], 0.5, p0, mode, 1e4, theta, "A", lse=lse)
+    torch.cuda.synchronize()
+    ref = PO.relation_fwd_model(f64(inp["P1"]), f64(inp["P2"]), f64(inp["V"]), inp["tau"].astype(np.float64),
+                                0.5, pos0, 1e4, mode, theta.astype(np.float64), "A")
+    assert_parity(f64(Y), ref, torch.bfloat16, f"redo fused {mode}")
+    want = R.prestep(P1, P2, I, p0, mode, 1e4, theta, "A")
+    if with_lse:
+        Y2, _ = R.fwd_lse(want[0], want[1], want[2], inp["tau"], 0.5)
+    else:
+        Y2 = R.fwd(want[0], want[1], want[2], inp["tau"], 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
