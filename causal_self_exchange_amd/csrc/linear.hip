@@ -29,10 +29,13 @@ constexpr int kChunkThreads = 256;     // chunk kernel: 4 waves, 66 KB of LDS (t
 constexpr int kOutThreads = 512;       // output kernel: 8 waves, 152 KB of LDS
 constexpr int kScanThreads = 256;
 static_assert(kL == 64, "the output kernel's sub-block pairs assume 4 blocks of 16 rows");
-// A diagonal 16-row block of the intra-chunk weights factors through its
-// middle row when every exponent of the two factors lies in [-40, 40]: the
-// factors and their products then stay normal fp32 numbers.
-constexpr float kFactorBound = 40.0f;
+// Decay prefixes are kept in base 2 (b2 = log2 of the retention product), so
+// every decay factor is one hardware 2^x. A diagonal 16-row block of the
+// intra-chunk weights factors through its middle row when every exponent of
+// the two factors lies in [-57, 57] (about e^+-40): the factors and their
+// products then stay normal fp32 numbers.
+constexpr float kFactorBound = 57.0f;
+__device__ __forceinline__ float pow2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -198,9 +201,10 @@ __device__ __forceinline__ void pipelined(Load load, Mma mma) {
   }
 }
 
-// In-place inclusive per-channel prefix of log alpha over the chunk (element
+// In-place inclusive per-channel prefix of log2 alpha over the chunk (element
 // (t, r) at b[t * rs + r * cs], holding alpha on entry; rows >= `rows` repeat
-// the last value). alpha is clamped to [1e-30, 1] (NaN to 1e-30): log alpha
+// the last value), so that e^{b_t - b_j} below is pow2 of a difference of
+// these. alpha is clamped to [1e-30, 1] (NaN to 1e-30): log alpha
 // stays finite, so differences of prefixes never form inf - inf, and a
 // retention below 1e-30 already wipes the state within one step to fp32
 // precision. NT / D threads share a channel, each a segment of consecutive
@@ -219,7 +223,7 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < kLen; ++i) {
-    if (t0 + i < rows) acc += logf(fminf(fmaxf(x[i], 1e-30f), 1.0f));
+    if (t0 + i < rows) acc += __builtin_amdgcn_logf(fminf(fmaxf(x[i], 1e-30f), 1.0f));
     x[i] = acc;
   }
   tot[seg * D + r] = acc;
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int t = 8 * cc + u;
-        x[k][u] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+        x[k][u] = t < rows ? s[t] * kt[t][r] * n2[t] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
       }
     }
     __syncthreads();
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   } else {
     for (int e = threadIdx.x; e < kL * D; e += NT) {
       const int t = e / D, r = e % D;
-      kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * __expf(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+      kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
     }
   }
   __syncthreads();
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
       for (int r = 0; r < 16; ++r)
         dC[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[m][r];
   }
-  if (threadIdx.x < D) a.decay[((size_t)bh * nc + c) * D + threadIdx.x] = __expf(bt[kL - 1][threadIdx.x]);
+  if (threadIdx.x < D) a.decay[((size_t)bh * nc + c) * D + threadIdx.x] = pow2(bt[kL - 1][threadIdx.x]);
 }
 
 // Phase 2: per state element (b*H + h, r, col): Cin_0 = 0,
@@ -572,10 +576,10 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
               }
             },
             [&](int ks, const OpP& o) {
-              const float bv = o.k * __expf(o.ref - o.bk);
+              const float bv = o.k * pow2(o.ref - o.bk);
 #pragma unroll
               for (int n = 0; n < N; ++n)
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.q[n] * __expf(o.bq[n] - o.ref), bv, acc[n], 0, 0, 0);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.q[n] * pow2(o.bq[n] - o.ref), bv, acc[n], 0, 0, 0);
             });
         // acc[n][i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16.
 #pragma unroll
@@ -611,8 +615,8 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 o.bk = bT[r][j];
               },
               [&](int ks, const OpAt& o) {
-                const float av = o.q * __expf(o.bq - o.ref);
-                const float bv = o.k * __expf(o.ref - o.bk);
+                const float av = o.q * pow2(o.bq - o.ref);
+                const float bv = o.k * pow2(o.ref - o.bk);
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
               });
           // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 tb + l16; only
@@ -625,7 +629,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
             const int t = 16 * tb + tl, j = 16 * tb + jl;
             float acc = 0.0f;
             if (jl < tl) {
-              for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], __expf(bT[r][t] - bT[r][j]), acc);
+              for (int r = 0; r < D; ++r) acc = fmaf(qT[r][t] * kT[r][j], pow2(bT[r][t] - bT[r][j]), acc);
             }
             put_at(t, j, acc);
           }
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int t = e % kL, cc = e / kL;
         float x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = qT[8 * cc + u][t] * __expf(bT[8 * cc + u][t]);
+        for (int u = 0; u < 8; ++u) x[u] = qT[8 * cc + u][t] * pow2(bT[8 * cc + u][t]);
         bf16x8v hi, lo;
         split_bf16(x, hi, lo);
         *reinterpret_cast<bf16x8v*>(qth + swd<D>(t, cc)) = hi;
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     } else {
       for (int e = tid; e < kL * D; e += NT) {
         const int r = e / kL, t = e % kL;
-        qT[r][t] *= __expf(bT[r][t]);
+        qT[r][t] *= pow2(bT[r][t]);
       }
     }
     __syncthreads();
