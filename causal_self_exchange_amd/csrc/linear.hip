@@ -122,6 +122,23 @@ struct Staged {
       }
     }
   }
+  // As store, each load's elements multiplied by sc[i] first.
+  template <bool kChannelMajor>
+  __device__ __forceinline__ void store_scaled(float* dst, int ld, int tid, const float (&sc)[kN]) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = tid + i * NT, e = idx * kVec;
+      if (idx >= kTot) break;
+      const int t = e / D, r0 = e % D;
+      float x[kVec];
+      unpack(i, x);
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) {
+        if (kChannelMajor) dst[(r0 + u) * ld + t] = x[u] * sc[i];
+        else dst[t * ld + r0 + u] = x[u] * sc[i];
+      }
+    }
+  }
   // bf16 rows (exact) into a channel-major bf16 tile: element (t, r) at
   // sw8(r, t / 8) + 2 (t % 8), i.e. the tokens of a channel contiguous.
   __device__ __forceinline__ void store_bf16_cm(char* dst, int tid) const {
@@ -138,13 +155,16 @@ struct Staged {
   }
 };
 
-// Row statistics of a chunk from its staged P1 and P2 rows: S_t into s[],
-// reciprocal row norms into n1[], n2[]. A row's D / kVec loads sit in
-// adjacent lanes, so each row takes a partial dot product per lane and a
-// short shuffle reduction; rows >= `rows` were loaded as zeros.
+// Row statistics of a chunk from its staged P1 and P2 rows: for each of the
+// thread's loads (row t), sc1 = S_t / |p1_t| and sc2 = S_t / |p2_t|, the
+// factors that turn the rows into S_t q_t and S_t k_t. A row's D / kVec loads
+// sit in adjacent lanes, so each row takes a partial dot product per lane
+// and a butterfly shuffle reduction that leaves the totals in every lane of
+// the row; rows >= `rows` (loaded as zeros) get 0.
 template <int NT, typename Tin, int D>
 __device__ __forceinline__ void staged_row_stats(const Staged<NT, Tin, D>& g1, const Staged<NT, Tin, D>& g2, int rows,
-                                                 float inv_scale, float* s, float* n1, float* n2, int tid) {
+                                                 float inv_scale, float (&sc1)[Staged<NT, Tin, D>::kN],
+                                                 float (&sc2)[Staged<NT, Tin, D>::kN], int tid) {
   using St = Staged<NT, Tin, D>;
   constexpr int kLanes = D / St::kVec;              // lanes per row
   static_assert(kLanes <= 64 && 64 % kLanes == 0 && NT % 64 == 0, "a row's loads share a wave");
@@ -167,13 +187,11 @@ __device__ __forceinline__ void staged_row_stats(const Staged<NT, Tin, D>& g1, c
       d11 += __shfl_xor(d11, w, kLanes);
       d22 += __shfl_xor(d22, w, kLanes);
     }
-    if (idx < St::kTot && idx % kLanes == 0) {
-      const int t = idx / kLanes;
-      s[t] = t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
-      // A zero row has no direction: its normalised coordinate is 0.
-      n1[t] = d11 > 0.0f ? 1.0f / sqrtf(d11) : 0.0f;
-      n2[t] = d22 > 0.0f ? 1.0f / sqrtf(d22) : 0.0f;
-    }
+    const int t = idx / kLanes;
+    const float st = idx < St::kTot && t < rows ? sigmoid_f32(d12 * inv_scale) : 0.0f;
+    // A zero row has no direction: its normalised coordinate is 0.
+    sc1[i] = d11 > 0.0f ? st * (1.0f / sqrtf(d11)) : 0.0f;
+    sc2[i] = d22 > 0.0f ? st * (1.0f / sqrtf(d22)) : 0.0f;
   }
 }
 
@@ -246,9 +264,8 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
 template <typename Tin, int D>
 __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kChunkThreads;
-  __shared__ float kt[kL][D];     // p2_j, then S_j k_j e^{b_last - b_j}
+  __shared__ float kt[kL][D];     // S_j k_j, then S_j k_j e^{b_last - b_j}
   __shared__ float bt[kL][D];     // alpha_j, then b_j
-  __shared__ float s[kL], n1[kL], n2[kL];
   __shared__ float tot[NT];
   const int nc = (a.T + kL - 1) / kL;
   const int c = blockIdx.x % nc;
@@ -296,8 +313,9 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
     g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
     g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
     ga.load(a.alpha + base, rows, threadIdx.x);
-    staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], s, n1, n2, threadIdx.x);
-    g2.template store<false>(&kt[0][0], D, threadIdx.x);
+    float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
+    staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
+    g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
     ga.template store<false>(&bt[0][0], D, threadIdx.x);
   }
   __syncthreads();
@@ -318,7 +336,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int t = 8 * cc + u;
-        x[k][u] = t < rows ? s[t] * kt[t][r] * n2[t] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+        x[k][u] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
       }
     }
     __syncthreads();
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   } else {
     for (int e = threadIdx.x; e < kL * D; e += NT) {
       const int t = e / D, r = e % D;
-      kt[t][r] = t < rows ? s[t] * kt[t][r] * n2[t] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+      kt[t][r] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
     }
   }
   __syncthreads();
@@ -461,7 +479,6 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ float bT[D][kP];     // b_{t,r}
   __shared__ float it[kL][D];     // I_j
   __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t] (the prefix's scratch before)
-  __shared__ float s[kL], n1[kL], n2[kL];
   static_assert(kL * kP >= NT, "prefix scratch fits in atT");
   // bf16 inputs: I is kept as a channel-major bf16 tile in the memory of
   // `it`, at as split bf16 tiles (token-major) in that of atT, and Qt as split
@@ -520,9 +537,12 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int rows = min(kL, a.T - c * kL);
     Tin* Y = static_cast<Tin*>(a.Y) + ((size_t)bh * a.T + (size_t)c * kL) * D;
     // The previous chunk's LDS is free (the barrier that ends its iteration).
-    staged_row_stats(nx.p1, nx.p2, rows, hp.scale * hp.inv_tau[h], s, n1, n2, tid);
-    nx.p1.template store<true>(&qT[0][0], kP, tid);
-    nx.p2.template store<true>(&kT[0][0], kP, tid);
+    {
+      float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
+      staged_row_stats(nx.p1, nx.p2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, tid);
+      nx.p1.template store_scaled<true>(&qT[0][0], kP, tid, sc1);    // S_t q_t
+      nx.p2.template store_scaled<true>(&kT[0][0], kP, tid, sc2);    // S_j k_j
+    }
     if constexpr (kSplit) nx.in.store_bf16_cm(itb, tid);
     else nx.in.template store<false>(&it[0][0], D, tid);
     nx.al.template store<true>(&bT[0][0], kP, tid);
@@ -539,12 +559,6 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
     __syncthreads();
     decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0], tid);
-    __syncthreads();
-    for (int e = tid; e < kL * D; e += NT) {
-      const int r = e / kL, t = e % kL;
-      qT[r][t] *= s[t] * n1[t];
-      kT[r][t] *= s[t] * n2[t];
-    }
     __syncthreads();
 
     // Sub-block tasks on the 8 waves. The pairs below the diagonal (tb, jb),
