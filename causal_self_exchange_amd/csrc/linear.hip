@@ -651,11 +651,14 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
       }
     }
     // The zero blocks above the diagonal.
+    // Block p of (0,1) (0,2) (0,3) (1,2) (1,3) (2,3), found by arithmetic:
+    // an indexed table would sit in constant memory and its load's wait
+    // would also drain the column and prefetch loads still in flight.
     for (int e = tid; e < 6 * 256; e += NT) {
-      constexpr int kUpT[6] = {0, 0, 0, 1, 1, 2};
-      constexpr int kUpJ[6] = {1, 2, 3, 2, 3, 3};
       const int p = e >> 8, tl = (e >> 4) & 15, jl = e & 15;
-      put_at(16 * kUpT[p] + tl, 16 * kUpJ[p] + jl, 0.0f);
+      const int tb = (p >= 3) + (p >= 5);
+      const int jb = p + 1 - 2 * (p >= 3) - (p >= 5);
+      put_at(16 * tb + tl, 16 * jb + jl, 0.0f);
     }
     __syncthreads();
     // Qt = S q o e^{b} (every exponent <= 0): in place, or split into
