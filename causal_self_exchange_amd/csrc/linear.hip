@@ -252,8 +252,13 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
   for (int i = 0; i < kLen; ++i) b[(t0 + i) * rs + r * cs] = x[i] + off;
 }
 
-// Phase 1: per (b*H + h, chunk): dC = sum_j S_j (k_j o e^{b_last - b_j}) I_j^T
-// and g = e^{b_last}, into the state slot of the chunk. dC = Kt^T I is a
+// Phase 1: per (b*H + h, group of a.group consecutive chunks): the group's
+// contribution to the state, dG = sum over its chunks c of
+// Diag(e^{b_last of the later chunks of the group}) dC_c with
+// dC_c = sum_j S_j (k_j o e^{b_last,c - b_j}) I_j^T, and the group's decay
+// g = e^{sum of its b_last}, into the group's state slot. The chunks are
+// taken in order with the state accumulators in registers: before chunk c is
+// added, the accumulated rows are scaled by e^{b_last,c}. dC_c = Kt^T I is a
 // d_h x d_h x 64 product: on v_mfma_f32_32x32x2_f32 for fp32 inputs, on
 // v_mfma_f32_32x32x16_bf16 over Kt's split bf16 pair for bf16 inputs. A wave
 // owns column block n and all row blocks (independent accumulators that share
@@ -268,147 +273,172 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   __shared__ float bt[kL][D];     // alpha_j, then b_j
   __shared__ float tot[NT];
   const int nc = (a.T + kL - 1) / kL;
-  const int c = blockIdx.x % nc;
-  const int bh = blockIdx.x / nc;
+  const int ng = (nc + a.group - 1) / a.group;
+  const int gi = blockIdx.x % ng;
+  const int bh = blockIdx.x / ng;
   const int h = bh % a.H;
-  const int t0 = c * kL;
-  const int rows = min(kL, a.T - t0);
-  const size_t base = ((size_t)bh * a.T + t0) * D;
-  const Tin* I = static_cast<const Tin*>(a.I) + base;
+  const int c0 = gi * a.group, c1 = min(nc, c0 + a.group);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
   constexpr int kT = D / 32;
   constexpr int kNPerWave = (kT + 3) / 4;            // column blocks per wave (ceil)
   constexpr bool kSplit = sizeof(Tin) == 2;          // bf16 MFMA on split operands
-
-  // I operands of this wave's column blocks, issued first and consumed last:
-  // fp32, B[j][col] = I_j[col] with j = 2 ks + lh; bf16, 8 rows j = 16 kk +
-  // 8 lh + e per k-step. Rows past the chunk's end read the last row (an
-  // address inside the tensor) and are zeroed afterwards, so no load sits
-  // behind a per-lane branch.
-  float bf[kSplit ? 1 : kNPerWave][kSplit ? 1 : kL / 2];
-  bf16x8v bi[kSplit ? kNPerWave : 1][kL / 16];
-#pragma unroll
-  for (int q = 0; q < kNPerWave; ++q) {
-    const int n = wave + 4 * q;
-    if (n >= kT) break;
-    if constexpr (kSplit) {
-#pragma unroll
-      for (int kk = 0; kk < kL / 16; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bi[q][kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
-#pragma unroll
-      for (int kk = 0; kk < kL / 16; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bi[q][kk][e] = 16 * kk + 8 * lh + e < rows ? bi[q][kk][e] : (__bf16)0.0f;
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
-#pragma unroll
-      for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
-    }
-  }
-  {
-    Staged<NT, Tin, D> g1, g2;
-    Staged<NT, float, D> ga;
-    g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
-    g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
-    ga.load(a.alpha + base, rows, threadIdx.x);
-    float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
-    staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
-    g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
-    ga.template store<false>(&bt[0][0], D, threadIdx.x);
-  }
-  __syncthreads();
-  decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
-  __syncthreads();
-  // Kt_j = S_j k_j o e^{b_last - b_j} (rows past the chunk's end: 0). The
-  // bf16 path splits it into two channel-major bf16 tiles (channel r, tokens
-  // contiguous) that take kt's place once every thread has read its values.
   char* const kh = reinterpret_cast<char*>(&kt[0][0]);
   char* const kl = kh + D * 128;
-  if constexpr (kSplit) {
-    constexpr int kG = (kL * D / 8 + NT - 1) / NT;   // 8-token groups per thread
-    float x[kG][8];
+
+  // acc[q][m]: rows 32 m + 8 (r >> 2) + 4 lh + (r & 3), columns 32 (wave + 4 q) + l32.
+  f32x16 acc[kNPerWave][kT];
 #pragma unroll
-    for (int k = 0; k < kG; ++k) {
-      const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
-      if (idx >= kL * D / 8) break;
+  for (int q = 0; q < kNPerWave; ++q)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = 8 * cc + u;
-        x[k][u] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+    for (int m = 0; m < kT; ++m) acc[q][m] = f32x16{};
+  float bsum = 0.0f;                                 // thread r < D: sum of b_last,c[r]
+
+  for (int c = c0; c < c1; ++c) {
+    const int t0 = c * kL;
+    const int rows = min(kL, a.T - t0);
+    const size_t base = ((size_t)bh * a.T + t0) * D;
+    const Tin* I = static_cast<const Tin*>(a.I) + base;
+    // I operands of this wave's column blocks, issued first and consumed
+    // last: fp32, B[j][col] = I_j[col] with j = 2 ks + lh; bf16, 8 rows j =
+    // 16 kk + 8 lh + e per k-step. Rows past the chunk's end read the last
+    // row (an address inside the tensor) and are zeroed afterwards, so no
+    // load sits behind a per-lane branch.
+    float bf[kSplit ? 1 : kNPerWave][kSplit ? 1 : kL / 2];
+    bf16x8v bi[kSplit ? kNPerWave : 1][kL / 16];
+#pragma unroll
+    for (int q = 0; q < kNPerWave; ++q) {
+      const int n = wave + 4 * q;
+      if (n >= kT) break;
+      if constexpr (kSplit) {
+#pragma unroll
+        for (int kk = 0; kk < kL / 16; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bi[q][kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
+#pragma unroll
+        for (int kk = 0; kk < kL / 16; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bi[q][kk][e] = 16 * kk + 8 * lh + e < rows ? bi[q][kk][e] : (__bf16)0.0f;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
+#pragma unroll
+        for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
+      }
+    }
+    {
+      Staged<NT, Tin, D> g1, g2;
+      Staged<NT, float, D> ga;
+      g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
+      g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
+      ga.load(a.alpha + base, rows, threadIdx.x);
+      float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
+      staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
+      g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
+      ga.template store<false>(&bt[0][0], D, threadIdx.x);
+    }
+    __syncthreads();
+    decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
+    __syncthreads();
+    // Kt_j = S_j k_j o e^{b_last - b_j} (rows past the chunk's end: 0). The
+    // bf16 path splits it into two channel-major bf16 tiles (channel r,
+    // tokens contiguous) that take kt's place once every thread has read its
+    // values.
+    if constexpr (kSplit) {
+      constexpr int kG = (kL * D / 8 + NT - 1) / NT;   // 8-token groups per thread
+      float x[kG][8];
+#pragma unroll
+      for (int k = 0; k < kG; ++k) {
+        const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
+        if (idx >= kL * D / 8) break;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int t = 8 * cc + u;
+          x[k][u] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kG; ++k) {
+        const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
+        if (idx >= kL * D / 8) break;
+        bf16x8v hi, lo;
+        split_bf16(x[k], hi, lo);
+        *reinterpret_cast<bf16x8v*>(kh + sw8(r, cc)) = hi;
+        *reinterpret_cast<bf16x8v*>(kl + sw8(r, cc)) = lo;
+      }
+    } else {
+      for (int e = threadIdx.x; e < kL * D; e += NT) {
+        const int t = e / D, r = e % D;
+        kt[t][r] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
       }
     }
     __syncthreads();
+    if (threadIdx.x < D) bsum += bt[kL - 1][threadIdx.x];
 #pragma unroll
-    for (int k = 0; k < kG; ++k) {
-      const int idx = threadIdx.x + k * NT, r = idx % D, cc = idx / D;
-      if (idx >= kL * D / 8) break;
-      bf16x8v hi, lo;
-      split_bf16(x[k], hi, lo);
-      *reinterpret_cast<bf16x8v*>(kh + sw8(r, cc)) = hi;
-      *reinterpret_cast<bf16x8v*>(kl + sw8(r, cc)) = lo;
+    for (int q = 0; q < kNPerWave; ++q) {
+      const int n = wave + 4 * q;
+      if (n >= kT) break;
+      if (c > c0) {
+        // The group's earlier chunks decay over this one.
+#pragma unroll
+        for (int m = 0; m < kT; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[q][m][r] *= pow2(bt[kL - 1][32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)]);
+      }
+      if constexpr (kSplit) {
+        // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per k-step.
+        struct Op { bf16x8v h[kT], l[kT]; };
+        pipelined<kL / 16, 2, Op>(
+            [&](int kk, Op& o) {
+#pragma unroll
+              for (int m = 0; m < kT; ++m) {
+                o.h[m] = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
+                o.l[m] = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
+              }
+            },
+            [&](int kk, const Op& o) {
+#pragma unroll
+              for (int m = 0; m < kT; ++m) {
+                acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h[m], bi[q][kk], acc[q][m], 0, 0, 0);
+                acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l[m], bi[q][kk], acc[q][m], 0, 0, 0);
+              }
+            });
+      } else {
+        struct Op { float a[kT]; };
+        pipelined<kL / 2, 4, Op>(
+            [&](int ks, Op& o) {
+#pragma unroll
+              for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
+            },
+            [&](int ks, const Op& o) {
+#pragma unroll
+              for (int m = 0; m < kT; ++m) acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[q][m], 0, 0, 0);
+            });
+      }
     }
-  } else {
-    for (int e = threadIdx.x; e < kL * D; e += NT) {
-      const int t = e / D, r = e % D;
-      kt[t][r] = t < rows ? kt[t][r] * pow2(bt[kL - 1][r] - bt[t][r]) : 0.0f;
-    }
+    __syncthreads();                                 // kt and bt are rewritten by the next chunk
   }
-  __syncthreads();
-  float* dC = a.state + ((size_t)bh * nc + c) * (size_t)D * D;
+  float* dG = a.state + ((size_t)bh * ng + gi) * (size_t)D * D;
 #pragma unroll
   for (int q = 0; q < kNPerWave; ++q) {
     const int n = wave + 4 * q;
     if (n >= kT) break;
-    f32x16 acc[kT];
-#pragma unroll
-    for (int m = 0; m < kT; ++m) acc[m] = f32x16{};
-    if constexpr (kSplit) {
-      // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per k-step.
-      struct Op { bf16x8v h[kT], l[kT]; };
-      pipelined<kL / 16, 2, Op>(
-          [&](int kk, Op& o) {
-#pragma unroll
-            for (int m = 0; m < kT; ++m) {
-              o.h[m] = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
-              o.l[m] = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
-            }
-          },
-          [&](int kk, const Op& o) {
-#pragma unroll
-            for (int m = 0; m < kT; ++m) {
-              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h[m], bi[q][kk], acc[m], 0, 0, 0);
-              acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l[m], bi[q][kk], acc[m], 0, 0, 0);
-            }
-          });
-    } else {
-      struct Op { float a[kT]; };
-      pipelined<kL / 2, 4, Op>(
-          [&](int ks, Op& o) {
-#pragma unroll
-            for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
-          },
-          [&](int ks, const Op& o) {
-#pragma unroll
-            for (int m = 0; m < kT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[m], 0, 0, 0);
-          });
-    }
 #pragma unroll
     for (int m = 0; m < kT; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        dC[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[m][r];
+        dG[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[q][m][r];
   }
-  if (threadIdx.x < D) a.decay[((size_t)bh * nc + c) * D + threadIdx.x] = pow2(bt[kL - 1][threadIdx.x]);
+  if (threadIdx.x < D) a.decay[((size_t)bh * ng + gi) * D + threadIdx.x] = pow2(bsum);
 }
 
-// Phase 2: per state element (b*H + h, r, col): Cin_0 = 0,
-// Cin_{c+1} = e^{b_last,c}[r] Cin_c + dC_c; each chunk slot is overwritten
-// with its entering state, and the final state goes to a.final (if given).
+// Phase 2: per state element (b*H + h, r, col), over the groups of chunks:
+// Cin_0 = 0, Cin_{g+1} = e^{sum of the group's b_last}[r] Cin_g + dG_g; each
+// group slot is overwritten with the state entering the group's first chunk,
+// and the final state goes to a.final (if given).
 // A thread owns 4 consecutive elements of one row r (16-byte accesses; the
 // state buffers are 16-byte aligned) and loads the contributions and decays
-// of kScanAhead chunks before it uses them, so that many loads are in flight
+// of kScanAhead groups before it uses them, so that many loads are in flight
 // per thread.
 constexpr int kScanAhead = 8;
 
@@ -421,15 +451,16 @@ __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
   const long long bh = idx / kQ;
   const int r = e / D;
   const int nc = (a.T + kL - 1) / kL;
-  float4* st = reinterpret_cast<float4*>(a.state + (size_t)bh * nc * D * D + e);
-  const float* g = a.decay + (size_t)bh * nc * D + r;
+  const int ng = (nc + a.group - 1) / a.group;
+  float4* st = reinterpret_cast<float4*>(a.state + (size_t)bh * ng * D * D + e);
+  const float* g = a.decay + (size_t)bh * ng * D + r;
   float4 C = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   auto step = [&](float4& slot, float4 dc, float gc) __attribute__((always_inline)) {
     slot = C;
     C = make_float4(fmaf(gc, C.x, dc.x), fmaf(gc, C.y, dc.y), fmaf(gc, C.z, dc.z), fmaf(gc, C.w, dc.w));
   };
   int c = 0;
-  for (; c + kScanAhead <= nc; c += kScanAhead) {
+  for (; c + kScanAhead <= ng; c += kScanAhead) {
     float4 dc[kScanAhead];
     float gc[kScanAhead];
 #pragma unroll
@@ -440,7 +471,7 @@ __global__ __launch_bounds__(kScanThreads) void lin_scan_kernel(LinArgs a) {
 #pragma unroll
     for (int k = 0; k < kScanAhead; ++k) step(st[(size_t)(c + k) * kQ], dc[k], gc[k]);
   }
-  for (; c < nc; ++c) step(st[(size_t)c * kQ], st[(size_t)c * kQ], g[(size_t)c * D]);
+  for (; c < ng; ++c) step(st[(size_t)c * kQ], st[(size_t)c * kQ], g[(size_t)c * D]);
   if (a.final) *reinterpret_cast<float4*>(a.final + (size_t)bh * D * D + e) = C;
 }
 
@@ -481,16 +512,20 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ float atT[kL][kP];   // at[t][j] stored as atT[j][t] (the prefix's scratch before)
   static_assert(kL * kP >= NT, "prefix scratch fits in atT");
   // bf16 inputs: I is kept as a channel-major bf16 tile in the memory of
-  // `it`, at as split bf16 tiles (token-major) in that of atT, and Qt as split
-  // bf16 tiles (token-major) in that of kT once the sub-block tasks are done
-  // with it.
+  // `it`, at as split bf16 tiles (token-major) in that of atT; once the
+  // sub-block tasks are done, Qt goes as split bf16 tiles (token-major) into
+  // the memory of qT and Kt_j = S_j k_j o e^{b_last - b_j} (the operand of the
+  // state update) as split bf16 tiles (channel-major) into that of kT.
   constexpr bool kSplit = sizeof(Tin) == 2;
   char* const itb = reinterpret_cast<char*>(&it[0][0]);
   char* const ath = reinterpret_cast<char*>(&atT[0][0]);
   char* const atl = ath + kL * 128;
-  char* const qth = reinterpret_cast<char*>(&kT[0][0]);
+  char* const qth = reinterpret_cast<char*>(&qT[0][0]);
   char* const qtl = qth + kL * 2 * D;
-  static_assert(2 * kL * 128 <= (int)sizeof(atT) && 4 * kL * D <= (int)sizeof(kT), "split tiles fit");
+  char* const kth = reinterpret_cast<char*>(&kT[0][0]);
+  char* const ktl = kth + D * 128;
+  static_assert(2 * kL * 128 <= (int)sizeof(atT) && 4 * kL * D <= (int)sizeof(qT) && 4 * kL * D <= (int)sizeof(kT),
+                "split tiles fit");
   // at[t][j] into its tile(s).
   auto put_at = [&](int t, int j, float v) __attribute__((always_inline)) {
     if constexpr (kSplit) {
@@ -503,7 +538,8 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
   };
   const int nc = (a.T + kL - 1) / kL;
-  const int total = a.B * a.H * nc;
+  const int ng = (nc + a.group - 1) / a.group;
+  const int total_g = a.B * a.H * ng;
   constexpr int kTN = D / 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool has_tile = wave < 2 * kTN;              // output tile (m, n) of this wave
@@ -524,14 +560,28 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     f.al.load(a.alpha + base, rows, tid);
   };
 
+  // The work-group takes the groups gl = blockIdx.x + k gridDim.x (gl = bh ng
+  // + group within the head) and walks each group's chunks in order, with
+  // the entering state of the current chunk in registers: loaded at the
+  // group's first chunk, stepped on chip to the next one (bf16 inputs; fp32
+  // inputs come with one chunk per group).
+  auto chunk_of = [&](int gl, int k) { return (gl / ng) * nc + (gl % ng) * a.group + k; };
+  // cf: this wave's column of Cin, element ks at cf[ks / 16][ks % 16]. fp32:
+  // B[r][col] with r = 2 ks + lh; bf16: the order of an MFMA accumulator,
+  // state row 32 (ks / 16) + 8 ((ks / 4) % 4) + 4 lh + ks % 4, so that the
+  // update accumulates into it.
+  f32x16 cf[kTN];
   OutPrefetch<Tin, D> nx;
-  if ((int)blockIdx.x < total) fetch(blockIdx.x, nx);
-  for (int g = blockIdx.x; g < total; g += gridDim.x) {
+  if ((int)blockIdx.x < total_g) fetch(chunk_of(blockIdx.x, 0), nx);
+  for (int gl = blockIdx.x, k = 0; gl < total_g;) {
     tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     lane = tid & 63;
     l32 = lane & 31;
     lh = lane >> 5;
+    const int len = min(a.group, nc - (gl % ng) * a.group);
+    const int g = chunk_of(gl, k);
+    const int ngl = k + 1 < len ? gl : gl + (int)gridDim.x, nk = k + 1 < len ? k + 1 : 0;
     const int c = g % nc, bh = g / nc;
     const int h = bh % a.H;
     const int rows = min(kL, a.T - c * kL);
@@ -546,17 +596,15 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     if constexpr (kSplit) nx.in.store_bf16_cm(itb, tid);
     else nx.in.template store<false>(&it[0][0], D, tid);
     nx.al.template store<true>(&bT[0][0], kP, tid);
-    float cf[D / 2];
-    if (has_tile) {
-      const float* cin = a.state + (size_t)g * D * D;
-      // fp32: B[r][col] with r = 2 ks + lh; bf16: rows r = 16 kk + 8 lh + e at cf[8 kk + e].
+    if (has_tile && k == 0) {
+      const float* cin = a.state + (size_t)gl * D * D;
 #pragma unroll
       for (int ks = 0; ks < D / 2; ++ks) {
-        const int r = kSplit ? 16 * (ks / 8) + 8 * lh + ks % 8 : 2 * ks + lh;
-        cf[ks] = cin[(size_t)r * D + 32 * n_out + l32];
+        const int r = kSplit ? 32 * (ks >> 4) + 8 * ((ks >> 2) & 3) + 4 * lh + (ks & 3) : 2 * ks + lh;
+        cf[ks >> 4][ks & 15] = cin[(size_t)r * D + 32 * n_out + l32];
       }
     }
-    if (g + (int)gridDim.x < total) fetch(g + gridDim.x, nx);
+    if (ngl < total_g) fetch(chunk_of(ngl, nk), nx);
     __syncthreads();
     decay_prefix<NT, D>(&bT[0][0], 1, kP, rows, &atT[0][0], tid);
     __syncthreads();
@@ -662,17 +710,41 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     __syncthreads();
     // Qt = S q o e^{b} (every exponent <= 0): in place, or split into
-    // token-major bf16 tiles (kT is no longer read).
+    // token-major bf16 tiles over qT, whose 16-byte chunk cc holds channels
+    // 16 (cc / 2) + 4 (cc % 2) + 8 (u / 4) + u % 4 (u = 0..7), the state rows
+    // that the lanes of half cc % 2 hold in cf. The bf16 path also splits
+    // Kt = S k o e^{b_last - b} into channel-major tiles over kT. Both read
+    // every value first: the tiles overwrite the arrays they are formed from.
     if constexpr (kSplit) {
-      for (int e = tid; e < kL * D / 8; e += NT) {
-        const int t = e % kL, cc = e / kL;
-        float x[8];
+      constexpr int kG = (kL * D / 8 + NT - 1) / NT;
+      float xq[kG][8], xk[kG][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = qT[8 * cc + u][t] * pow2(bT[8 * cc + u][t]);
+      for (int q = 0; q < kG; ++q) {
+        const int e = tid + q * NT;
+        if (e >= kL * D / 8) break;
+        const int t = e % kL, cc = e / kL;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = 16 * (cc >> 1) + 4 * (cc & 1) + 8 * (u >> 2) + (u & 3);
+          xq[q][u] = qT[r][t] * pow2(bT[r][t]);
+        }
+        const int rk = e % D, ck = e / D;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xk[q][u] = kT[rk][8 * ck + u] * pow2(bT[rk][kL - 1] - bT[rk][8 * ck + u]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kG; ++q) {
+        const int e = tid + q * NT;
+        if (e >= kL * D / 8) break;
+        const int t = e % kL, cc = e / kL, rk = e % D, ck = e / D;
         bf16x8v hi, lo;
-        split_bf16(x, hi, lo);
+        split_bf16(xq[q], hi, lo);
         *reinterpret_cast<bf16x8v*>(qth + swd<D>(t, cc)) = hi;
         *reinterpret_cast<bf16x8v*>(qtl + swd<D>(t, cc)) = lo;
+        split_bf16(xk[q], hi, lo);
+        *reinterpret_cast<bf16x8v*>(kth + sw8(rk, ck)) = hi;
+        *reinterpret_cast<bf16x8v*>(ktl + sw8(rk, ck)) = lo;
       }
     } else {
       for (int e = tid; e < kL * D; e += NT) {
@@ -709,7 +781,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
             [&](int kk, const OpQ& o) {
               float x[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = cf[8 * kk + e];
+              for (int e = 0; e < 8; ++e) x[e] = cf[kk >> 1][8 * (kk & 1) + e];
               bf16x8v ch, cl;
               split_bf16(x, ch, cl);
               acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, ch, acc, 0, 0, 0);
@@ -725,7 +797,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
             },
             [&](int ks, const Op2& o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a, o.b, acc, 0, 0, 0); });
         pipelined<D / 2, 8, float>([&](int ks, float& o) { o = qT[2 * ks + lh][t]; },
-                                   [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks], acc, 0, 0, 0); });
+                                   [&](int ks, float o) { acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o, cf[ks >> 4][ks & 15], acc, 0, 0, 0); });
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -735,26 +807,71 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
         else iv = it[tr][col];
         if (tr < rows) Y[(size_t)tr * D + col] = from_f32<Tin>(iv + acc[r]);
       }
+      if constexpr (kSplit) {
+        if (k + 1 < len) {
+          // The next chunk's entering state: cf = e^{b_last} cf + (Kt^T I)
+          // column, accumulated into cf on the same split operands (the
+          // chunk is whole).
+#pragma unroll
+          for (int ks = 0; ks < D / 2; ++ks)
+            cf[ks >> 4][ks & 15] *= pow2(bT[32 * (ks >> 4) + 8 * ((ks >> 2) & 3) + 4 * lh + (ks & 3)][kL - 1]);
+          struct OpU { bf16x8v h, l, b; };
+          pipelined<kTN * kL / 16, 2, OpU>(
+              [&](int st, OpU& o) {
+                const int m = st / (kL / 16), kk = st % (kL / 16);
+                o.h = lds_bf16x8(kth, sw8(32 * m + l32, 2 * kk + lh));
+                o.l = lds_bf16x8(ktl, sw8(32 * m + l32, 2 * kk + lh));
+                o.b = lds_bf16x8(itb, sw8(col, 2 * kk + lh));
+              },
+              [&](int st, const OpU& o) {
+                const int m = st / (kL / 16);
+                cf[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, o.b, cf[m], 0, 0, 0);
+                cf[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, o.b, cf[m], 0, 0, 0);
+              });
+        }
+      }
     }
     __syncthreads();
+    gl = ngl;
+    k = nk;
   }
 }
 
+// Chunks per group: the largest power of two up to kMaxGroup that still
+// leaves kMinGroupsPerCu groups per compute unit (1 if none does). Larger
+// groups move fewer states through HBM (one per group is written, scanned
+// and read back) but walk more chunks in sequence per work-group. fp32 inputs
+// take one chunk per group (their output kernel has no on-chip update).
+constexpr int kMaxGroup = 16;
+constexpr int kMinGroupsPerCu = 1;
+
 template <typename Tin, int D>
-hipError_t launch_typed(const LinArgs& a, const HeadParams& hp, hipStream_t s) {
-  const int nc = (a.T + kL - 1) / kL;
-  const long long wg = (long long)a.B * a.H * nc;
-  const long long scan_threads = (long long)a.B * a.H * D * D / 4;
-  if (wg > 0x7fffffffLL || (scan_threads + kScanThreads - 1) / kScanThreads > 0x7fffffffLL) return hipErrorInvalidValue;
-  // The output kernel is persistent: one work-group per compute unit (its LDS
-  // admits one).
+hipError_t launch_typed(const LinArgs& args, const HeadParams& hp, hipStream_t s) {
+  const int nc = (args.T + kL - 1) / kL;
+  const long long chunks = (long long)args.B * args.H * nc;
+  const long long scan_threads = (long long)args.B * args.H * D * D / 4;
+  if (chunks > 0x7fffffffLL || (scan_threads + kScanThreads - 1) / kScanThreads > 0x7fffffffLL) return hipErrorInvalidValue;
   int n_cu = 0;
   const hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((lin_chunk_kernel<Tin, D>), dim3((unsigned)wg), dim3(kChunkThreads), 0, s, a, hp);
+  LinArgs a = args;
+  a.group = 1;
+  if (sizeof(Tin) == 2) {
+    for (int gsz = kMaxGroup; gsz > 1; gsz >>= 1) {
+      if ((long long)args.B * args.H * ((nc + gsz - 1) / gsz) >= (long long)kMinGroupsPerCu * n_cu) {
+        a.group = gsz;
+        break;
+      }
+    }
+  }
+  const long long groups = (long long)args.B * args.H * ((nc + a.group - 1) / a.group);
+  hipLaunchKernelGGL((lin_chunk_kernel<Tin, D>), dim3((unsigned)groups), dim3(kChunkThreads), 0, s, a, hp);
   hipLaunchKernelGGL((lin_scan_kernel<D>), dim3((unsigned)((scan_threads + kScanThreads - 1) / kScanThreads)),
                      dim3(kScanThreads), 0, s, a);
-  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)(wg < n_cu ? wg : n_cu)), dim3(kOutThreads), 0, s, a, hp);
+  // The output kernel is persistent: one work-group per compute unit (its LDS
+  // admits one).
+  hipLaunchKernelGGL((lin_out_kernel<Tin, D>), dim3((unsigned)(groups < n_cu ? groups : n_cu)), dim3(kOutThreads), 0, s,
+                     a, hp);
   return hipGetLastError();
 }
 

@@ -115,9 +115,10 @@ struct LinArgs {
   const float* alpha;   // [B][H][T][d_h] channel-wise retention
   void* Y;
   float* final;         // optional [B][H][d_h][d_h] final state C_T
-  float* state;         // workspace: [B*H][ceil(T/64)][d_h][d_h] chunk states
-  float* decay;         // workspace: [B*H][ceil(T/64)][d_h] chunk decays
+  float* state;         // workspace: [B*H][groups][d_h][d_h] group states
+  float* decay;         // workspace: [B*H][groups][d_h] group decays
   int B, H, T, d_h;
+  int group;            // chunks per group (set by the launcher; groups = ceil(ceil(T/64) / group))
 };
 inline int64_t lin_state_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D * D; }
 inline int64_t lin_decay_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D; }

@@ -315,7 +315,7 @@ rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I, co
   char* ws = static_cast<char*>(workspace);
   float* state = reinterpret_cast<float*>(ws);
   float* decay = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float)));
-  rel::LinArgs a{P1, P2, I, alpha, Y, state_out, state, decay, B, H, T, d_h};
+  rel::LinArgs a{P1, P2, I, alpha, Y, state_out, state, decay, B, H, T, d_h, 1};
   return rel::launch_linear(a, hp, dt == REL_BF16, stream) == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
 

@@ -128,3 +128,25 @@ def test_linear_long_shape_full_heads(h):
     sub = {k: inp[k][:, h:h + 1] for k in ("P1", "P2", "V", "alpha")}
     sub["tau"] = inp["tau"][h:h + 1]
     _check(sub, Y[:, h:h + 1], st[:, h:h + 1], "bf16", f"long h={h}")
+
+
+# Shapes whose chunk count selects grouped walks (on a 256-CU device: 2, 4, 8
+# and 16 chunks per group), with ragged last chunks and last groups shorter
+# than the rest. Heads are flattened as b * H + h; the first, a middle and
+# the last are checked against the oracle.
+GROUP_SHAPES = [
+    (1, 100, 350, 32), (1, 64, 1000, 64), (2, 32, 2000, 128), (4, 64, 600, 64),
+]
+
+
+@pytest.mark.parametrize("shape", GROUP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_linear_grouped_chunk_walks(shape):
+    B, H, T, D = shape
+    cfg = W.FwdConfig("l", B, H, T, D, "bf16")
+    inp = W.make_linear_inputs(cfg, 77)
+    Y, st = _run(inp)
+    for bh in sorted({0, (B * H) // 2 + 1, B * H - 1}):
+        b, h = divmod(bh, H)
+        sub = {k: inp[k][b:b + 1, h:h + 1] for k in ("P1", "P2", "V", "alpha")}
+        sub["tau"] = inp["tau"][h:h + 1]
+        _check(sub, Y[b:b + 1, h:h + 1], st[b:b + 1, h:h + 1], "bf16", f"{shape} head {bh}")
