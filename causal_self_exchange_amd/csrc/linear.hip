@@ -25,7 +25,7 @@ namespace rel {
 namespace {
 
 constexpr int kL = kLinChunk;          // tokens per chunk
-constexpr int kChunkThreads = 256;     // chunk kernel: 4 waves, 66 KB of LDS (two work-groups per CU)
+constexpr int kChunkThreads = 512;     // chunk kernel: 8 waves, 66 KB of LDS
 constexpr int kOutThreads = 512;       // output kernel: 8 waves, 152 KB of LDS
 constexpr int kScanThreads = 256;
 static_assert(kL == 64, "the output kernel's sub-block pairs assume 4 blocks of 16 rows");
@@ -260,12 +260,12 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
 // taken in order with the state accumulators in registers: before chunk c is
 // added, the accumulated rows are scaled by e^{b_last,c}. dC_c = Kt^T I is a
 // d_h x d_h x 64 product: on v_mfma_f32_32x32x2_f32 for fp32 inputs, on
-// v_mfma_f32_32x32x16_bf16 over Kt's split bf16 pair for bf16 inputs. A wave
-// owns column block n and all row blocks (independent accumulators that share
-// the I operand, which comes straight from global memory into registers). P1
-// is only needed for the row statistics, which come from the staged
-// registers; LDS holds Kt (then its split tiles) and the decay prefix, 66 KB
-// at d_h = 128, so two work-groups fit per CU.
+// v_mfma_f32_32x32x16_bf16 over Kt's split bf16 pair for bf16 inputs. The
+// 32 x 32 state tiles are dealt to the 8 waves (tile w + 8 i to wave w, so a
+// wave's tiles share one column block and its I operand, which comes
+// straight from global memory into registers). P1 is only needed for the row
+// statistics, which come from the staged registers; LDS holds Kt (then its
+// split tiles) and the decay prefix, 66 KB at d_h = 128.
 template <typename Tin, int D>
 __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kChunkThreads;
@@ -279,62 +279,80 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   const int h = bh % a.H;
   const int c0 = gi * a.group, c1 = min(nc, c0 + a.group);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, lh = lane >> 5;
+  constexpr int kW = NT / 64;
   constexpr int kT = D / 32;
-  constexpr int kNPerWave = (kT + 3) / 4;            // column blocks per wave (ceil)
-  constexpr bool kSplit = sizeof(Tin) == 2;          // bf16 MFMA on split operands
+  constexpr int kTiles = kT * kT;
+  constexpr int kTPW = (kTiles + kW - 1) / kW;        // tiles per wave
+  static_assert(kW % kT == 0, "a wave's tiles share their column block");
+  const bool has_tiles = wave < kTiles;
+  const int n = wave % kT;                            // the wave's column block
+  constexpr bool kSplit = sizeof(Tin) == 2;           // bf16 MFMA on split operands
   char* const kh = reinterpret_cast<char*>(&kt[0][0]);
   char* const kl = kh + D * 128;
 
-  // acc[q][m]: rows 32 m + 8 (r >> 2) + 4 lh + (r & 3), columns 32 (wave + 4 q) + l32.
-  f32x16 acc[kNPerWave][kT];
+  // acc[i]: tile w + 8 i = (m, n), m = (w + 8 i) / kT; element r at row
+  // 32 m + 8 (r >> 2) + 4 lh + (r & 3), column 32 n + l32.
+  f32x16 acc[kTPW];
 #pragma unroll
-  for (int q = 0; q < kNPerWave; ++q)
-#pragma unroll
-    for (int m = 0; m < kT; ++m) acc[q][m] = f32x16{};
-  float bsum = 0.0f;                                 // thread r < D: sum of b_last,c[r]
+  for (int i = 0; i < kTPW; ++i) acc[i] = f32x16{};
+  float bsum = 0.0f;                                  // thread r < D: sum of b_last,c[r]
 
-  for (int c = c0; c < c1; ++c) {
+  // A chunk's rows in registers, every load issued before any is used. I
+  // operands of the wave's column block: fp32, B[j][col] = I_j[col] with j =
+  // 2 ks + lh; bf16, 8 rows j = 16 kk + 8 lh + e per k-step. Rows past the
+  // chunk's end read the last row (an address inside the tensor) and are
+  // zeroed where they are used, so no load sits behind a per-lane branch.
+  // (Loading the next chunk during the current one measured no faster: the
+  // work-group is bound by its per-chunk phases, not by load latency.)
+  struct Rows {
+    Staged<NT, Tin, D> g1, g2;
+    Staged<NT, float, D> ga;
+    float bf[kSplit ? 1 : kL / 2];
+    bf16x8v bi[kL / 16];
+  };
+  auto fetch = [&](int c, Rows& f) __attribute__((always_inline)) {
     const int t0 = c * kL;
     const int rows = min(kL, a.T - t0);
     const size_t base = ((size_t)bh * a.T + t0) * D;
     const Tin* I = static_cast<const Tin*>(a.I) + base;
-    // I operands of this wave's column blocks, issued first and consumed
-    // last: fp32, B[j][col] = I_j[col] with j = 2 ks + lh; bf16, 8 rows j =
-    // 16 kk + 8 lh + e per k-step. Rows past the chunk's end read the last
-    // row (an address inside the tensor) and are zeroed afterwards, so no
-    // load sits behind a per-lane branch.
-    float bf[kSplit ? 1 : kNPerWave][kSplit ? 1 : kL / 2];
-    bf16x8v bi[kSplit ? kNPerWave : 1][kL / 16];
-#pragma unroll
-    for (int q = 0; q < kNPerWave; ++q) {
-      const int n = wave + 4 * q;
-      if (n >= kT) break;
+    if (has_tiles) {
       if constexpr (kSplit) {
 #pragma unroll
         for (int kk = 0; kk < kL / 16; ++kk)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bi[q][kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
+          for (int e = 0; e < 8; ++e) f.bi[kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kL / 2; ++ks) f.bf[ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
+      }
+    }
+    f.g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
+    f.g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
+    f.ga.load(a.alpha + base, rows, threadIdx.x);
+  };
+
+  Rows nx;
+  for (int c = c0; c < c1; ++c) {
+    fetch(c, nx);
+    const int rows = min(kL, a.T - c * kL);
+    float bf[kSplit ? 1 : kL / 2];
+    bf16x8v bi[kL / 16];
+    if (has_tiles) {
+      if constexpr (kSplit) {
 #pragma unroll
         for (int kk = 0; kk < kL / 16; ++kk)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bi[q][kk][e] = 16 * kk + 8 * lh + e < rows ? bi[q][kk][e] : (__bf16)0.0f;
+          for (int e = 0; e < 8; ++e) bi[kk][e] = 16 * kk + 8 * lh + e < rows ? nx.bi[kk][e] : (__bf16)0.0f;
       } else {
 #pragma unroll
-        for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
-#pragma unroll
-        for (int ks = 0; ks < kL / 2; ++ks) bf[q][ks] = 2 * ks + lh < rows ? bf[q][ks] : 0.0f;
+        for (int ks = 0; ks < kL / 2; ++ks) bf[ks] = 2 * ks + lh < rows ? nx.bf[ks] : 0.0f;
       }
     }
     {
-      Staged<NT, Tin, D> g1, g2;
-      Staged<NT, float, D> ga;
-      g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
-      g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
-      ga.load(a.alpha + base, rows, threadIdx.x);
       float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
-      staged_row_stats(g1, g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
-      g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
-      ga.template store<false>(&bt[0][0], D, threadIdx.x);
+      staged_row_stats(nx.g1, nx.g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
+      nx.g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
+      nx.ga.template store<false>(&bt[0][0], D, threadIdx.x);
     }
     __syncthreads();
     decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
@@ -374,60 +392,56 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
     }
     __syncthreads();
     if (threadIdx.x < D) bsum += bt[kL - 1][threadIdx.x];
-#pragma unroll
-    for (int q = 0; q < kNPerWave; ++q) {
-      const int n = wave + 4 * q;
-      if (n >= kT) break;
+    if (has_tiles) {
       if (c > c0) {
         // The group's earlier chunks decay over this one.
 #pragma unroll
-        for (int m = 0; m < kT; ++m)
+        for (int i = 0; i < kTPW; ++i) {
+          const int m = (wave + kW * i) / kT;
+          if (m >= kT) break;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[q][m][r] *= pow2(bt[kL - 1][32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)]);
+          for (int r = 0; r < 16; ++r) acc[i][r] *= pow2(bt[kL - 1][32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)]);
+        }
       }
       if constexpr (kSplit) {
-        // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per k-step.
-        struct Op { bf16x8v h[kT], l[kT]; };
-        pipelined<kL / 16, 2, Op>(
-            [&](int kk, Op& o) {
-#pragma unroll
-              for (int m = 0; m < kT; ++m) {
-                o.h[m] = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
-                o.l[m] = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
-              }
+        // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per
+        // k-step; step st is the wave's tile st % kTPW at k-step st / kTPW.
+        struct Op { bf16x8v h, l; };
+        pipelined<kTPW * kL / 16, kTPW, Op>(
+            [&](int st, Op& o) {
+              const int m = (wave + kW * (st % kTPW)) / kT, kk = st / kTPW;
+              o.h = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
+              o.l = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
             },
-            [&](int kk, const Op& o) {
-#pragma unroll
-              for (int m = 0; m < kT; ++m) {
-                acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h[m], bi[q][kk], acc[q][m], 0, 0, 0);
-                acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l[m], bi[q][kk], acc[q][m], 0, 0, 0);
-              }
+            [&](int st, const Op& o) {
+              const int i = st % kTPW, kk = st / kTPW;
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, bi[kk], acc[i], 0, 0, 0);
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, bi[kk], acc[i], 0, 0, 0);
             });
       } else {
-        struct Op { float a[kT]; };
+        struct Op { float a[kTPW]; };
         pipelined<kL / 2, 4, Op>(
             [&](int ks, Op& o) {
 #pragma unroll
-              for (int m = 0; m < kT; ++m) o.a[m] = kt[2 * ks + lh][32 * m + l32];
+              for (int i = 0; i < kTPW; ++i) o.a[i] = kt[2 * ks + lh][32 * ((wave + kW * i) / kT) + l32];
             },
             [&](int ks, const Op& o) {
 #pragma unroll
-              for (int m = 0; m < kT; ++m) acc[q][m] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[m], bf[q][ks], acc[q][m], 0, 0, 0);
+              for (int i = 0; i < kTPW; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[i], bf[ks], acc[i], 0, 0, 0);
             });
       }
     }
-    __syncthreads();                                 // kt and bt are rewritten by the next chunk
+    __syncthreads();                                  // kt and bt are rewritten by the next chunk
   }
-  float* dG = a.state + ((size_t)bh * ng + gi) * (size_t)D * D;
+  if (has_tiles) {
+    float* dG = a.state + ((size_t)bh * ng + gi) * (size_t)D * D;
 #pragma unroll
-  for (int q = 0; q < kNPerWave; ++q) {
-    const int n = wave + 4 * q;
-    if (n >= kT) break;
-#pragma unroll
-    for (int m = 0; m < kT; ++m)
+    for (int i = 0; i < kTPW; ++i) {
+      const int m = (wave + kW * i) / kT;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        dG[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[q][m][r];
+        dG[(size_t)(32 * m + 8 * (r >> 2) + 4 * lh + (r & 3)) * D + 32 * n + l32] = acc[i][r];
+    }
   }
   if (threadIdx.x < D) a.decay[((size_t)bh * ng + gi) * D + threadIdx.x] = pow2(bsum);
 }
@@ -624,6 +638,33 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
         f32x4 acc[N];
 #pragma unroll
         for (int n = 0; n < N; ++n) acc[n] = f32x4{};
+        if constexpr (kSplit) {
+          // On v_mfma_f32_16x16x32_bf16 over split operands: k-group kk
+          // takes channels r = 32 kk + 8 lq + u (u = 0..7) in two steps of
+          // four.
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const int r0 = 32 * kk + 8 * lq;
+            float ref[8], x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              ref[u] = bT[r0 + u][R];
+              x[u] = kT[r0 + u][j] * pow2(ref[u] - bT[r0 + u][j]);
+            }
+            bf16x8v bh, bl;
+            split_bf16(x, bh, bl);
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+#pragma unroll
+              for (int u = 0; u < 8; ++u) x[u] = qT[r0 + u][tq[n]] * pow2(bT[r0 + u][tq[n]] - ref[u]);
+              bf16x8v ah, al;
+              split_bf16(x, ah, al);
+              acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[n], 0, 0, 0);
+              acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[n], 0, 0, 0);
+              acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[n], 0, 0, 0);
+            }
+          }
+        } else {
         struct OpP { float ref, k, bk, q[N], bq[N]; };
         pipelined<D / 4, 8 / N, OpP>(
             [&](int ks, OpP& o) {
@@ -643,6 +684,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
               for (int n = 0; n < N; ++n)
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.q[n] * pow2(o.bq[n] - o.ref), bv, acc[n], 0, 0, 0);
             });
+        }
         // acc[n][i]: row t = 16 tb + 4 lq + i, column j = 16 jb + l16.
 #pragma unroll
         for (int n = 0; n < N; ++n)
@@ -666,6 +708,25 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if (__all(ok)) {
           const int t = 16 * tb + l16, j = 16 * tb + l16;
           f32x4 acc = {};
+          if constexpr (kSplit) {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+              const int r0 = 32 * kk + 8 * lq;
+              float av[8], bv[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const float ref = bT[r0 + u][R];
+                av[u] = qT[r0 + u][t] * pow2(bT[r0 + u][t] - ref);
+                bv[u] = kT[r0 + u][j] * pow2(ref - bT[r0 + u][j]);
+              }
+              bf16x8v ah, al, bh, bl;
+              split_bf16(av, ah, al);
+              split_bf16(bv, bh, bl);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+            }
+          } else {
           struct OpAt { float ref, q, bq, k, bk; };
           pipelined<D / 4, 8, OpAt>(
               [&](int ks, OpAt& o) {
@@ -681,6 +742,7 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 const float bv = o.k * pow2(o.ref - o.bk);
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
               });
+          }
           // acc[i]: row t = 16 tb + 4 lq + i, column j = 16 tb + l16; only
           // j < t is history.
 #pragma unroll
