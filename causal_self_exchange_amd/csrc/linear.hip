@@ -269,9 +269,11 @@ __device__ __forceinline__ void decay_prefix(float* b, int rs, int cs, int rows,
 template <typename Tin, int D>
 __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, HeadParams hp) {
   constexpr int NT = kChunkThreads;
+  constexpr bool kSplit = sizeof(Tin) == 2;           // bf16 MFMA on split operands
   __shared__ float kt[kL][D];     // S_j k_j, then S_j k_j e^{b_last - b_j}
   __shared__ float bt[kL][D];     // alpha_j, then b_j
   __shared__ float tot[NT];
+  __shared__ __attribute__((aligned(16))) char itb[kSplit ? D * 128 : 16];   // bf16: I, channel-major
   const int nc = (a.T + kL - 1) / kL;
   const int ng = (nc + a.group - 1) / a.group;
   const int gi = blockIdx.x % ng;
@@ -286,7 +288,6 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   static_assert(kW % kT == 0, "a wave's tiles share their column block");
   const bool has_tiles = wave < kTiles;
   const int n = wave % kT;                            // the wave's column block
-  constexpr bool kSplit = sizeof(Tin) == 2;           // bf16 MFMA on split operands
   char* const kh = reinterpret_cast<char*>(&kt[0][0]);
   char* const kl = kh + D * 128;
 
@@ -297,34 +298,30 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   for (int i = 0; i < kTPW; ++i) acc[i] = f32x16{};
   float bsum = 0.0f;                                  // thread r < D: sum of b_last,c[r]
 
-  // A chunk's rows in registers, every load issued before any is used. I
-  // operands of the wave's column block: fp32, B[j][col] = I_j[col] with j =
-  // 2 ks + lh; bf16, 8 rows j = 16 kk + 8 lh + e per k-step. Rows past the
-  // chunk's end read the last row (an address inside the tensor) and are
-  // zeroed where they are used, so no load sits behind a per-lane branch.
-  // (Loading the next chunk during the current one measured no faster: the
-  // work-group is bound by its per-chunk phases, not by load latency.)
+  // A chunk's rows in registers, every load issued before any is used. bf16
+  // inputs stage I like P1 and P2 (16-byte row loads), then store it as a
+  // channel-major bf16 tile from which each MFMA's I operand is one 16-byte
+  // read. fp32 inputs load the I operands of the wave's column block
+  // directly, B[j][col] = I_j[col] with j = 2 ks + lh; rows past the chunk's
+  // end read the last row (an address inside the tensor) and are zeroed
+  // where they are used. The next chunk's rows are loaded while the current
+  // one is computed: no register waits for them before the next chunk.
   struct Rows {
     Staged<NT, Tin, D> g1, g2;
     Staged<NT, float, D> ga;
+    Staged<NT, Tin, kSplit ? D : 8> gv;
     float bf[kSplit ? 1 : kL / 2];
-    bf16x8v bi[kL / 16];
   };
   auto fetch = [&](int c, Rows& f) __attribute__((always_inline)) {
     const int t0 = c * kL;
     const int rows = min(kL, a.T - t0);
     const size_t base = ((size_t)bh * a.T + t0) * D;
     const Tin* I = static_cast<const Tin*>(a.I) + base;
-    if (has_tiles) {
-      if constexpr (kSplit) {
+    if constexpr (kSplit) {
+      f.gv.load(I, rows, threadIdx.x);
+    } else if (has_tiles) {
 #pragma unroll
-        for (int kk = 0; kk < kL / 16; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f.bi[kk][e] = I[(size_t)min(16 * kk + 8 * lh + e, rows - 1) * D + 32 * n + l32];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < kL / 2; ++ks) f.bf[ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
-      }
+      for (int ks = 0; ks < kL / 2; ++ks) f.bf[ks] = ld_val(I, (size_t)min(2 * ks + lh, rows - 1) * D + 32 * n + l32);
     }
     f.g1.load(static_cast<const Tin*>(a.P1) + base, rows, threadIdx.x);
     f.g2.load(static_cast<const Tin*>(a.P2) + base, rows, threadIdx.x);
@@ -332,18 +329,12 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   };
 
   Rows nx;
+  fetch(c0, nx);
   for (int c = c0; c < c1; ++c) {
-    fetch(c, nx);
     const int rows = min(kL, a.T - c * kL);
     float bf[kSplit ? 1 : kL / 2];
-    bf16x8v bi[kL / 16];
-    if (has_tiles) {
-      if constexpr (kSplit) {
-#pragma unroll
-        for (int kk = 0; kk < kL / 16; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bi[kk][e] = 16 * kk + 8 * lh + e < rows ? nx.bi[kk][e] : (__bf16)0.0f;
-      } else {
+    if constexpr (!kSplit) {
+      if (has_tiles) {
 #pragma unroll
         for (int ks = 0; ks < kL / 2; ++ks) bf[ks] = 2 * ks + lh < rows ? nx.bf[ks] : 0.0f;
       }
@@ -353,7 +344,9 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
       staged_row_stats(nx.g1, nx.g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
       nx.g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
       nx.ga.template store<false>(&bt[0][0], D, threadIdx.x);
+      if constexpr (kSplit) nx.gv.store_bf16_cm(itb, threadIdx.x);
     }
+    if (c + 1 < c1) fetch(c + 1, nx);
     __syncthreads();
     decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
     __syncthreads();
@@ -406,17 +399,18 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
       if constexpr (kSplit) {
         // A[r][j] = Kt_j[r] (hi and lo), B[j][col] = I_j[col], 16 tokens per
         // k-step; step st is the wave's tile st % kTPW at k-step st / kTPW.
-        struct Op { bf16x8v h, l; };
+        struct Op { bf16x8v h, l, b; };
         pipelined<kTPW * kL / 16, kTPW, Op>(
             [&](int st, Op& o) {
               const int m = (wave + kW * (st % kTPW)) / kT, kk = st / kTPW;
               o.h = lds_bf16x8(kh, sw8(32 * m + l32, 2 * kk + lh));
               o.l = lds_bf16x8(kl, sw8(32 * m + l32, 2 * kk + lh));
+              o.b = lds_bf16x8(itb, sw8(32 * n + l32, 2 * kk + lh));
             },
             [&](int st, const Op& o) {
-              const int i = st % kTPW, kk = st / kTPW;
-              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, bi[kk], acc[i], 0, 0, 0);
-              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, bi[kk], acc[i], 0, 0, 0);
+              const int i = st % kTPW;
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.h, o.b, acc[i], 0, 0, 0);
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.l, o.b, acc[i], 0, 0, 0);
             });
       } else {
         struct Op { float a[kTPW]; };
