@@ -304,8 +304,9 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   // read. fp32 inputs load the I operands of the wave's column block
   // directly, B[j][col] = I_j[col] with j = 2 ks + lh; rows past the chunk's
   // end read the last row (an address inside the tensor) and are zeroed
-  // where they are used. The next chunk's rows are loaded while the current
-  // one is computed: no register waits for them before the next chunk.
+  // where they are used. With bf16 inputs the next chunk's rows are loaded
+  // while the current one is computed: no register waits for them before the
+  // next chunk. fp32 inputs (one chunk per group) load at the chunk's start.
   struct Rows {
     Staged<NT, Tin, D> g1, g2;
     Staged<NT, float, D> ga;
@@ -329,24 +330,34 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
   };
 
   Rows nx;
-  fetch(c0, nx);
+  if constexpr (kSplit) fetch(c0, nx);
   for (int c = c0; c < c1; ++c) {
     const int rows = min(kL, a.T - c * kL);
-    float bf[kSplit ? 1 : kL / 2];
     if constexpr (!kSplit) {
+      fetch(c, nx);           // the I operands are consumed in place: no load ahead
       if (has_tiles) {
 #pragma unroll
-        for (int ks = 0; ks < kL / 2; ++ks) bf[ks] = 2 * ks + lh < rows ? nx.bf[ks] : 0.0f;
+        for (int ks = 0; ks < kL / 2; ++ks) nx.bf[ks] = 2 * ks + lh < rows ? nx.bf[ks] : 0.0f;
       }
     }
     {
       float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
       staged_row_stats(nx.g1, nx.g2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, threadIdx.x);
+      // The row factors, for the output kernel: one lane per row writes them.
+      constexpr int kLanes = D / Staged<NT, Tin, D>::kVec;
+#pragma unroll
+      for (int i = 0; i < Staged<NT, Tin, D>::kN; ++i) {
+        const int idx = threadIdx.x + i * NT, t = idx / kLanes;
+        if (idx < Staged<NT, Tin, D>::kTot && idx % kLanes == 0 && t < rows)
+          *reinterpret_cast<float2*>(a.rowsc + ((size_t)bh * a.T + (size_t)c * kL + t) * 2) = make_float2(sc1[i], sc2[i]);
+      }
       nx.g2.template store_scaled<false>(&kt[0][0], D, threadIdx.x, sc2);     // S_j k_j
       nx.ga.template store<false>(&bt[0][0], D, threadIdx.x);
       if constexpr (kSplit) nx.gv.store_bf16_cm(itb, threadIdx.x);
     }
-    if (c + 1 < c1) fetch(c + 1, nx);
+    if constexpr (kSplit) {
+      if (c + 1 < c1) fetch(c + 1, nx);
+    }
     __syncthreads();
     decay_prefix<NT, D>(&bt[0][0], D, 1, rows, tot, threadIdx.x);
     __syncthreads();
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(kChunkThreads) void lin_chunk_kernel(LinArgs a, Hea
             },
             [&](int ks, const Op& o) {
 #pragma unroll
-              for (int i = 0; i < kTPW; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[i], bf[ks], acc[i], 0, 0, 0);
+              for (int i = 0; i < kTPW; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a[i], nx.bf[ks], acc[i], 0, 0, 0);
             });
       }
     }
@@ -506,6 +517,7 @@ template <typename Tin, int D>
 struct OutPrefetch {
   Staged<kOutThreads, Tin, D> p1, p2, in;
   Staged<kOutThreads, float, D> al;
+  float2 sc[Staged<kOutThreads, Tin, D>::kN];    // the row factors of the p1 / p2 loads' rows
 };
 
 template <typename Tin, int D>
@@ -566,6 +578,14 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     f.p2.load(static_cast<const Tin*>(a.P2) + base, rows, tid);
     f.in.load(static_cast<const Tin*>(a.I) + base, rows, tid);
     f.al.load(a.alpha + base, rows, tid);
+    constexpr int kLanes = D / Staged<NT, Tin, D>::kVec;
+#pragma unroll
+    for (int i = 0; i < Staged<NT, Tin, D>::kN; ++i) {
+      const int idx = tid + i * NT, t = idx / kLanes;
+      f.sc[i] = idx < Staged<NT, Tin, D>::kTot && t < rows
+                    ? *reinterpret_cast<const float2*>(a.rowsc + ((size_t)bh * a.T + (size_t)c * kL + t) * 2)
+                    : make_float2(0.0f, 0.0f);
+    }
   };
 
   // The work-group takes the groups gl = blockIdx.x + k gridDim.x (gl = bh ng
@@ -591,13 +611,17 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int g = chunk_of(gl, k);
     const int ngl = k + 1 < len ? gl : gl + (int)gridDim.x, nk = k + 1 < len ? k + 1 : 0;
     const int c = g % nc, bh = g / nc;
-    const int h = bh % a.H;
     const int rows = min(kL, a.T - c * kL);
     Tin* Y = static_cast<Tin*>(a.Y) + ((size_t)bh * a.T + (size_t)c * kL) * D;
     // The previous chunk's LDS is free (the barrier that ends its iteration).
     {
+      // The row factors S_t / |p1_t| and S_t / |p2_t| that the chunk kernel wrote.
       float sc1[Staged<NT, Tin, D>::kN], sc2[Staged<NT, Tin, D>::kN];
-      staged_row_stats(nx.p1, nx.p2, rows, hp.scale * hp.inv_tau[h], sc1, sc2, tid);
+#pragma unroll
+      for (int i = 0; i < Staged<NT, Tin, D>::kN; ++i) {
+        sc1[i] = nx.sc[i].x;
+        sc2[i] = nx.sc[i].y;
+      }
       nx.p1.template store_scaled<true>(&qT[0][0], kP, tid, sc1);    // S_t q_t
       nx.p2.template store_scaled<true>(&kT[0][0], kP, tid, sc2);    // S_j k_j
     }

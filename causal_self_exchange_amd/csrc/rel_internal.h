@@ -117,11 +117,13 @@ struct LinArgs {
   float* final;         // optional [B][H][d_h][d_h] final state C_T
   float* state;         // workspace: [B*H][groups][d_h][d_h] group states
   float* decay;         // workspace: [B*H][groups][d_h] group decays
+  float* rowsc;         // workspace: [B*H][T][2] row factors S_t / |p1_t|, S_t / |p2_t|
   int B, H, T, d_h;
   int group;            // chunks per group (set by the launcher; groups = ceil(ceil(T/64) / group))
 };
 inline int64_t lin_state_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D * D; }
 inline int64_t lin_decay_floats(int64_t BH, int64_t T, int64_t D) { return BH * ((T + kLinChunk - 1) / kLinChunk) * D; }
+inline int64_t lin_rowsc_floats(int64_t BH, int64_t T) { return BH * T * 2; }
 
 // Cache rows per decode partial state: the workspace holds ceil(L_cap / 256)
 // states per (b, h), one per partial work-group.

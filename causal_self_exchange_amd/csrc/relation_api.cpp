@@ -279,7 +279,8 @@ size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h) {
   if (!count(n, {B, H, T, d_h}) || !head_dim_ok(d_h)) return 0;
   const int64_t BH = static_cast<int64_t>(B) * H;
   return align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float)) +
-         align256(static_cast<size_t>(rel::lin_decay_floats(BH, T, d_h)) * sizeof(float));
+         align256(static_cast<size_t>(rel::lin_decay_floats(BH, T, d_h)) * sizeof(float)) +
+         align256(static_cast<size_t>(rel::lin_rowsc_floats(BH, T)) * sizeof(float));
 }
 
 rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I, const float* alpha,
@@ -314,8 +315,11 @@ rel_status relation_linear_fwd(const void* P1, const void* P2, const void* I, co
   const int64_t BH = static_cast<int64_t>(B) * H;
   char* ws = static_cast<char*>(workspace);
   float* state = reinterpret_cast<float*>(ws);
-  float* decay = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float)));
-  rel::LinArgs a{P1, P2, I, alpha, Y, state_out, state, decay, B, H, T, d_h, 1};
+  const size_t state_bytes = align256(static_cast<size_t>(rel::lin_state_floats(BH, T, d_h)) * sizeof(float));
+  const size_t decay_bytes = align256(static_cast<size_t>(rel::lin_decay_floats(BH, T, d_h)) * sizeof(float));
+  float* decay = reinterpret_cast<float*>(ws + state_bytes);
+  float* rowsc = reinterpret_cast<float*>(ws + state_bytes + decay_bytes);
+  rel::LinArgs a{P1, P2, I, alpha, Y, state_out, state, decay, rowsc, B, H, T, d_h, 1};
   return rel::launch_linear(a, hp, dt == REL_BF16, stream) == hipSuccess ? REL_OK : REL_E_LAUNCH;
 }
 

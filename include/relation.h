@@ -253,8 +253,9 @@ rel_status relation_fwd_model(const void* P1, const void* P2, const void* I,
 
 /*
  * relation_linear_workspace_bytes - device workspace relation_linear_fwd
- * needs (one d_h x d_h fp32 state and d_h decays per 64-token chunk and
- * head). 0 on invalid sizes.
+ * needs (at most one d_h x d_h fp32 state and d_h decays per 64-token chunk
+ * and head, and two fp32 row factors per token and head). 0 on invalid
+ * sizes.
  */
 size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h);
 

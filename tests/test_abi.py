@@ -327,6 +327,8 @@ def test_linear_rejects_invalid_arguments(kw, code):
 
 def test_linear_workspace_bytes():
     lib = R.lib()
-    assert lib.relation_linear_workspace_bytes(1, 32, 8192, 128) == 32 * 128 * 128 * 128 * 4 + 32 * 128 * 128 * 4
-    assert lib.relation_linear_workspace_bytes(1, 1, 1, 32) == 32 * 32 * 4 + 256
+    # chunk states, chunk decays and two row factors per token, each 256-byte aligned
+    assert lib.relation_linear_workspace_bytes(1, 32, 8192, 128) == (32 * 128 * 128 * 128 * 4 + 32 * 128 * 128 * 4
+                                                                     + 32 * 8192 * 2 * 4)
+    assert lib.relation_linear_workspace_bytes(1, 1, 1, 32) == 32 * 32 * 4 + 256 + 256
     assert lib.relation_linear_workspace_bytes(1, 1, 10, 48) == 0
