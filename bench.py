@@ -217,7 +217,9 @@ def bench_linear(torch, R, W, steps, warmup):
     workloads.make_linear_inputs. Work per chunk of L = 64 tokens and head:
     the chunk state 2 L d^2, the read from the entering state 2 L d^2, the
     intra-chunk coefficients and their application 2 L^2 d (half of it
-    masked), the scan 2 d^2: counted as (4 d^2 + 2 L d) FLOP per token."""
+    masked), the scan 2 d^2: counted as (4 d^2 + 2 L d) FLOP per token (the
+    on-chip state update within a group repeats the chunk state's product
+    and is not counted)."""
     cfg = W.CONFIGS["long"]
     inp = W.make_linear_inputs(cfg, 42)
     P1, P2, I = (inp[k].cuda() for k in ("P1", "P2", "V"))
@@ -235,11 +237,18 @@ def bench_linear(torch, R, W, steps, warmup):
     ntok = cfg.B * cfg.H * cfg.T
     flops = float(ntok) * (4 * d * d + 2 * L * d)
     io_bytes = float(ntok) * d * (3 * 2 + 4 + 2)          # P1, P2, I bf16 + alpha fp32 in, Y bf16 out
-    state_bytes = float(cfg.B * cfg.H * ((cfg.T + L - 1) // L)) * d * d * 4 * 4   # chunk states: write, scan r/w, read
-    return {"workload": "linear relation: B=1 H=32 T=8192 d_h=128 bf16, seeded retention, 64-token chunks",
+    # Chunks per group as the library picks them for bf16 inputs: the largest
+    # power of two up to 16 that leaves one group per compute unit.
+    nc, bh = (cfg.T + L - 1) // L, cfg.B * cfg.H
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    group = next((g for g in (16, 8, 4, 2) if bh * ((nc + g - 1) // g) >= n_cu), 1)
+    groups = bh * ((nc + group - 1) // group)
+    # group states (write, scan read and write, read) and row factors (write, read)
+    state_bytes = float(groups) * d * d * 4 * 4 + float(ntok) * 2 * 4 * 2
+    return {"workload": f"linear relation: B=1 H=32 T=8192 d_h=128 bf16, seeded retention, 64-token chunks in groups of {group}",
             "us_per_call": round(ms * 1e3, 2), "tokens/s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
             "TFLOP/s_counted": round(flops / (ms * 1e-3) / 1e12, 2),
-            "arithmetic": "fp32 accumulation; chunk products on bf16 MFMA over split bf16 operand pairs",
+            "arithmetic": "fp32 accumulation; products on bf16 MFMA over split bf16 operand pairs",
             "GB/s_io_plus_states": round((io_bytes + state_bytes) / (ms * 1e-3) / 1e9, 1),
             "flops_counted": flops, "io_bytes": io_bytes, "state_bytes": state_bytes}
 

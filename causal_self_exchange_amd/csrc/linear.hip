@@ -11,12 +11,16 @@
 //             + S_t sum_{j<t in chunk} S_j (sum_r q_{t,r} k_{j,r} e^{b_{t,r} - b_{j,r}}) I_j
 //   Cin_{c+1} = Diag(e^{b_last}) Cin_c + sum_j S_j (k_j o e^{b_last - b_j}) I_j^T.
 // Every exponent above is <= 0, so any retention in (0, 1] is safe.
-// Three kernels: chunk (the bracketed sum and e^{b_last} per chunk), scan
-// (the elementwise recurrence over chunks, one thread per state element),
-// output (Y per chunk). Arithmetic is fp32 throughout; with bf16 inputs the
-// two large products (the chunk contributions K^T I and the output's at I and
-// Qt Cin) run on bf16 MFMA with every fp32 operand split into a bf16 pair
-// (I itself is exact in bf16), which carries it to about 2^-17 relative.
+// Chunks are taken in groups of consecutive chunks of one head, and only one
+// state per group passes through memory. Three kernels: chunk (per group, its
+// chunks in order with the state accumulators in registers: the group's
+// contribution and decay), scan (the elementwise recurrence over groups, one
+// thread per state element), output (per group, its chunks in order: Y, with
+// the entering state stepped from chunk to chunk on chip). Arithmetic is fp32
+// throughout; with bf16 inputs the large products (the contributions K^T I,
+// the output's at I, Qt Cin and state update, and its intra-chunk sub-blocks)
+// run on bf16 MFMA with every fp32 operand split into a bf16 pair (I itself
+// is exact in bf16), which carries it to about 2^-17 relative.
 #include "rel_internal.h"
 #include "rel_device.h"
 
