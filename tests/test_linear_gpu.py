@@ -136,6 +136,7 @@ def test_linear_long_shape_full_heads(h):
 # the last are checked against the oracle.
 GROUP_SHAPES = [
     (1, 100, 350, 32), (1, 64, 1000, 64), (2, 32, 2000, 128), (4, 64, 600, 64),
+    (1, 96, 600, 128),      # groups of 4, 4 and 2 chunks per head; 288 groups on 256 work-groups
 ]
 
 
