@@ -266,8 +266,11 @@ size_t relation_linear_workspace_bytes(int B, int H, int T, int d_h);
  *   q_t = p1_t / |p1_t|,  k_t = p2_t / |p2_t|   (0 for a zero row),
  *   C-_t = Diag(alpha_t) C_{t-1},  Y_t = I_t + S_t (C-_t)^T q_t,
  *   C_t = C-_t + S_t k_t I_t^T        (read before write).
- * Evaluated in 64-token chunks: per-chunk state contributions, a scan over
- * chunks, then each chunk's outputs from its entering state.
+ * Evaluated in 64-token chunks taken in groups of consecutive chunks (up to
+ * 16, chosen from the sizes and the device's compute-unit count; one for fp32
+ * inputs): per-group state contributions, a scan over groups, then each
+ * chunk's outputs from its entering state, stepped from chunk to chunk
+ * within a group. The group size changes only the summation order.
  *
  *   P1, P2, I : in, device [B, H, T, d_h], dtype dt (P1 / P2 after RoPE, I the
  *               mixed information state)
